@@ -1,0 +1,277 @@
+"""ctypes wrapper of the CPU oracle — TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check and the benchmark's CPU-baseline leg import this package.
+It wraps oracle/liboracle.so (plain C, fp32, OpenMP over rows), which shares no code
+with the HIP library.  Tensors are torch CPU tensors; bf16 travels as its bit pattern.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "liboracle.so")
+_lib = None
+
+
+class Dims(C.Structure):
+    _fields_ = [("n_tokens", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
+                ("head_dim", C.c_int32), ("mlp", C.c_int32), ("fc2_group", C.c_int32),
+                ("ln_eps", C.c_float)]
+
+
+class Layout(C.Structure):
+    _fields_ = [("video_t", C.c_int32), ("video_h", C.c_int32), ("video_w", C.c_int32),
+                ("n_text", C.c_int32), ("n_audio", C.c_int32), ("split_t", C.c_int32),
+                ("split_h", C.c_int32), ("split_w", C.c_int32), ("theta", C.c_float)]
+
+
+class Block(C.Structure):
+    _fields_ = [("int8", C.c_int32)] + \
+        [(n, C.c_void_p) for n in ("wqkv", "wo", "w1", "w2", "qqkv", "qo", "q1", "q2",
+                                   "sqkv", "so", "s1", "s2", "mod")]
+
+
+class Taps(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("h1", "t", "q", "k", "v", "o", "y1", "x1", "h2", "u",
+                                          "gl", "y2", "att_max", "att_sum")]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        _lib = C.CDLL(_LIB_PATH)
+        _lib.orc_gelu_tanh_f32.restype = C.c_float
+        _lib.orc_gelu_tanh_f32.argtypes = [C.c_float]
+        for name in ("orc_layout_tokens", "orc_rope_tables", "orc_token_pair", "orc_token_restore",
+                     "orc_block_fwd", "orc_stack_fwd"):
+            getattr(_lib, name).restype = C.c_int32
+    return _lib
+
+
+def _p(t):
+    if t is None:
+        return None
+    assert t.device.type == "cpu" and t.is_contiguous()
+    return C.c_void_p(t.data_ptr())
+
+
+def _i64(v):
+    return C.c_int64(int(v))
+
+
+def bf16(shape):
+    return torch.empty(shape, dtype=torch.bfloat16)
+
+
+def dims_of(w, n_tokens=None) -> Dims:
+    return Dims(int(n_tokens if n_tokens is not None else w.n_tokens), w.hidden, w.heads, w.head_dim,
+                w.mlp, w.fc2_group, w.ln_eps)
+
+
+def layout_of(w) -> Layout:
+    st, sh, sw = w.split
+    return Layout(w.video_t, w.video_h, w.video_w, w.n_text, w.n_audio, st, sh, sw, w.rope_theta)
+
+
+# ------------------------------------------------------------------ helpers
+
+def f32_to_bf16(x: torch.Tensor) -> torch.Tensor:
+    x = x.contiguous().to(torch.float32)
+    out = bf16(x.shape)
+    lib().orc_f32_to_bf16(_p(x), _p(out), _i64(x.numel()))
+    return out
+
+
+def gelu_tanh(u: float) -> float:
+    return float(lib().orc_gelu_tanh_f32(C.c_float(u)))
+
+
+def layout_tokens(w, reduced: bool) -> int:
+    return int(lib().orc_layout_tokens(C.byref(layout_of(w)), int(reduced)))
+
+
+def rope_tables(w, reduced: bool = False):
+    n = layout_tokens(w, reduced)
+    cos = torch.empty((n, w.head_dim // 2), dtype=torch.float32)
+    sin = torch.empty_like(cos)
+    rc = lib().orc_rope_tables(C.byref(layout_of(w)), w.head_dim, int(reduced), _p(cos), _p(sin))
+    if rc != n:
+        raise ValueError("bad rotary layout")
+    return cos, sin
+
+
+# ------------------------------------------------------------------ stages
+
+def adaln(x, shift, scale, eps=1e-6, stats=False):
+    n, d = x.shape
+    h = bf16((n, d))
+    mean = torch.empty(n, dtype=torch.float32)
+    rstd = torch.empty(n, dtype=torch.float32)
+    lib().orc_adaln(_i64(n), C.c_int32(d), C.c_float(eps), _p(x.contiguous()), _p(shift.contiguous()),
+                    _p(scale.contiguous()), _p(h), _p(mean), _p(rstd))
+    return (h, mean, rstd) if stats else h
+
+
+def q8_rows(v, group=None):
+    rows, cols = v.shape
+    group = cols if group is None else group
+    q = torch.empty((rows, cols), dtype=torch.int8)
+    s = torch.empty((rows, cols // group), dtype=torch.float32)
+    lib().orc_q8_rows(_i64(rows), _i64(cols), _i64(group), _p(v.contiguous()), _p(q), _p(s))
+    return q, s
+
+
+def quantize_weights(w):
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.int8)
+    s = torch.empty(rows, dtype=torch.float32)
+    lib().orc_quantize_weights(_i64(rows), _i64(cols), _p(w.contiguous()), _p(q), _p(s))
+    return q, s
+
+
+def gemm_f32(a, w):
+    M, K = a.shape
+    N = w.shape[0]
+    acc = torch.empty((M, N), dtype=torch.float32)
+    lib().orc_gemm_f32(_i64(M), _i64(N), _i64(K), _p(a.contiguous()), _p(w.contiguous()), _p(acc))
+    return acc
+
+
+def gemm_i32(qa, qw):
+    M, K = qa.shape
+    N = qw.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32)
+    lib().orc_gemm_i32(_i64(M), _i64(N), _i64(K), _p(qa.contiguous()), _p(qw.contiguous()), _p(acc))
+    return acc
+
+
+def dequant_bf16(acc, sa, sw):
+    M, N = acc.shape
+    out = bf16((M, N))
+    lib().orc_dequant_bf16(_i64(M), _i64(N), _p(acc.contiguous()), _p(sa.contiguous()),
+                           _p(sw.contiguous()), _p(out))
+    return out
+
+
+def fc2_int8(qa, sa, qw, sw, group):
+    M, K = qa.shape
+    N = qw.shape[0]
+    y = bf16((M, N))
+    lib().orc_fc2_int8(_i64(M), _i64(N), _i64(K), _i64(group), _p(qa.contiguous()), _p(sa.contiguous()),
+                       _p(qw.contiguous()), _p(sw.contiguous()), _p(y))
+    return y
+
+
+def rope_split(t, cos, sin, heads, head_dim):
+    N = t.shape[0]
+    d = heads * head_dim
+    q, k, v = (bf16((heads, N, head_dim)) for _ in range(3))
+    lib().orc_rope_split(_i64(N), C.c_int32(d), C.c_int32(heads), C.c_int32(head_dim), _p(t.contiguous()),
+                         _p(cos.contiguous()), _p(sin.contiguous()), _p(q), _p(k), _p(v))
+    return q, k, v
+
+
+def attention(q, k, v, stats=False):
+    H, N, hd = q.shape
+    o = bf16((H, N, hd))
+    mx = torch.empty((H, N), dtype=torch.float32)
+    sm = torch.empty((H, N), dtype=torch.float32)
+    lib().orc_attention(C.c_int32(H), _i64(N), C.c_int32(hd), _p(q.contiguous()), _p(k.contiguous()),
+                        _p(v.contiguous()), _p(o), _p(mx), _p(sm))
+    return (o, mx, sm) if stats else o
+
+
+def gelu_rows(u):
+    gl = bf16(u.shape)
+    lib().orc_gelu_rows(_i64(u.numel()), _p(u.contiguous()), _p(gl))
+    return gl
+
+
+def gate(x, g, y):
+    n, d = x.shape
+    out = bf16((n, d))
+    lib().orc_gate(_i64(n), C.c_int32(d), _p(x.contiguous()), _p(g.contiguous()), _p(y.contiguous()), _p(out))
+    return out
+
+
+def token_pair(w, x):
+    r = bf16((layout_tokens(w, True), x.shape[1]))
+    lib().orc_token_pair(C.byref(layout_of(w)), C.c_int32(x.shape[1]), _p(x.contiguous()), _p(r))
+    return r
+
+
+def token_restore(w, bypass, y, r_in):
+    x = bf16(bypass.shape)
+    lib().orc_token_restore(C.byref(layout_of(w)), C.c_int32(bypass.shape[1]), _p(bypass.contiguous()),
+                            _p(y.contiguous()), _p(r_in.contiguous()), _p(x))
+    return x
+
+
+# ------------------------------------------------------------------ block and stack
+
+def _block_struct(p: dict, keep: list) -> Block:
+    """p: bf16 weights {wqkv, wo, w1, w2, mod} and, for int8, {qqkv, sqkv, qo, so, q1, s1, q2, s2}."""
+    b = Block()
+    b.int8 = 1 if "qqkv" in p else 0
+    for name in ("wqkv", "wo", "w1", "w2", "qqkv", "qo", "q1", "q2", "sqkv", "so", "s1", "s2", "mod"):
+        t = p.get(name)
+        if t is not None:
+            t = t.contiguous()
+            keep.append(t)
+            setattr(b, name, t.data_ptr())
+    return b
+
+
+def quantize_block(p: dict) -> dict:
+    """Adds the int8 codes and scales of the four weight matrices to a bf16 block dict."""
+    out = dict(p)
+    for w, q, s in (("wqkv", "qqkv", "sqkv"), ("wo", "qo", "so"), ("w1", "q1", "s1"), ("w2", "q2", "s2")):
+        out[q], out[s] = quantize_weights(p[w])
+    return out
+
+
+TAP_NAMES = ("h1", "t", "q", "k", "v", "o", "y1", "x1", "h2", "u", "gl", "y2", "att_max", "att_sum")
+
+
+def block_fwd(w, p: dict, x, cos=None, sin=None, fused=False, taps=False, n_tokens=None):
+    """One block on x (bf16 [N][d]); returns the new residual (and a dict of stage tensors)."""
+    N = x.shape[0] if n_tokens is None else n_tokens
+    d, H, hd, f = w.hidden, w.heads, w.head_dim, w.mlp
+    if cos is None:
+        cos, sin = rope_tables(w)
+    keep = []
+    b = _block_struct(p, keep)
+    xo = x.contiguous().clone()
+    tp = None
+    tapd = {}
+    if taps:
+        shapes = {"h1": (N, d), "t": (N, 3 * d), "q": (H, N, hd), "k": (H, N, hd), "v": (H, N, hd),
+                  "o": (H, N, hd), "y1": (N, d), "x1": (N, d), "h2": (N, d), "u": (N, f), "gl": (N, f),
+                  "y2": (N, d)}
+        for k_, s_ in shapes.items():
+            tapd[k_] = bf16(s_)
+        tapd["att_max"] = torch.empty((H, N), dtype=torch.float32)
+        tapd["att_sum"] = torch.empty((H, N), dtype=torch.float32)
+        tp = Taps(*[tapd[n].data_ptr() for n in TAP_NAMES])
+    rc = lib().orc_block_fwd(C.byref(dims_of(w, N)), C.byref(b), _p(cos.contiguous()), _p(sin.contiguous()),
+                             _p(xo), int(fused), C.byref(tp) if tp is not None else None)
+    if rc != 0:
+        raise ValueError(f"orc_block_fwd failed: {rc}")
+    return (xo, tapd) if taps else xo
+
+
+def stack_fwd(w, blocks: list, x, reduce_after=-1, restore_before=-1, fused=False):
+    keep = []
+    arr = (Block * len(blocks))(*[_block_struct(p, keep) for p in blocks])
+    xo = x.contiguous().clone()
+    rc = lib().orc_stack_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), C.c_int32(len(blocks)), arr,
+                             C.c_int32(reduce_after), C.c_int32(restore_before), _p(xo), int(fused))
+    if rc != 0:
+        raise ValueError(f"orc_stack_fwd failed: {rc}")
+    return xo

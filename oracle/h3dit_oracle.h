@@ -1,0 +1,87 @@
+/*
+ * CPU oracle for the MiniMax-H3 single-stream Omni DiT block — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the CPU-baseline leg of the benchmark may
+ * call this library.  It shares no code, header, table or helper with the HIP path.
+ *
+ * Sources (web pages about antirez's h3.c / h3-metal engine):
+ *   [RV]  alphalab.site, "h3-metal 把 MiniMax-H3 搬上 Apple Silicon：突破與代價（2026）"
+ *   [DD]  linlog.top article 1265 (h3.c deep dive), sections
+ *         "MiniMax H3：原生音频视频一体化生成", "h3.c 的核心设计", "int8 量化：从 36 秒到 19 秒",
+ *         "DiT 融合内核：减少全局内存往返", "Token 缩减：28% 的去噪时间消减"
+ *   [NS]  daily.steinslab.io, "零 Python 依赖：Redis 作者的 3.5 秒端侧实验"
+ * The pages describe the block in words only; widths, the activation, eps, the
+ * rotary split and every rounding point are readings, each stated where it is used.
+ *
+ * Conventions: bf16 values travel as uint16_t bit patterns; every matrix is row-major;
+ * weights are [out][in]; all arithmetic is IEEE fp32 (the library is built with
+ * -ffp-contract=off, so a*b+c is two roundings), sums run in ascending index order.
+ */
+#ifndef H3DIT_ORACLE_H
+#define H3DIT_ORACLE_H
+#include <stdint.h>
+
+typedef struct {
+  int32_t n_tokens, hidden, heads, head_dim, mlp, fc2_group;
+  float ln_eps;
+} orc_dims;
+
+typedef struct {
+  int32_t video_t, video_h, video_w; /* video tokens first, (t, h, w) row-major */
+  int32_t n_text, n_audio;           /* then text, then audio */
+  int32_t split_t, split_h, split_w; /* head-dim share of each video axis (sum = head_dim) */
+  float theta;
+} orc_layout;
+
+typedef struct {
+  int32_t int8;                         /* 0: bf16 weights; 1: int8 weights + per-row scales */
+  const uint16_t *wqkv, *wo, *w1, *w2;  /* bf16 [3d][d], [d][d], [f][d], [d][f] */
+  const int8_t *qqkv, *qo, *q1, *q2;    /* int8, same shapes */
+  const float *sqkv, *so, *s1, *s2;     /* fp32 per output row */
+  const uint16_t *mod;                  /* bf16 [6][d]: shift1 scale1 gate1 shift2 scale2 gate2 */
+} orc_block;
+
+typedef struct {                        /* optional stage outputs; any pointer may be NULL */
+  uint16_t *h1;                         /* [N][d] AdaLN1 output */
+  uint16_t *t;                          /* [N][3d] QKV projection before rotary */
+  uint16_t *q, *k, *v;                  /* [H][N][hd] */
+  uint16_t *o;                          /* [H][N][hd] attention output */
+  uint16_t *y1, *x1, *h2, *u, *gl, *y2; /* [N][d] ... [N][f] ... [N][d] */
+  float *att_max, *att_sum;             /* [H][N] softmax row max and row sum */
+} orc_taps;
+
+/* scalar helpers exposed for the pins */
+void orc_f32_to_bf16(const float *in, uint16_t *out, int64_t n);
+float orc_gelu_tanh_f32(float u);
+int32_t orc_layout_tokens(const orc_layout *L, int32_t reduced);
+int32_t orc_rope_tables(const orc_layout *L, int32_t head_dim, int32_t reduced, float *cosv, float *sinv);
+
+/* stages */
+void orc_adaln(int64_t n, int32_t d, float eps, const uint16_t *x, const uint16_t *shift,
+               const uint16_t *scale, uint16_t *h, float *mean, float *rstd);
+void orc_q8_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v, int8_t *q, float *s);
+void orc_quantize_weights(int64_t rows, int64_t cols, const uint16_t *w, int8_t *q, float *s);
+void orc_gemm_f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *W, float *acc);
+void orc_gemm_i32(int64_t M, int64_t N, int64_t K, const int8_t *A, const int8_t *W, int32_t *acc);
+void orc_rope_split(int64_t N, int32_t d, int32_t H, int32_t hd, const uint16_t *t,
+                    const float *cosv, const float *sinv, uint16_t *q, uint16_t *k, uint16_t *v);
+void orc_attention(int32_t H, int64_t N, int32_t hd, const uint16_t *q, const uint16_t *k,
+                   const uint16_t *v, uint16_t *o, float *row_max, float *row_sum);
+void orc_gelu_rows(int64_t n, const uint16_t *u, uint16_t *gl);
+void orc_gate(int64_t n, int32_t d, const uint16_t *x, const uint16_t *gate, const uint16_t *y,
+              uint16_t *out);
+void orc_fc2_int8(int64_t M, int64_t N, int64_t K, int64_t group, const int8_t *qa,
+                  const float *sa, const int8_t *qw, const float *sw, uint16_t *y);
+void orc_dequant_bf16(int64_t M, int64_t N, const int32_t *acc, const float *sa, const float *sw,
+                      uint16_t *out);
+int32_t orc_token_pair(const orc_layout *L, int32_t d, const uint16_t *x, uint16_t *r);
+int32_t orc_token_restore(const orc_layout *L, int32_t d, const uint16_t *bypass,
+                          const uint16_t *y, const uint16_t *r_in, uint16_t *x);
+
+/* whole block and stack */
+int32_t orc_block_fwd(const orc_dims *dims, const orc_block *blk, const float *cosv,
+                      const float *sinv, uint16_t *x, int32_t fused, orc_taps *taps);
+int32_t orc_stack_fwd(const orc_dims *dims, const orc_layout *L, int32_t n_blocks,
+                      const orc_block *blocks, int32_t reduce_after, int32_t restore_before,
+                      uint16_t *x, int32_t fused);
+#endif

@@ -1,0 +1,576 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+closed forms, invariants, exact special cases, brute force in float64 and library
+routines (torch's bf16 rounding, layer_norm, scaled_dot_product_attention, tanh-GELU,
+int64 matmul, complex multiplication).  Each test names the property it pins.
+
+The pages (web articles on antirez's h3.c engine for MiniMax-H3) print no worked example
+or intermediate value, so no golden tensor from them exists; tests/golden/ holds the
+small hand-derived cases used here, each with its derivation."""
+import json
+import math
+import os
+
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+from synth import WORKLOADS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+W0 = WORKLOADS[0]
+
+
+def bf(x):
+    return x.to(torch.float32).to(torch.bfloat16)
+
+
+def ulp_diff(a, b):
+    """Distance in bf16 units of last place between two bf16 tensors of one sign pattern."""
+    ai = a.view(torch.int16).to(torch.int32)
+    bi = b.view(torch.int16).to(torch.int32)
+    ai = torch.where(ai < 0, -(ai & 0x7FFF), ai)
+    bi = torch.where(bi < 0, -(bi & 0x7FFF), bi)
+    return (ai - bi).abs()
+
+
+def relerr(g, r):
+    g = g.to(torch.float64)
+    r = r.to(torch.float64)
+    return float((g - r).abs().max() / r.abs().max().clamp_min(1e-30))
+
+
+# ----------------------------------------------------------------------------- generator
+
+def test_philox_known_answer():
+    # Philox-4x32-10, counter (0,0,0,0), key (0,0): Random123 known-answer vector.
+    z = torch.zeros(1, dtype=torch.int64)
+    out = synth.philox4x32_10(z, z, z, z, 0, 0)
+    assert [int(o) for o in out] == [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]
+
+
+def test_generator_deterministic_and_normal():
+    a = synth.normal_bf16(7, 3, 1, (300, 200), 0.02)
+    b = synth.normal_bf16(7, 3, 1, (300, 200), 0.02)
+    c = synth.normal_bf16(7, 4, 1, (300, 200), 0.02)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
+    x = a.to(torch.float64)
+    assert abs(float(x.mean())) < 0.02 * 0.02
+    assert abs(float(x.std()) - 0.02) < 0.02 * 0.02
+
+
+# ----------------------------------------------------------------------------- bf16 rounding
+
+def test_bf16_rounding_matches_torch_rne():
+    g = torch.Generator().manual_seed(0)
+    x = torch.randn(200000, generator=g) * torch.exp(torch.randn(200000, generator=g) * 4)
+    ties = (torch.arange(4096, dtype=torch.int32) * 65536 + 0x3F800000 + 0x8000).view(torch.float32)
+    x = torch.cat([x, ties, -ties, torch.tensor([0.0, -0.0, 1e-40, 3.0e38])])
+    got = oracle.f32_to_bf16(x)
+    assert torch.equal(got.view(torch.int16), x.to(torch.bfloat16).view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- GELU
+
+def test_gelu_tanh_closed_forms_and_library():
+    assert oracle.gelu_tanh(0.0) == 0.0
+    xs = torch.linspace(-8, 8, 2001, dtype=torch.float64)
+    ours = torch.tensor([oracle.gelu_tanh(float(v)) for v in xs], dtype=torch.float64)
+    ref = F.gelu(xs, approximate="tanh")
+    assert float((ours - ref).abs().max()) < 4e-6 * 8
+    neg = torch.tensor([oracle.gelu_tanh(-float(v)) for v in xs], dtype=torch.float64)
+    # gelu(x) - gelu(-x) = x
+    assert float((ours - neg - xs).abs().max()) < 1e-5
+    # large |x|: gelu -> x for x >> 0, -> 0 for x << 0
+    assert oracle.gelu_tanh(10.0) == 10.0 and oracle.gelu_tanh(-10.0) == 0.0
+
+
+def test_gelu_rows_rounding():
+    u = bf(torch.randn(4096, dtype=torch.float64) * 3)
+    got = oracle.gelu_rows(u)
+    ref64 = F.gelu(u.to(torch.float64), approximate="tanh")
+    ref = bf(ref64)
+    # away from the negative tail: within one bf16 step of the float64 value
+    ok = u.to(torch.float64) > -3
+    assert int(ulp_diff(got[ok], ref[ok]).max()) <= 1
+    # in the tail 1 + tanh(z) cancels in fp32: absolute error stays below |u| * 2^-22
+    err = (got.to(torch.float64) - ref64).abs()
+    assert torch.all(err <= u.to(torch.float64).abs() * 2.0 ** -22 + ref64.abs() * 2.0 ** -8)
+
+
+# ----------------------------------------------------------------------------- AdaLN
+
+def test_adaln_zero_modulation_is_layernorm():
+    g = torch.Generator().manual_seed(1)
+    x = bf(torch.randn(64, 256, generator=g) * 3 + 0.5)
+    z = torch.zeros(256, dtype=torch.bfloat16)
+    h, mean, rstd = oracle.adaln(x, z, z, 1e-6, stats=True)
+    ref = F.layer_norm(x.to(torch.float64), (256,), eps=1e-6)
+    assert int(ulp_diff(h, bf(ref)).max()) <= 1
+    x64 = x.to(torch.float64)
+    assert float((mean.to(torch.float64) - x64.mean(1)).abs().max()) < 1e-5
+    var = x64.var(1, unbiased=False)
+    assert float((rstd.to(torch.float64) - 1 / torch.sqrt(var + 1e-6)).abs().max() / rstd.max()) < 1e-5
+    # normalised output: mean 0, variance v / (v + eps)
+    hf = h.to(torch.float64)
+    assert float(hf.mean(1).abs().max()) < 2e-2
+    assert float((hf.var(1, unbiased=False) - var / (var + 1e-6)).abs().max()) < 2e-2
+
+
+def test_adaln_modulation_form():
+    g = torch.Generator().manual_seed(2)
+    x = bf(torch.randn(32, 512, generator=g))
+    sh = bf(torch.randn(512, generator=g) * 0.1)
+    sc = bf(torch.randn(512, generator=g) * 0.1)
+    h = oracle.adaln(x, sh, sc)
+    ln = F.layer_norm(x.to(torch.float64), (512,), eps=1e-6)
+    ref = bf(ln * (1 + sc.to(torch.float64)) + sh.to(torch.float64))
+    assert int(ulp_diff(h, ref).max()) <= 1
+    # scale = -1 cancels the normalised part: output is the shift
+    h2 = oracle.adaln(x, sh, torch.full((512,), -1.0, dtype=torch.bfloat16))
+    assert torch.equal(h2.view(torch.int16), sh.expand(32, 512).contiguous().view(torch.int16))
+
+
+def test_adaln_constant_row_is_shift():
+    x = torch.full((4, 5120), 1.375, dtype=torch.bfloat16)
+    sh = bf(torch.linspace(-1, 1, 5120))
+    h = oracle.adaln(x, sh, bf(torch.randn(5120)))
+    assert torch.equal(h.view(torch.int16), sh.expand(4, 5120).contiguous().view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- int8 codes
+
+def test_q8_worked_cases():
+    with open(os.path.join(GOLDEN, "q8_cases.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        v = torch.tensor([c["values"]], dtype=torch.float32).to(torch.bfloat16)
+        q, s = oracle.q8_rows(v)
+        assert q[0].tolist() == c["codes"], c["note"]
+        assert float(s[0, 0]) == float(torch.tensor(c["scale"], dtype=torch.float32)), c["note"]
+
+
+def test_q8_properties():
+    g = torch.Generator().manual_seed(3)
+    v = bf(torch.randn(200, 2048, generator=g) * torch.exp(torch.randn(200, 1, generator=g)))
+    q, s = oracle.q8_rows(v, 1024)
+    vf = v.to(torch.float64).view(200, 2, 1024)
+    qf = q.to(torch.float64).view(200, 2, 1024)
+    s64 = s.to(torch.float64).unsqueeze(-1)
+    assert int(q.abs().max()) == 127
+    assert torch.all(qf.abs().amax(-1) == 127)                      # absmax element maps to 127
+    # rounding error <= s/2, up to the fp32 rounding of v/s (|v/s| <= 127)
+    assert float(((vf - qf * s64).abs() - s64 * (0.5 + 127 * 2.0 ** -23)).max()) <= 0
+    # scale is absmax / 127 in fp32
+    am = v.to(torch.float32).view(200, 2, 1024).abs().amax(-1)
+    assert torch.equal(s, am / 127.0)
+
+
+def test_quantize_weights_is_per_row_q8():
+    g = torch.Generator().manual_seed(4)
+    w = bf(torch.randn(96, 320, generator=g) * 0.02)
+    q, s = oracle.quantize_weights(w)
+    q2, s2 = oracle.q8_rows(w)
+    assert torch.equal(q, q2) and torch.equal(s, s2[:, 0])
+
+
+# ----------------------------------------------------------------------------- projections
+
+def test_gemm_i32_exact():
+    g = torch.Generator().manual_seed(5)
+    a = torch.randint(-127, 128, (33, 700), generator=g, dtype=torch.int8)
+    w = torch.randint(-127, 128, (45, 700), generator=g, dtype=torch.int8)
+    acc = oracle.gemm_i32(a, w)
+    ref = a.to(torch.int64) @ w.to(torch.int64).T
+    assert torch.equal(acc.to(torch.int64), ref)
+    ones = torch.full((2, 20480), 127, dtype=torch.int8)
+    assert int(oracle.gemm_i32(ones, ones)[0, 0]) == 20480 * 16129
+
+
+def test_gemm_f32_against_float64():
+    g = torch.Generator().manual_seed(6)
+    a = bf(torch.randn(40, 1024, generator=g))
+    w = bf(torch.randn(72, 1024, generator=g) * 0.02)
+    acc = oracle.gemm_f32(a, w)
+    ref = a.to(torch.float64) @ w.to(torch.float64).T
+    bound = 1024 * 2.0 ** -24 * (a.to(torch.float64).abs() @ w.to(torch.float64).abs().T)
+    assert torch.all((acc.to(torch.float64) - ref).abs() <= bound)
+    # small integers: every partial sum exact
+    ai = bf(torch.randint(-8, 9, (5, 64), generator=g).to(torch.float32))
+    wi = bf(torch.randint(-8, 9, (7, 64), generator=g).to(torch.float32))
+    assert torch.equal(oracle.gemm_f32(ai, wi), (ai.to(torch.float64) @ wi.to(torch.float64).T).to(torch.float32))
+    # operand orientation: W is [out][in]
+    e = torch.zeros(3, 64, dtype=torch.bfloat16)
+    e[1, 5] = 1
+    assert torch.equal(oracle.gemm_f32(ai, e)[:, 1], ai[:, 5].to(torch.float32))
+
+
+def test_dequant_order():
+    acc = torch.tensor([[123456789, -7]], dtype=torch.int32)
+    sa = torch.tensor([0.01], dtype=torch.float32)
+    sw = torch.tensor([0.003, 2.0], dtype=torch.float32)
+    out = oracle.dequant_bf16(acc, sa, sw)
+    ref = bf((acc.to(torch.float32) * sa[:, None]) * sw[None, :])
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_fc2_single_group_equals_per_token():
+    g = torch.Generator().manual_seed(7)
+    qa = torch.randint(-127, 128, (16, 1024), generator=g, dtype=torch.int8)
+    sa = torch.rand(16, 1, generator=g) * 0.01
+    qw = torch.randint(-127, 128, (40, 1024), generator=g, dtype=torch.int8)
+    sw = torch.rand(40, generator=g) * 0.001
+    y = oracle.fc2_int8(qa, sa, qw, sw, 1024)
+    ref = oracle.dequant_bf16(oracle.gemm_i32(qa, qw), sa[:, 0], sw)
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
+def test_fc2_groups_against_int64():
+    g = torch.Generator().manual_seed(8)
+    qa = torch.randint(-127, 128, (8, 4096), generator=g, dtype=torch.int8)
+    sa = torch.rand(8, 4, generator=g) * 0.01
+    qw = torch.randint(-127, 128, (24, 4096), generator=g, dtype=torch.int8)
+    sw = torch.rand(24, generator=g) * 0.001
+    y = oracle.fc2_int8(qa, sa, qw, sw, 1024)
+    acc = torch.einsum("mgk,ngk->mng", qa.view(8, 4, 1024).to(torch.int64), qw.view(24, 4, 1024).to(torch.int64))
+    ref = (acc.to(torch.float64) * sa.to(torch.float64)[:, None, :]).sum(-1) * sw.to(torch.float64)
+    assert relerr(y, ref) < 8e-3
+    # equal group scales: per-token result up to fp32 summation order
+    sa_eq = sa[:, :1].expand(8, 4).contiguous()
+    y_eq = oracle.fc2_int8(qa, sa_eq, qw, sw, 1024)
+    ref_eq = oracle.dequant_bf16(oracle.gemm_i32(qa, qw), sa_eq[:, 0].contiguous(), sw)
+    assert int(ulp_diff(y_eq, ref_eq).max()) <= 1
+
+
+# ----------------------------------------------------------------------------- rotary
+
+def test_rope_tables_closed_forms():
+    w = W0
+    cos, sin = oracle.rope_tables(w)
+    N, half = cos.shape
+    assert N == w.n_tokens and half == w.head_dim // 2
+    # token (0,0,0) and the first text/audio tokens sit at position 0: identity rotation
+    for n in (0, w.n_video, w.n_video + w.n_text):
+        assert torch.all(cos[n] == 1) and torch.all(sin[n] == 0)
+    assert torch.allclose(cos * cos + sin * sin, torch.ones_like(cos), atol=1e-6)
+    st, sh, sw = w.split
+    # video token (t,h,w): time pairs depend only on t, height pairs on h, width pairs on w
+    def tok(t, h, x):
+        return (t * w.video_h + h) * w.video_w + x
+    a, b = tok(2, 5, 3), tok(2, 1, 7)
+    assert torch.equal(cos[a, : st // 2], cos[b, : st // 2])
+    assert not torch.equal(cos[a, st // 2:], cos[b, st // 2:])
+    # the first pair of each section turns by exactly the position (frequency theta^0 = 1)
+    assert abs(float(cos[a, 0]) - math.cos(2)) < 1e-7
+    assert abs(float(cos[a, st // 2]) - math.cos(5)) < 1e-7
+    assert abs(float(cos[a, (st + sh) // 2]) - math.cos(3)) < 1e-7
+    # last pair of the width section: frequency theta^(-2(sw/2-1)/sw)
+    f = 10000.0 ** (-2 * (sw // 2 - 1) / sw)
+    assert abs(float(sin[a, half - 1]) - math.sin(3 * f)) < 1e-7
+    # text token at index p: 1-D rotary over the whole head dim
+    p = 7
+    n = w.n_video + p
+    j = torch.arange(half, dtype=torch.float64)
+    assert torch.allclose(cos[n].to(torch.float64), torch.cos(p * 10000.0 ** (-2 * j / w.head_dim)), atol=1e-7)
+
+
+def test_rope_relative_position_property():
+    # <R(m) q, R(n) k> depends only on m - n, per axis (checked in float64 with the tables)
+    w = W0.replace(video_w=16)
+    cos, sin = oracle.rope_tables(w)
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn(w.head_dim // 2, dtype=torch.complex128, generator=g)
+    k = torch.randn(w.head_dim // 2, dtype=torch.complex128, generator=g)
+    rot = torch.complex(cos.to(torch.float64), sin.to(torch.float64))
+
+    def tok(t, h, x):
+        return (t * w.video_h + h) * w.video_w + x
+
+    def score(m, n):
+        return float(((q * rot[m]) * torch.conj(k * rot[n])).real.sum())
+
+    assert abs(score(tok(1, 2, 3), tok(0, 1, 1)) - score(tok(2, 3, 5), tok(1, 2, 3))) < 1e-5
+    assert abs(score(tok(1, 2, 3), tok(0, 1, 1)) - score(tok(1, 2, 4), tok(0, 1, 1))) > 1e-3
+
+
+def test_rope_reduced_positions_are_midpoints():
+    w = WORKLOADS[4].replace(video_t=2, video_h=3, video_w=7, n_text=5, n_audio=3,
+                             hidden=256, heads=4, head_dim=64, mlp=1024)
+    cf, sf = oracle.rope_tables(w, reduced=False)
+    cr, sr = oracle.rope_tables(w, reduced=True)
+    assert cr.shape[0] == 2 * 3 * 4 + 8
+    # pair token (t,h,k) lies between (t,h,2k) and (t,h,2k+1): rotations compose so that
+    # R(mid)^2 = R(2k) R(2k+1) (angles add), per pair of the head dim
+    full = torch.complex(cf.to(torch.float64), sf.to(torch.float64))
+    red = torch.complex(cr.to(torch.float64), sr.to(torch.float64))
+    for t in range(2):
+        for h in range(3):
+            for kk in range(3):
+                a = full[(t * 3 + h) * 7 + 2 * kk]
+                b = full[(t * 3 + h) * 7 + 2 * kk + 1]
+                r = red[(t * 3 + h) * 4 + kk]
+                assert torch.allclose(r * r, a * b, atol=1e-6)
+            # unpaired last column keeps its rotation
+            assert torch.allclose(red[(t * 3 + h) * 4 + 3], full[(t * 3 + h) * 7 + 6], atol=0)
+    # text/audio unchanged
+    assert torch.equal(cr[24:], cf[42:])
+
+
+def test_rope_split_layout_and_sign():
+    N, H, hd = 5, 3, 8
+    d = H * hd
+    g = torch.Generator().manual_seed(10)
+    t = bf(torch.randn(N, 3 * d, generator=g))
+    one = torch.ones(N, hd // 2)
+    zero = torch.zeros(N, hd // 2)
+    q, k, v = oracle.rope_split(t, one, zero, H, hd)
+    tt = t.view(N, 3, H, hd).permute(1, 2, 0, 3)
+    assert torch.equal(q.view(torch.int16), tt[0].contiguous().view(torch.int16))
+    assert torch.equal(k.view(torch.int16), tt[1].contiguous().view(torch.int16))
+    assert torch.equal(v.view(torch.int16), tt[2].contiguous().view(torch.int16))
+    # quarter turn: (a, b) -> (-b, a), as multiplication by i of a + ib
+    q, k, _ = oracle.rope_split(t, zero, one, H, hd)
+    z = torch.view_as_complex(tt[0].to(torch.float32).reshape(H, N, hd // 2, 2).contiguous()) * 1j
+    assert torch.equal(q.to(torch.float32), torch.view_as_real(z).reshape(H, N, hd))
+    # general angle against complex multiplication in float64
+    ang = torch.rand(N, hd // 2, generator=g) * 6.28
+    c, s = torch.cos(ang), torch.sin(ang)
+    q, k, _ = oracle.rope_split(t, c, s, H, hd)
+    zq = torch.view_as_complex(tt[1].to(torch.float64).reshape(H, N, hd // 2, 2).contiguous())
+    rk = torch.view_as_real(zq * torch.complex(c.to(torch.float64), s.to(torch.float64))).reshape(H, N, hd)
+    assert int(ulp_diff(k, bf(rk)).max()) <= 1
+
+
+# ----------------------------------------------------------------------------- attention
+
+def test_attention_single_token_and_constant_values():
+    g = torch.Generator().manual_seed(11)
+    q = bf(torch.randn(2, 1, 64, generator=g))
+    k = bf(torch.randn(2, 1, 64, generator=g))
+    v = bf(torch.randn(2, 1, 64, generator=g))
+    assert torch.equal(oracle.attention(q, k, v).view(torch.int16), v.view(torch.int16))  # N = 1
+    q = bf(torch.randn(2, 50, 128, generator=g) * 3)
+    k = bf(torch.randn(2, 50, 128, generator=g) * 3)
+    ones = torch.ones(2, 50, 128, dtype=torch.bfloat16)
+    assert torch.all(oracle.attention(q, k, ones).to(torch.float32) == 1.0)  # rows sum to 1
+    # identical keys: uniform weights, output = mean of V
+    kk = k[:, :1].expand(2, 50, 128).contiguous()
+    v = bf(torch.randn(2, 50, 128, generator=g))
+    o = oracle.attention(q, kk, v)
+    assert int(ulp_diff(o, bf(v.to(torch.float64).mean(1, keepdim=True).expand_as(v))).max()) <= 1
+
+
+@pytest.mark.parametrize("N,hd", [(7, 64), (64, 128), (33, 128)])
+def test_attention_brute_force_float64(N, hd):
+    g = torch.Generator().manual_seed(N + hd)
+    q = bf(torch.randn(3, N, hd, generator=g) * 2)
+    k = bf(torch.randn(3, N, hd, generator=g) * 2)
+    v = bf(torch.randn(3, N, hd, generator=g))
+    o, mx, sm = oracle.attention(q, k, v, stats=True)
+    q64, k64, v64 = (t.to(torch.float64) for t in (q, k, v))
+    ref = F.scaled_dot_product_attention(q64, k64, v64)
+    assert int(ulp_diff(o, bf(ref)).max()) <= 1
+    s = (q64 @ k64.transpose(1, 2)) / math.sqrt(hd)
+    assert torch.allclose(mx.to(torch.float64), s.amax(-1), rtol=1e-5, atol=1e-5)
+    p = torch.exp(s - s.amax(-1, keepdim=True)).sum(-1)
+    assert torch.allclose(sm.to(torch.float64), p, rtol=1e-5)
+    # one-hot values read the probabilities out: column j of O is P[:, j]
+    eye = torch.zeros(3, N, hd, dtype=torch.bfloat16)
+    for j in range(min(N, hd)):
+        eye[:, j, j] = 1
+    P = torch.softmax(s, -1)
+    o1 = oracle.attention(q, k, eye)
+    assert int(ulp_diff(o1[:, :, : min(N, hd)], bf(P[:, :, : min(N, hd)])).max()) <= 1
+
+
+# ----------------------------------------------------------------------------- gate
+
+def test_gate_closed_forms():
+    g = torch.Generator().manual_seed(12)
+    x = bf(torch.randn(8, 256, generator=g))
+    y = bf(torch.randn(8, 256, generator=g))
+    zero = torch.zeros(256, dtype=torch.bfloat16)
+    assert torch.equal(oracle.gate(x, zero, y).view(torch.int16), x.view(torch.int16))
+    one = torch.ones(256, dtype=torch.bfloat16)
+    assert torch.all(oracle.gate(x, one, bf(-x.to(torch.float32))).to(torch.float32) == 0)
+    gg = bf(torch.randn(256, generator=g) * 0.1)
+    ref = bf(x.to(torch.float64) + gg.to(torch.float64) * y.to(torch.float64))
+    assert torch.equal(oracle.gate(x, gg, y).view(torch.int16), ref.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- token reduction
+
+def _small_tr(video_w):
+    return WORKLOADS[4].replace(video_t=2, video_h=3, video_w=video_w, n_text=5, n_audio=3,
+                                hidden=256, heads=4, head_dim=64, mlp=1024)
+
+
+@pytest.mark.parametrize("video_w", [6, 7])
+def test_token_pair_and_restore(video_w):
+    w = _small_tr(video_w)
+    g = torch.Generator().manual_seed(13)
+    x = bf(torch.randn(w.n_tokens, 256, generator=g))
+    r = oracle.token_pair(w, x)
+    wr = video_w // 2 + video_w % 2
+    assert r.shape[0] == 6 * wr + 8
+    xv = x[: w.n_video].view(6, video_w, 256).to(torch.float64)
+    rv = r[: 6 * wr].view(6, wr, 256)
+    mean = bf((xv[:, 0: 2 * (video_w // 2): 2] + xv[:, 1: 2 * (video_w // 2): 2]) / 2)
+    assert torch.equal(rv[:, : video_w // 2].contiguous().view(torch.int16), mean.view(torch.int16))
+    if video_w % 2:
+        assert torch.equal(rv[:, -1].view(torch.int16), x[: w.n_video].view(6, video_w, 256)[:, -1].view(torch.int16))
+    assert torch.equal(r[6 * wr:].view(torch.int16), x[w.n_video:].view(torch.int16))
+    # restore with an unchanged reduced residual is the identity on every token
+    back = oracle.token_restore(w, x, r, r)
+    assert torch.equal(back.view(torch.int16), x.view(torch.int16))
+    # restore = bypass + (pair update); unpaired, text and audio take the new value
+    y = bf(r.to(torch.float32) + torch.randn(r.shape, generator=g) * 0.1)
+    back = oracle.token_restore(w, x, y, r)
+    upd = y.to(torch.float32) - r.to(torch.float32)
+    for row in range(6):
+        for c in range(video_w):
+            i = row * video_w + c
+            p = row * wr + min(c // 2, wr - 1)
+            if c // 2 < video_w // 2:
+                exp = bf(x[i].to(torch.float32) + upd[p])
+            else:
+                exp = y[p]
+            assert torch.equal(back[i].view(torch.int16), exp.view(torch.int16))
+    assert torch.equal(back[w.n_video:].view(torch.int16), y[6 * wr:].view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- whole block
+
+def _tiny_inputs(seed=1000, w=W0):
+    x = synth.make_x(w, seed)
+    p = synth.make_block(w, seed, 0)
+    return x, p
+
+
+def _zero_gates(p):
+    p = dict(p)
+    mod = p["mod"].clone()
+    mod[2] = 0
+    mod[5] = 0
+    p["mod"] = mod
+    return p
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_block_zero_gates_is_identity(int8):
+    x, p = _tiny_inputs()
+    p = _zero_gates(p)
+    if int8:
+        p = oracle.quantize_block(p)
+    out = oracle.block_fwd(W0, p, x)
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_block_fused_equals_unfused(int8):
+    x, p = _tiny_inputs()
+    if int8:
+        p = oracle.quantize_block(p)
+    a = oracle.block_fwd(W0, p, x, fused=False)
+    b = oracle.block_fwd(W0, p, x, fused=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not torch.equal(a.view(torch.int16), x.view(torch.int16))
+
+
+def torch_block_float64(w, p, x, cos, sin):
+    """The block from library routines in float64, rounded to bf16 at the same points:
+    layer_norm, complex rotation, scaled_dot_product_attention, tanh-GELU, matmul."""
+    N, d, H, hd = x.shape[0], w.hidden, w.heads, w.head_dim
+    D = torch.float64
+    mod = p["mod"].to(D)
+
+    def adaln(v, sh, sc):
+        return bf(F.layer_norm(v.to(D), (d,), eps=w.ln_eps) * (1 + sc) + sh)
+
+    h1 = adaln(x, mod[0], mod[1])
+    t = bf(h1.to(D) @ p["wqkv"].to(D).T)
+    tq = t.view(N, 3, H, hd).permute(1, 2, 0, 3).to(D)
+    rot = torch.complex(cos.to(D), sin.to(D))
+    def rope(z):
+        return bf(torch.view_as_real(torch.view_as_complex(z.reshape(H, N, hd // 2, 2).contiguous()) * rot).reshape(H, N, hd))
+    q, k, v = rope(tq[0]), rope(tq[1]), bf(tq[2])
+    o = bf(F.scaled_dot_product_attention(q.to(D), k.to(D), v.to(D)))
+    ot = o.permute(1, 0, 2).reshape(N, d)
+    y1 = bf(ot.to(D) @ p["wo"].to(D).T)
+    x1 = bf(x.to(D) + mod[2] * y1.to(D))
+    h2 = adaln(x1, mod[3], mod[4])
+    u = bf(h2.to(D) @ p["w1"].to(D).T)
+    gl = bf(F.gelu(u.to(D), approximate="tanh"))
+    y2 = bf(gl.to(D) @ p["w2"].to(D).T)
+    return bf(x1.to(D) + mod[5] * y2.to(D)), {"h1": h1, "q": q, "k": k, "v": v, "o": o, "y1": y1,
+                                              "x1": x1, "h2": h2, "u": u, "gl": gl, "y2": y2}
+
+
+def test_block_against_float64_library_composition():
+    x, p = _tiny_inputs()
+    cos, sin = oracle.rope_tables(W0)
+    out, taps = oracle.block_fwd(W0, p, x, cos, sin, taps=True)
+    ref, rt = torch_block_float64(W0, p, x, cos, sin)
+    for name in ("h1", "q", "k", "v", "o", "y1", "x1", "h2", "u", "gl", "y2"):
+        assert relerr(taps[name], rt[name]) < 2e-2, name
+    assert relerr(out, ref) < 2e-2
+    # the update itself (out - x) also agrees, not just the dominant residual
+    assert relerr(out.to(torch.float64) - x.to(torch.float64), ref.to(torch.float64) - x.to(torch.float64)) < 3e-2
+
+
+def test_int8_block_close_to_bf16_block():
+    x, p = _tiny_inputs()
+    # the int8 codes only perturb the projections: branch outputs stay within a few percent
+    _, ta = oracle.block_fwd(W0, p, x, taps=True)
+    _, tb = oracle.block_fwd(W0, oracle.quantize_block(p), x, taps=True)
+    for name in ("t", "y1", "u", "y2"):
+        assert relerr(tb[name], ta[name]) < 0.05, name
+
+
+# ----------------------------------------------------------------------------- stack
+
+def _stack_inputs(w, n_blocks, seed=1000):
+    x = synth.make_x(w, seed)
+    blocks = [synth.make_block(w, seed, b) for b in range(n_blocks)]
+    return x, blocks
+
+
+def test_stack_fused_equals_unfused_and_chains_blocks():
+    w = W0
+    x, blocks = _stack_inputs(w, 3)
+    a = oracle.stack_fwd(w, blocks, x, fused=False)
+    b = oracle.stack_fwd(w, blocks, x, fused=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    y = x
+    for p in blocks:
+        y = oracle.block_fwd(w, p, y)
+    assert torch.equal(a.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("video_w", [6, 7])
+def test_stack_reduction_with_identity_middle_is_identity(video_w):
+    # gates 0 in the reduced span: pair then restore returns every token unchanged, so the
+    # stack equals the unreduced stack whose middle blocks are skipped
+    w = _small_tr(video_w)
+    x, blocks = _stack_inputs(w, 5)
+    for b in (2, 3):
+        blocks[b] = _zero_gates(blocks[b])
+    out = oracle.stack_fwd(w, blocks, x, reduce_after=1, restore_before=4, fused=True)
+    ref = oracle.stack_fwd(w, [blocks[0], blocks[1], blocks[4]], x)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_stack_reduction_matches_stepwise():
+    w = _small_tr(7)
+    x, blocks = _stack_inputs(w, 4)
+    out = oracle.stack_fwd(w, blocks, x, reduce_after=0, restore_before=3, fused=True)
+    cr, sr = oracle.rope_tables(w, reduced=True)
+    y = oracle.block_fwd(w, blocks[0], x)
+    r = oracle.token_pair(w, y)
+    z = oracle.block_fwd(w, blocks[1], r, cr, sr)
+    z = oracle.block_fwd(w, blocks[2], z, cr, sr)
+    y = oracle.token_restore(w, y, z, r)
+    y = oracle.block_fwd(w, blocks[3], y)
+    assert torch.equal(out.view(torch.int16), y.view(torch.int16))
