@@ -1,0 +1,274 @@
+"""Python binding of libh3dit.so, the MI355X (gfx950) MiniMax-H3 DiT block library.
+
+Argument marshalling only: every step of the block runs in the library's HIP kernels.
+torch supplies device memory and the current stream.  Importing this package without the
+built library raises ImportError; there is no fallback path.
+
+Entry points mirror include/h3dit.h (quantize_weights, block_fwd, stack_fwd) and
+include/h3dit_stages.h (one call per kernel, used for stage-wise checks and timing).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libh3dit.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "or `python audio_diffusion_transformer_dit_amd/build.py`")
+
+_lib = C.CDLL(LIB_PATH)
+
+OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+BF16, INT8 = 0, 1
+NOFUSE_GATE_ADALN, NOFUSE_ROPE, NOFUSE_GELU, NOFUSE_QUANT, NOFUSE_CROSS_BLOCK, NO_ALIAS = 1, 2, 4, 8, 16, 32
+OUT_BF16, OUT_F32, OUT_I32, OUT_GELU, OUT_QKV = 0, 1, 2, 3, 4
+
+EXPORTS = ("h3dit_quantize_weights", "h3dit_block_fwd", "h3dit_stack_fwd", "h3dit_rope_tables",
+           "h3dit_row_gate_adaln", "h3dit_quantize_rows", "h3dit_linear", "h3dit_rope_split", "h3dit_gelu",
+           "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore")
+
+
+class H3Error(RuntimeError):
+    def __init__(self, name, code):
+        names = {EINVAL: "EINVAL", EWORKSPACE: "EWORKSPACE", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP"}
+        super().__init__(f"{name} failed: {names.get(code, code)}")
+        self.code = code
+
+
+class Dims(C.Structure):
+    _fields_ = [("n_tokens", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
+                ("mlp", C.c_int32), ("fc2_group", C.c_int32), ("ln_eps", C.c_float)]
+
+
+class Layout(C.Structure):
+    _fields_ = [("video_t", C.c_int32), ("video_h", C.c_int32), ("video_w", C.c_int32), ("n_text", C.c_int32),
+                ("n_audio", C.c_int32), ("rope_t", C.c_int32), ("rope_h", C.c_int32), ("rope_w", C.c_int32),
+                ("rope_theta", C.c_float)]
+
+
+class BlockW(C.Structure):
+    _fields_ = [("precision", C.c_int32), ("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("w_fc1", C.c_void_p),
+                ("w_fc2", C.c_void_p), ("s_qkv", C.c_void_p), ("s_o", C.c_void_p), ("s_fc1", C.c_void_p),
+                ("s_fc2", C.c_void_p), ("mod", C.c_void_p)]
+
+
+class TokenReduction(C.Structure):
+    _fields_ = [("reduce_after", C.c_int32), ("restore_before", C.c_int32)]
+
+
+class LinearArgs(C.Structure):
+    _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64), ("precision", C.c_int32),
+                ("a", C.c_void_p), ("a_headmajor_hd", C.c_int32), ("a_scale", C.c_void_p), ("a_group", C.c_int32),
+                ("w", C.c_void_p), ("w_scale", C.c_void_p), ("out_kind", C.c_int32), ("out", C.c_void_p),
+                ("cos_t", C.c_void_p), ("sin_t", C.c_void_p), ("heads", C.c_int32), ("head_dim", C.c_int32),
+                ("out_q", C.c_void_p), ("out_k", C.c_void_p), ("out_v", C.c_void_p)]
+
+
+_P = C.c_void_p
+_lib.h3dit_quantize_weights.argtypes = [_P, C.c_int64, C.c_int64, _P, _P, _P]
+_lib.h3dit_block_fwd.argtypes = [_P, _P, _P, _P, C.c_uint32, _P, _P, _P]
+_lib.h3dit_stack_fwd.argtypes = [_P, _P, C.c_int32, _P, _P, _P, C.c_uint32, _P, _P, _P]
+_lib.h3dit_rope_tables.argtypes = [_P, C.c_int32, C.c_int32, _P, _P, _P]
+_lib.h3dit_row_gate_adaln.argtypes = [C.c_int64, C.c_int32, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.h3dit_quantize_rows.argtypes = [C.c_int64, C.c_int64, C.c_int64, _P, C.c_int32, _P, _P, _P]
+_lib.h3dit_linear.argtypes = [_P, _P]
+_lib.h3dit_rope_split.argtypes = [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
+_lib.h3dit_gelu.argtypes = [C.c_int64, _P, _P, _P]
+_lib.h3dit_attention.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
+_lib.h3dit_token_pair.argtypes = [_P, C.c_int32, _P, _P, _P, _P]
+_lib.h3dit_token_restore.argtypes = [_P, C.c_int32, _P, _P, _P, _P]
+for _n in EXPORTS:
+    getattr(_lib, _n).restype = C.c_int
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(name, rc):
+    if rc < 0:
+        raise H3Error(name, rc)
+    return rc
+
+
+def dims_of(w, n_tokens=None) -> Dims:
+    return Dims(int(w.n_tokens if n_tokens is None else n_tokens), w.hidden, w.heads, w.head_dim, w.mlp,
+                w.fc2_group, w.ln_eps)
+
+
+def layout_of(w) -> Layout:
+    st, sh, sw = w.split
+    return Layout(w.video_t, w.video_h, w.video_w, w.n_text, w.n_audio, st, sh, sw, w.rope_theta)
+
+
+def ldv(n: int) -> int:
+    """Row pitch of V^T [H][hd][ldv]: tokens rounded up to a multiple of 8."""
+    return (int(n) + 7) // 8 * 8
+
+
+# ------------------------------------------------------------------ h3dit.h
+
+def quantize_weights(w: torch.Tensor, stream=None):
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=w.device)
+    s = torch.empty(rows, dtype=torch.float32, device=w.device)
+    _check("h3dit_quantize_weights", _lib.h3dit_quantize_weights(_ptr(w), rows, cols, _ptr(q), _ptr(s), _stream(stream)))
+    return q, s
+
+
+def block_struct(p: dict) -> BlockW:
+    """p: {wqkv, wo, w1, w2, mod} bf16 device tensors, or int8 codes {qqkv, qo, q1, q2} with
+    scales {sqkv, so, s1, s2} and mod."""
+    if "qqkv" in p:
+        return BlockW(INT8, _ptr(p["qqkv"]), _ptr(p["qo"]), _ptr(p["q1"]), _ptr(p["q2"]), _ptr(p["sqkv"]),
+                      _ptr(p["so"]), _ptr(p["s1"]), _ptr(p["s2"]), _ptr(p["mod"]))
+    return BlockW(BF16, _ptr(p["wqkv"]), _ptr(p["wo"]), _ptr(p["w1"]), _ptr(p["w2"]), None, None, None, None,
+                  _ptr(p["mod"]))
+
+
+def quantize_block(p: dict, stream=None) -> dict:
+    out = {"mod": p["mod"]}
+    for w, q, s in (("wqkv", "qqkv", "sqkv"), ("wo", "qo", "so"), ("w1", "q1", "s1"), ("w2", "q2", "s2")):
+        out[q], out[s] = quantize_weights(p[w], stream)
+    return out
+
+
+def block_workspace(w, p: dict, flags: int = 0) -> int:
+    size = C.c_size_t(0)
+    b = block_struct(p)
+    _check("h3dit_block_fwd", _lib.h3dit_block_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), C.byref(b), None,
+                                                   flags, None, C.byref(size), None))
+    return size.value
+
+
+def stack_workspace(w, blocks: list, flags: int = 0, reduction=None) -> int:
+    size = C.c_size_t(0)
+    arr = (BlockW * len(blocks))(*[block_struct(p) for p in blocks])
+    tr = TokenReduction(*reduction) if reduction else None
+    _check("h3dit_stack_fwd", _lib.h3dit_stack_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), len(blocks), arr,
+                                                   C.byref(tr) if tr else None, None, flags, None, C.byref(size),
+                                                   None))
+    return size.value
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def block_fwd(w, p: dict, x: torch.Tensor, flags: int = 0, workspace: torch.Tensor = None, stream=None):
+    """x (bf16 [N][d], device) is updated in place and returned."""
+    b = block_struct(p)
+    if workspace is None:
+        workspace = alloc_workspace(block_workspace(w, p, flags), x.device)
+    size = C.c_size_t(workspace.numel())
+    _check("h3dit_block_fwd", _lib.h3dit_block_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), C.byref(b), _ptr(x),
+                                                   flags, _ptr(workspace), C.byref(size), _stream(stream)))
+    return x
+
+
+class Stack:
+    """Holds the host-side block array of a stack so repeated calls marshal nothing new."""
+
+    def __init__(self, w, blocks: list, flags: int = 0, reduction=None):
+        self.w = w
+        self.blocks = blocks
+        self.flags = flags
+        self.arr = (BlockW * len(blocks))(*[block_struct(p) for p in blocks])
+        self.tr = TokenReduction(*reduction) if reduction else None
+        self.dims = dims_of(w)
+        self.layout = layout_of(w)
+        self.workspace_bytes = stack_workspace(w, blocks, flags, reduction)
+
+    def __call__(self, x: torch.Tensor, workspace: torch.Tensor, stream=None):
+        size = C.c_size_t(workspace.numel())
+        _check("h3dit_stack_fwd", _lib.h3dit_stack_fwd(C.byref(self.dims), C.byref(self.layout), len(self.blocks),
+                                                       self.arr, C.byref(self.tr) if self.tr else None, _ptr(x),
+                                                       self.flags, _ptr(workspace), C.byref(size), _stream(stream)))
+        return x
+
+
+def stack_fwd(w, blocks: list, x: torch.Tensor, flags: int = 0, reduction=None, workspace=None, stream=None):
+    s = Stack(w, blocks, flags, reduction)
+    if workspace is None:
+        workspace = alloc_workspace(s.workspace_bytes, x.device)
+    return s(x, workspace, stream)
+
+
+# ------------------------------------------------------------------ h3dit_stages.h
+
+def rope_tables(w, reduced=False, device="cuda", stream=None):
+    n = w.n_tokens if not reduced else (w.video_t * w.video_h * (w.video_w // 2 + w.video_w % 2) + w.n_text + w.n_audio)
+    cos = torch.empty((n, w.head_dim // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check("h3dit_rope_tables", _lib.h3dit_rope_tables(C.byref(layout_of(w)), w.head_dim, int(reduced), _ptr(cos),
+                                                       _ptr(sin), _stream(stream)))
+    return cos, sin
+
+
+def row_gate_adaln(x, gate=None, y=None, x_out=None, shift=None, scale=None, h=None, q=None, s=None, eps=1e-6,
+                   stream=None):
+    n, d = x.shape
+    _check("h3dit_row_gate_adaln", _lib.h3dit_row_gate_adaln(n, d, eps, _ptr(x), _ptr(gate), _ptr(y), _ptr(x_out),
+                                                             _ptr(shift), _ptr(scale), _ptr(h), _ptr(q), _ptr(s),
+                                                             _stream(stream)))
+
+
+def quantize_rows(v, rows, cols, group, headmajor_hd=0, stream=None):
+    q = torch.empty((rows, cols), dtype=torch.int8, device=v.device)
+    s = torch.empty((rows, cols // group), dtype=torch.float32, device=v.device)
+    _check("h3dit_quantize_rows", _lib.h3dit_quantize_rows(rows, cols, group, _ptr(v), headmajor_hd, _ptr(q), _ptr(s),
+                                                           _stream(stream)))
+    return q, s
+
+
+def linear(M, N, K, a, w, out_kind=OUT_BF16, out=None, precision=BF16, a_headmajor_hd=0, a_scale=None, a_group=0,
+           w_scale=None, cos=None, sin=None, heads=0, head_dim=0, out_q=None, out_k=None, out_v=None, stream=None):
+    args = LinearArgs(M, N, K, precision, _ptr(a), a_headmajor_hd, _ptr(a_scale), a_group, _ptr(w), _ptr(w_scale),
+                      out_kind, _ptr(out), _ptr(cos), _ptr(sin), heads, head_dim, _ptr(out_q), _ptr(out_k),
+                      _ptr(out_v))
+    _check("h3dit_linear", _lib.h3dit_linear(C.byref(args), _stream(stream)))
+
+
+def rope_split(n, heads, head_dim, t, cos, sin, q, k, vt, stream=None):
+    _check("h3dit_rope_split", _lib.h3dit_rope_split(n, heads, head_dim, _ptr(t), _ptr(cos), _ptr(sin), _ptr(q),
+                                                     _ptr(k), _ptr(vt), _stream(stream)))
+
+
+def gelu(u, gl, stream=None):
+    _check("h3dit_gelu", _lib.h3dit_gelu(u.numel(), _ptr(u), _ptr(gl), _stream(stream)))
+
+
+def attention(heads, n, head_dim, q, k, vt, o, row_max=None, row_sum=None, stream=None):
+    _check("h3dit_attention", _lib.h3dit_attention(heads, n, head_dim, _ptr(q), _ptr(k), _ptr(vt), _ptr(o),
+                                                   _ptr(row_max), _ptr(row_sum), _stream(stream)))
+
+
+def token_pair(w, x, r, r_in=None, stream=None):
+    _check("h3dit_token_pair", _lib.h3dit_token_pair(C.byref(layout_of(w)), x.shape[1], _ptr(x), _ptr(r), _ptr(r_in),
+                                                     _stream(stream)))
+
+
+def token_restore(w, x, y, r_in, stream=None):
+    _check("h3dit_token_restore", _lib.h3dit_token_restore(C.byref(layout_of(w)), x.shape[1], _ptr(x), _ptr(y),
+                                                           _ptr(r_in), _stream(stream)))

@@ -1,0 +1,493 @@
+// C ABI of the H3 DiT block library: argument validation, the workspace (arena) plan, and
+// the launch sequence of one block and of a stack of blocks.  Every arithmetic step runs in
+// the kernels of rowops.hip, gemm.hip and attention.hip; this file only orders launches.
+//
+// Arena plan ([DD] "DiT 融合内核", 激活缓冲别名: activations follow their lifetime inside the
+// block; the QKV arena is reused for the attention heads and then for the normalised MLP
+// input, and the attention-output arena becomes the MLP output):
+//   A  q | k | V^T  ->  attention output over q  ->  MLP input (h2 / int8 q2)  ->  int8 FC2 input
+//   B  out-projection output y1  ->  FC2 output y2
+//   C  AdaLN1 output (h1 / int8 q1)  ->  int8 attention output codes  ->  FC1+GELU output
+// With H3DIT_NO_ALIAS each of these gets its own region.
+#include <string.h>
+
+#include <atomic>
+
+#include "common.hpp"
+
+namespace {
+
+using namespace h3;
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t layout_tokens(const h3dit_layout &L, bool reduced) {
+  const int64_t wr = reduced ? (L.video_w / 2 + L.video_w % 2) : L.video_w;
+  return (int64_t)L.video_t * L.video_h * wr + L.n_text + L.n_audio;
+}
+
+int check_dims(const h3dit_dims *D, const h3dit_layout *L, int precision) {
+  if (!D || !L) return H3DIT_EINVAL;
+  if (D->n_tokens < 1 || D->heads < 1 || D->hidden != D->heads * D->head_dim) return H3DIT_EINVAL;
+  if (D->head_dim != 64 && D->head_dim != 128) return H3DIT_EUNSUPPORTED;
+  if (D->hidden % 256 || D->hidden > 8192 || D->mlp < 256 || D->mlp % 256) return H3DIT_EINVAL;
+  if (!(D->ln_eps >= 0.0f)) return H3DIT_EINVAL;
+  if (precision != H3DIT_BF16 && precision != H3DIT_INT8) return H3DIT_EINVAL;
+  if (precision == H3DIT_INT8) {
+    if (D->fc2_group < 128 || D->fc2_group % 128 || D->fc2_group > 8192 || D->mlp % D->fc2_group) return H3DIT_EINVAL;
+  }
+  if (L->video_t < 0 || L->video_h < 0 || L->video_w < 0 || L->n_text < 0 || L->n_audio < 0) return H3DIT_EINVAL;
+  if (layout_tokens(*L, false) != D->n_tokens) return H3DIT_EINVAL;
+  if (L->rope_t < 0 || L->rope_h < 0 || L->rope_w < 0 || (L->rope_t | L->rope_h | L->rope_w) & 1 ||
+      L->rope_t + L->rope_h + L->rope_w != D->head_dim || !(L->rope_theta > 0.0f))
+    return H3DIT_EINVAL;
+  // 32-bit buffer offsets inside the kernels
+  if ((int64_t)D->n_tokens * D->mlp * 2 >= ((int64_t)1 << 31)) return H3DIT_EINVAL;
+  return H3DIT_OK;
+}
+
+int check_block(const h3dit_block_w *b, int precision) {
+  if (!b || b->precision != precision) return H3DIT_EINVAL;
+  const void *w[4] = {b->w_qkv, b->w_o, b->w_fc1, b->w_fc2};
+  for (const void *p : w)
+    if (!p || !aligned(p, 16)) return H3DIT_EINVAL;
+  if (!b->mod || !aligned(b->mod, 16)) return H3DIT_EINVAL;
+  if (precision == H3DIT_INT8) {
+    const float *s[4] = {b->s_qkv, b->s_o, b->s_fc1, b->s_fc2};
+    for (const float *p : s)
+      if (!p || !aligned(p, 4)) return H3DIT_EINVAL;
+  }
+  return H3DIT_OK;
+}
+
+// gfx950 check, once per device
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return H3DIT_EHIP;
+  if (dev < 0 || dev >= 64) return H3DIT_EUNSUPPORTED;
+  int v = g_arch_ok[dev].load();
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return H3DIT_EHIP;
+    v = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(v);
+  }
+  return v == 1 ? H3DIT_OK : H3DIT_EUNSUPPORTED;
+}
+
+struct Plan {
+  size_t total = 0;
+  size_t cos_f = 0, sin_f = 0, cos_r = 0, sin_r = 0;
+  size_t q = 0, k = 0, vt = 0, o = 0, h2 = 0, qg = 0;  // arena A roles
+  size_t y1 = 0, y2 = 0;                              // arena B roles
+  size_t h1 = 0, qo = 0, gl = 0;                      // arena C roles
+  size_t t = 0, hb = 0;                               // unfused-only regions
+  size_t sa = 0, sg = 0;                              // per-token / per-group scales
+  size_t red = 0, r_in = 0;                           // token reduction
+};
+
+Plan make_plan(const h3dit_dims &D, const h3dit_layout &L, int precision, uint32_t flags, bool reduction) {
+  const size_t N = (size_t)D.n_tokens, d = (size_t)D.hidden, f = (size_t)D.mlp, hd = (size_t)D.head_dim;
+  const size_t ldv = (N + 7) / 8 * 8;
+  const bool i8 = precision == H3DIT_INT8;
+  const size_t Nd2 = N * d * 2;
+  Plan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  p.cos_f = take(N * hd / 2 * 4);
+  p.sin_f = take(N * hd / 2 * 4);
+  if (reduction) {
+    const size_t Nr = (size_t)layout_tokens(L, true);
+    p.cos_r = take(Nr * hd / 2 * 4);
+    p.sin_r = take(Nr * hd / 2 * 4);
+    p.red = take(Nr * d * 2);
+    p.r_in = take(Nr * d * 2);
+  }
+  p.sa = take(N * 4);
+  if (i8) p.sg = take(N * (f / (size_t)D.fc2_group) * 4);
+  if (flags & H3DIT_NOFUSE_ROPE) p.t = take(3 * Nd2);
+  if (flags & H3DIT_NOFUSE_QUANT) p.hb = take(Nd2);
+  const size_t qkv = 2 * Nd2 + d * ldv * 2;
+  if (!(flags & H3DIT_NO_ALIAS)) {
+    const size_t A = take(i8 ? (qkv > N * f ? qkv : N * f) : qkv);
+    const size_t B = take(Nd2);
+    const size_t C = take(N * f * 2 > Nd2 ? N * f * 2 : Nd2);
+    p.q = A; p.k = A + Nd2; p.vt = A + 2 * Nd2; p.o = A; p.h2 = A; p.qg = A;
+    p.y1 = B; p.y2 = B;
+    p.h1 = C; p.qo = C; p.gl = C;
+  } else {
+    p.q = take(Nd2); p.k = take(Nd2); p.vt = take(d * ldv * 2); p.o = take(Nd2);
+    p.h2 = take(Nd2); p.y1 = take(Nd2); p.y2 = take(Nd2); p.h1 = take(Nd2); p.gl = take(N * f * 2);
+    if (i8) { p.qo = take(N * d); p.qg = take(N * f); }
+  }
+  p.total = off;
+  return p;
+}
+
+#define TRY(expr)                                   \
+  do {                                              \
+    if ((expr) != hipSuccess) return H3DIT_EHIP;    \
+  } while (0)
+
+struct Ctx {
+  const h3dit_dims *D;
+  uint32_t flags;
+  uint8_t *ws;
+  Plan P;
+  hipStream_t st;
+  template <class T>
+  T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
+};
+
+// AdaLN (with optional gate) producing the projection input of the next GEMM: bf16 into
+// dst_bf16, or int8 codes into dst_q plus per-token scales.
+int adaln_into(const Ctx &c, int64_t n, const uint16_t *x, const uint16_t *gate, const uint16_t *y, uint16_t *x_out,
+               const uint16_t *shift, const uint16_t *scale, bool i8, size_t dst) {
+  const int d = c.D->hidden;
+  if (!i8) {
+    TRY(launch_row(n, d, c.D->ln_eps, x, gate, y, x_out, shift, scale, c.at<uint16_t>(dst), nullptr, nullptr, c.st));
+  } else if (!(c.flags & H3DIT_NOFUSE_QUANT)) {
+    TRY(launch_row(n, d, c.D->ln_eps, x, gate, y, x_out, shift, scale, nullptr, c.at<int8_t>(dst), c.at<float>(c.P.sa),
+                   c.st));
+  } else {
+    TRY(launch_row(n, d, c.D->ln_eps, x, gate, y, x_out, shift, scale, c.at<uint16_t>(c.P.hb), nullptr, nullptr, c.st));
+    TRY(launch_quant_rows(n, d, d, c.at<uint16_t>(c.P.hb), 0, c.at<int8_t>(dst), c.at<float>(c.P.sa), c.st));
+  }
+  return H3DIT_OK;
+}
+
+// One block on x [n][d].  h1_ready: AdaLN1 output already in place (produced by the previous
+// block's final gate).  next: block whose AdaLN1 the final gate also produces, or NULL.
+int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, const h3dit_block_w &b, uint16_t *x,
+              bool h1_ready, const h3dit_block_w *next) {
+  const h3dit_dims &D = *c.D;
+  const int d = D.hidden, H = D.heads, hd = D.head_dim, f = D.mlp;
+  const bool i8 = b.precision == H3DIT_INT8;
+  const uint32_t F = c.flags;
+  const uint16_t *mod = b.mod;
+  const uint16_t *sh1 = mod, *sc1 = mod + d, *g1 = mod + 2 * d, *sh2 = mod + 3 * d, *sc2 = mod + 4 * d, *g2 = mod + 5 * d;
+  const Plan &P = c.P;
+  int rc;
+
+  // AdaLN1
+  if (!h1_ready && (rc = adaln_into(c, n, x, nullptr, nullptr, nullptr, sh1, sc1, i8, P.h1)) != H3DIT_OK) return rc;
+
+  // QKV projection + rotary + head-major split
+  h3dit_linear_args la{};
+  la.M = n; la.N = 3 * d; la.K = d;
+  la.precision = b.precision;
+  la.a = c.at<void>(P.h1);
+  la.a_scale = i8 ? c.at<float>(P.sa) : nullptr;
+  la.w = b.w_qkv;
+  la.w_scale = b.s_qkv;
+  la.cos_t = cos_t; la.sin_t = sin_t; la.heads = H; la.head_dim = hd;
+  if (!(F & H3DIT_NOFUSE_ROPE)) {
+    la.out_kind = H3DIT_OUT_QKV;
+    la.out_q = c.at<uint16_t>(P.q); la.out_k = c.at<uint16_t>(P.k); la.out_v = c.at<uint16_t>(P.vt);
+    TRY(launch_linear(la, c.st));
+  } else {
+    la.out_kind = H3DIT_OUT_BF16;
+    la.out = c.at<void>(P.t);
+    TRY(launch_linear(la, c.st));
+    TRY(launch_rope_split(n, H, hd, c.at<uint16_t>(P.t), cos_t, sin_t, c.at<uint16_t>(P.q), c.at<uint16_t>(P.k),
+                          c.at<uint16_t>(P.vt), c.st));
+  }
+
+  // attention (output over q in the aliased plan)
+  TRY(launch_attention(H, n, hd, c.at<uint16_t>(P.q), c.at<uint16_t>(P.k), c.at<uint16_t>(P.vt), c.at<uint16_t>(P.o),
+                       nullptr, nullptr, c.st));
+
+  // output projection
+  la = h3dit_linear_args{};
+  la.M = n; la.N = d; la.K = d; la.precision = b.precision; la.w = b.w_o; la.w_scale = b.s_o;
+  la.out_kind = H3DIT_OUT_BF16; la.out = c.at<void>(P.y1);
+  if (!i8) {
+    la.a = c.at<void>(P.o);
+    la.a_headmajor_hd = hd;
+  } else {
+    TRY(launch_quant_rows(n, d, d, c.at<uint16_t>(P.o), hd, c.at<int8_t>(P.qo), c.at<float>(P.sa), c.st));
+    la.a = c.at<void>(P.qo);
+    la.a_scale = c.at<float>(P.sa);
+  }
+  TRY(launch_linear(la, c.st));
+
+  // gate1 + AdaLN2
+  if (!(F & H3DIT_NOFUSE_GATE_ADALN)) {
+    if ((rc = adaln_into(c, n, x, g1, c.at<uint16_t>(P.y1), x, sh2, sc2, i8, P.h2)) != H3DIT_OK) return rc;
+  } else {
+    TRY(launch_row(n, d, D.ln_eps, x, g1, c.at<uint16_t>(P.y1), x, nullptr, nullptr, nullptr, nullptr, nullptr, c.st));
+    if ((rc = adaln_into(c, n, x, nullptr, nullptr, nullptr, sh2, sc2, i8, P.h2)) != H3DIT_OK) return rc;
+  }
+
+  // FC1 + GELU
+  la = h3dit_linear_args{};
+  la.M = n; la.N = f; la.K = d; la.precision = b.precision; la.w = b.w_fc1; la.w_scale = b.s_fc1;
+  la.a = c.at<void>(P.h2); la.a_scale = i8 ? c.at<float>(P.sa) : nullptr;
+  la.out = c.at<void>(P.gl);
+  la.out_kind = (F & H3DIT_NOFUSE_GELU) ? H3DIT_OUT_BF16 : H3DIT_OUT_GELU;
+  TRY(launch_linear(la, c.st));
+  if (F & H3DIT_NOFUSE_GELU) TRY(launch_gelu((int64_t)n * f, c.at<uint16_t>(P.gl), c.at<uint16_t>(P.gl), c.st));
+
+  // FC2
+  la = h3dit_linear_args{};
+  la.M = n; la.N = d; la.K = f; la.precision = b.precision; la.w = b.w_fc2; la.w_scale = b.s_fc2;
+  la.out_kind = H3DIT_OUT_BF16; la.out = c.at<void>(P.y2);
+  if (!i8) {
+    la.a = c.at<void>(P.gl);
+  } else {
+    TRY(launch_quant_rows(n, f, D.fc2_group, c.at<uint16_t>(P.gl), 0, c.at<int8_t>(P.qg), c.at<float>(P.sg), c.st));
+    la.a = c.at<void>(P.qg);
+    la.a_scale = c.at<float>(P.sg);
+    la.a_group = D.fc2_group;
+  }
+  TRY(launch_linear(la, c.st));
+
+  // gate2, optionally with the next block's AdaLN1
+  if (next) {
+    const bool ni8 = next->precision == H3DIT_INT8;
+    if ((rc = adaln_into(c, n, x, g2, c.at<uint16_t>(P.y2), x, next->mod, next->mod + d, ni8, P.h1)) != H3DIT_OK)
+      return rc;
+  } else {
+    TRY(launch_row(n, d, D.ln_eps, x, g2, c.at<uint16_t>(P.y2), x, nullptr, nullptr, nullptr, nullptr, nullptr, c.st));
+  }
+  return H3DIT_OK;
+}
+
+int prepare(const h3dit_dims *dims, const h3dit_layout *layout, int precision, uint32_t flags, bool reduction,
+            uint16_t *x, void *workspace, size_t *workspace_bytes, Plan &plan) {
+  if (!workspace_bytes) return H3DIT_EINVAL;
+  if (flags & ~(uint32_t)63) return H3DIT_EINVAL;
+  int rc = check_dims(dims, layout, precision);
+  if (rc) return rc;
+  plan = make_plan(*dims, *layout, precision, flags, reduction);
+  if (!workspace) {
+    *workspace_bytes = plan.total;
+    return 1;  // size query answered
+  }
+  if (!x || !aligned(x, 16) || !aligned(workspace, ALIGN)) return H3DIT_EINVAL;
+  if (*workspace_bytes < plan.total) {
+    *workspace_bytes = plan.total;
+    return H3DIT_EWORKSPACE;
+  }
+  return H3DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3dit_quantize_weights(const uint16_t *w, int64_t rows, int64_t cols, int8_t *q, float *s, void *stream) {
+  if (!w || !q || !s || rows < 0 || cols < 8 || cols % 8 || rows > INT32_MAX) return H3DIT_EINVAL;
+  if (!aligned(w, 16) || !aligned(q, 8) || !aligned(s, 4)) return H3DIT_EINVAL;
+  if (rows == 0) return H3DIT_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_quant_rows(rows, cols, cols, w, 0, q, s, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_block_w *blk, uint16_t *x,
+                    uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream) {
+  if (!blk) return H3DIT_EINVAL;
+  Plan plan;
+  int rc = prepare(dims, layout, blk->precision, flags, false, x, workspace, workspace_bytes, plan);
+  if (rc == 1) return H3DIT_OK;
+  if (rc) return rc;
+  if ((rc = check_block(blk, blk->precision))) return rc;
+  if ((rc = check_device())) return rc;
+  Ctx c{dims, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
+  float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
+  TRY(launch_rope_tables(*layout, dims->head_dim, 0, cf, sf, c.st));
+  return run_block(c, dims->n_tokens, cf, sf, *blk, x, false, nullptr);
+}
+
+int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks, const h3dit_block_w *blocks,
+                    const h3dit_token_reduction *tr, uint16_t *x, uint32_t flags, void *workspace,
+                    size_t *workspace_bytes, void *stream) {
+  if (!blocks || n_blocks < 1) return H3DIT_EINVAL;
+  const int precision = blocks[0].precision;
+  if (tr && (tr->reduce_after < 0 || tr->restore_before <= tr->reduce_after || tr->reduce_after >= n_blocks))
+    return H3DIT_EINVAL;
+  Plan plan;
+  int rc = prepare(dims, layout, precision, flags, tr != nullptr, x, workspace, workspace_bytes, plan);
+  if (rc == 1) return H3DIT_OK;
+  if (rc) return rc;
+  for (int32_t b = 0; b < n_blocks; b++)
+    if ((rc = check_block(&blocks[b], precision))) return rc;
+  if ((rc = check_device())) return rc;
+  Ctx c{dims, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
+  float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
+  float *cr = nullptr, *sr = nullptr;
+  TRY(launch_rope_tables(*layout, dims->head_dim, 0, cf, sf, c.st));
+  if (tr) {
+    cr = c.at<float>(plan.cos_r);
+    sr = c.at<float>(plan.sin_r);
+    TRY(launch_rope_tables(*layout, dims->head_dim, 1, cr, sr, c.st));
+  }
+  const int64_t Nf = dims->n_tokens, Nr = layout_tokens(*layout, true);
+  const int d = dims->hidden;
+  uint16_t *red = tr ? c.at<uint16_t>(plan.red) : nullptr, *r_in = tr ? c.at<uint16_t>(plan.r_in) : nullptr;
+  const bool cross = !(flags & (H3DIT_NOFUSE_CROSS_BLOCK | H3DIT_NOFUSE_GATE_ADALN));
+  bool reduced = false, h1_ready = false;
+  for (int32_t b = 0; b < n_blocks; b++) {
+    if (reduced && b == tr->restore_before) {
+      TRY(launch_token_restore(*layout, d, x, red, r_in, c.st));
+      reduced = false;
+      h1_ready = false;
+    }
+    const bool boundary = (tr && (b == tr->reduce_after || b + 1 == tr->restore_before)) || b + 1 == n_blocks;
+    const h3dit_block_w *next = (cross && !boundary) ? &blocks[b + 1] : nullptr;
+    rc = run_block(c, reduced ? Nr : Nf, reduced ? cr : cf, reduced ? sr : sf, blocks[b], reduced ? red : x, h1_ready,
+                   next);
+    if (rc) return rc;
+    h1_ready = next != nullptr;
+    if (tr && b == tr->reduce_after) {
+      TRY(launch_token_pair(*layout, d, x, red, r_in, c.st));
+      reduced = true;
+      h1_ready = false;
+    }
+  }
+  if (reduced) TRY(launch_token_restore(*layout, d, x, red, r_in, c.st));
+  return H3DIT_OK;
+}
+
+// ---------------------------------------------------------------- stage entry points
+
+int h3dit_rope_tables(const h3dit_layout *L, int32_t head_dim, int32_t reduced, float *cos_t, float *sin_t,
+                      void *stream) {
+  if (!L || !cos_t || !sin_t || (head_dim != 64 && head_dim != 128)) return H3DIT_EINVAL;
+  if (L->video_t < 0 || L->video_h < 0 || L->video_w < 0 || L->n_text < 0 || L->n_audio < 0) return H3DIT_EINVAL;
+  if (L->rope_t < 0 || L->rope_h < 0 || L->rope_w < 0 || (L->rope_t | L->rope_h | L->rope_w) & 1 ||
+      L->rope_t + L->rope_h + L->rope_w != head_dim || !(L->rope_theta > 0.0f))
+    return H3DIT_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_rope_tables(*L, head_dim, reduced ? 1 : 0, cos_t, sin_t, (hipStream_t)stream));
+  return (int)layout_tokens(*L, reduced != 0);
+}
+
+int h3dit_row_gate_adaln(int64_t n, int32_t d, float eps, const uint16_t *x, const uint16_t *gate, const uint16_t *y,
+                         uint16_t *x_out, const uint16_t *shift, const uint16_t *scale, uint16_t *h, int8_t *q,
+                         float *s, void *stream) {
+  if (n < 0 || d < 8 || d % 8 || d > 8192 || !x || !aligned(x, 16)) return H3DIT_EINVAL;
+  if (!gate && !shift) return H3DIT_EINVAL;
+  if (gate && (!y || !x_out || !aligned(gate, 16) || !aligned(y, 16) || !aligned(x_out, 16))) return H3DIT_EINVAL;
+  if (shift && (!scale || !aligned(shift, 16) || !aligned(scale, 16))) return H3DIT_EINVAL;
+  if (shift && !h && !q) return H3DIT_EINVAL;
+  if (h && !aligned(h, 16)) return H3DIT_EINVAL;
+  if (q && (!s || !aligned(q, 8) || !aligned(s, 4))) return H3DIT_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_row(n, d, eps, x, gate, y, x_out, shift, scale, h, q, s, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v, int32_t headmajor_hd, int8_t *q,
+                        float *s, void *stream) {
+  if (rows < 0 || cols < 8 || group < 8 || group % 8 || cols % group || rows > INT32_MAX) return H3DIT_EINVAL;
+  if (headmajor_hd < 0 || (headmajor_hd > 0 && (headmajor_hd % 8 || cols % headmajor_hd || group > 8192)))
+    return H3DIT_EINVAL;
+  if (!v || !q || !s || !aligned(v, 16) || !aligned(q, 8) || !aligned(s, 4)) return H3DIT_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_quant_rows(rows, cols, group, v, headmajor_hd, q, s, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_linear(const h3dit_linear_args *a, void *stream) {
+  if (!a || a->M < 0 || a->N < 128 || a->N % 128 || a->K < 128 || a->K % 128) return H3DIT_EINVAL;
+  if (!a->a || !a->w || !aligned(a->a, 16) || !aligned(a->w, 16)) return H3DIT_EINVAL;
+  const bool i8 = a->precision == H3DIT_INT8;
+  if (!i8 && a->precision != H3DIT_BF16) return H3DIT_EINVAL;
+  const int esz = i8 ? 1 : 2;
+  if ((a->M + 255) * a->K * esz >= ((int64_t)1 << 32) || a->N * a->K * esz >= ((int64_t)1 << 32)) return H3DIT_EINVAL;
+  if (a->a_headmajor_hd && (i8 || (a->a_headmajor_hd != 64 && a->a_headmajor_hd != 128) || a->K % a->a_headmajor_hd))
+    return H3DIT_EINVAL;
+  if (i8) {
+    if (!a->a_scale || !a->w_scale) return H3DIT_EINVAL;
+    if (a->a_group && (a->a_group % 128 || a->K % a->a_group || a->out_kind != H3DIT_OUT_BF16)) return H3DIT_EINVAL;
+    if (a->out_kind == H3DIT_OUT_F32) return H3DIT_EINVAL;
+  } else if (a->out_kind == H3DIT_OUT_I32 || a->a_group) {
+    return H3DIT_EINVAL;
+  }
+  if (a->out_kind == H3DIT_OUT_QKV) {
+    if (a->head_dim != 64 && a->head_dim != 128) return H3DIT_EINVAL;
+    const int64_t d = (int64_t)a->heads * a->head_dim;
+    if (a->N != 3 * d || d % 128 || !a->cos_t || !a->sin_t || !a->out_q || !a->out_k || !a->out_v) return H3DIT_EINVAL;
+    if (!aligned(a->cos_t, 16) || !aligned(a->sin_t, 16) || !aligned(a->out_q, 16) || !aligned(a->out_k, 16) ||
+        !aligned(a->out_v, 16))
+      return H3DIT_EINVAL;
+  } else if (a->out_kind < 0 || a->out_kind > H3DIT_OUT_QKV || !a->out || !aligned(a->out, 16)) {
+    return H3DIT_EINVAL;
+  }
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_linear(*a, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_rope_split(int64_t n, int32_t heads, int32_t head_dim, const uint16_t *t, const float *cos_t,
+                     const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *vt, void *stream) {
+  if (n < 0 || heads < 1 || (head_dim != 64 && head_dim != 128)) return H3DIT_EINVAL;
+  if (!t || !cos_t || !sin_t || !q || !k || !vt || !aligned(t, 16) || !aligned(q, 16) || !aligned(k, 16))
+    return H3DIT_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_rope_split(n, heads, head_dim, t, cos_t, sin_t, q, k, vt, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_gelu(int64_t count, const uint16_t *u, uint16_t *gl, void *stream) {
+  if (count < 0 || count % 8 || !u || !gl || !aligned(u, 16) || !aligned(gl, 16)) return H3DIT_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_gelu(count, u, gl, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_attention(int32_t heads, int64_t n, int32_t head_dim, const uint16_t *q, const uint16_t *k,
+                    const uint16_t *vt, uint16_t *o, float *row_max, float *row_sum, void *stream) {
+  if (heads < 1 || n < 0 || (head_dim != 64 && head_dim != 128)) return H3DIT_EINVAL;
+  if (!q || !k || !vt || !o || !aligned(q, 16) || !aligned(k, 16) || !aligned(vt, 16) || !aligned(o, 16))
+    return H3DIT_EINVAL;
+  if ((row_max == nullptr) != (row_sum == nullptr)) return H3DIT_EINVAL;
+  const int64_t ldv = (n + 7) / 8 * 8;
+  if ((int64_t)heads * (n + 64) * head_dim * 2 >= ((int64_t)1 << 32) ||
+      (int64_t)heads * head_dim * (ldv + 64) * 2 >= ((int64_t)1 << 32))
+    return H3DIT_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_attention(heads, n, head_dim, q, k, vt, o, row_max, row_sum, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_token_pair(const h3dit_layout *L, int32_t d, const uint16_t *x, uint16_t *r, uint16_t *r_in, void *stream) {
+  if (!L || d < 8 || d % 8 || !x || !r || !aligned(x, 16) || !aligned(r, 16) || (r_in && !aligned(r_in, 16)))
+    return H3DIT_EINVAL;
+  if (L->video_t < 0 || L->video_h < 0 || L->video_w < 0 || L->n_text < 0 || L->n_audio < 0) return H3DIT_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_token_pair(*L, d, x, r, r_in, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_token_restore(const h3dit_layout *L, int32_t d, uint16_t *x, const uint16_t *y, const uint16_t *r_in,
+                        void *stream) {
+  if (!L || d < 8 || d % 8 || !x || !y || !r_in || !aligned(x, 16) || !aligned(y, 16) || !aligned(r_in, 16))
+    return H3DIT_EINVAL;
+  if (L->video_t < 0 || L->video_h < 0 || L->video_w < 0 || L->n_text < 0 || L->n_audio < 0) return H3DIT_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_token_restore(*L, d, x, y, r_in, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+}  // extern "C"

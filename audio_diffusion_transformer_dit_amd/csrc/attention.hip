@@ -1,0 +1,215 @@
+// Full non-causal attention of the H3 DiT block on gfx950 MFMA ([RV] README: the first public
+// release uses full attention over the whole joint token sequence).
+//
+// One workgroup = 4 waves = 128 queries of one head; each wave owns 32 queries and walks all
+// keys in blocks of 64 with an online softmax in the exp2 domain.  Scores are computed
+// transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16 with keys as rows), so each lane holds
+// one query column: the row max and row sum are 16 lane-local values plus one exchange with
+// the other half-wave, and the rescale of the output is a per-lane scalar.  O^T = V^T P^T
+// reuses the score registers as the B operand; the key order inside a 16-key step is the
+// score layout's (4 keys from each 8-key half), and the A operand (V^T, stored [hd][keys])
+// is read in that same order, two 8-byte LDS reads per step.  K and V^T tiles go global ->
+// LDS with buffer_load ... lds, double-buffered, chunk c of row r at slot c ^ (r & 7).
+#include "common.hpp"
+
+namespace h3 {
+
+constexpr int AQ = 128;    // queries per workgroup
+constexpr int AKV = 64;    // keys per block
+constexpr int ATHREADS = 256;
+
+template <int HD>
+struct AttCfg {
+  static constexpr int KROW = HD * 2;          // bytes per K row
+  static constexpr int KBYTES = AKV * KROW;    // K tile
+  static constexpr int VROW = AKV * 2;         // bytes per V^T row (64 keys)
+  static constexpr int VBYTES = HD * VROW;     // V^T tile
+  static constexpr int STAGE = KBYTES + VBYTES;
+};
+
+template <int HD>
+__device__ __forceinline__ void att_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint8_t *st,
+                                         int64_t kbase_row, int64_t vbase_row, int ldv, int kb) {
+  using C = AttCfg<HD>;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // K: rows of HD*2 bytes = HD/8 chunks; one instruction fills 1 KiB = 1024/KROW rows
+  constexpr int KCH = HD / 8;
+  constexpr int KRPI = 1024 / C::KROW;
+  {
+    const int rl = lane / KCH, slot = lane % KCH;
+#pragma unroll
+    for (int i = 0; i < AKV / (KRPI * 4); i++) {
+      const int rb = i * 4 + wid;
+      const int row = rb * KRPI + rl;
+      const int chunk = slot ^ (row & 7);
+      const uint32_t off = (uint32_t)(((kbase_row + (int64_t)kb * AKV + row) * HD + chunk * 8) * 2);
+      buffer_load_lds16(rk, (lds_void *)(st + rb * 1024), off);
+    }
+  }
+  // V^T: HD rows of 128 bytes (8 chunks), 8 rows per instruction
+  {
+    const int rl = lane >> 3, slot = lane & 7;
+#pragma unroll
+    for (int i = 0; i < HD / 32; i++) {
+      const int rb = i * 4 + wid;
+      const int row = rb * 8 + rl;
+      const int chunk = slot ^ (row & 7);
+      const uint32_t off = (uint32_t)((((vbase_row + row) * (int64_t)ldv) + (int64_t)kb * AKV + chunk * 8) * 2);
+      buffer_load_lds16(rv, (lds_void *)(st + C::KBYTES + rb * 1024), off);
+    }
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                           const uint16_t *__restrict__ vt, uint16_t *o, int64_t N,
+                                                           int ldv, int heads, float *row_max, float *row_sum) {
+  using C = AttCfg<HD>;
+  constexpr int KS = HD / 16;   // 16-dim steps of the score product
+  constexpr int DT = HD / 32;   // 32-dim output tiles
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int hsel = lane >> 5, l32 = lane & 31;
+  const int64_t q0 = (int64_t)blockIdx.x * AQ + wid * 32;
+  const int64_t qrow = q0 + l32;
+  const int64_t head_rows = (int64_t)h * N;
+
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k, (uint32_t)((int64_t)heads * N * HD * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt, (uint32_t)((int64_t)heads * HD * ldv * 2));
+
+  const int nkb = (int)((N + AKV - 1) / AKV);
+  att_load<HD>(rk, rv, smem, head_rows, (int64_t)h * HD, ldv, 0);
+
+  // Q fragments (B operand: column = query, 8 dims per lane and step), kept in registers
+  u32x4 qf[KS];
+  {
+    const int64_t qr = qrow < N ? qrow : N - 1;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(q + (head_rows + qr) * HD);
+#pragma unroll
+    for (int s = 0; s < KS; s++) qf[s] = src[2 * s + hsel];
+  }
+  const float c2 = (1.0f / sqrtf((float)HD)) * 1.4426950408889634f;  // score scale in log2 units
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; t++) acc[t] = f32x16{0};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  wait_vmem();
+  __syncthreads();
+
+  for (int kb = 0; kb < nkb; kb++) {
+    uint8_t *cur = smem + (kb & 1) * C::STAGE;
+    if (kb + 1 < nkb) att_load<HD>(rk, rv, smem + ((kb + 1) & 1) * C::STAGE, head_rows, (int64_t)h * HD, ldv, kb + 1);
+    const int valid = (int)min((int64_t)AKV, N - (int64_t)kb * AKV);
+    if (valid < AKV) {
+      // keys past the end: zero their values so that 0-weight * garbage stays 0
+      for (int idx = threadIdx.x; idx < HD * AKV; idx += ATHREADS) {
+        const int row = idx / AKV, key = idx % AKV;
+        if (key >= valid)
+          *reinterpret_cast<uint16_t *>(cur + C::KBYTES + row * C::VROW + (((key >> 3) ^ (row & 7)) << 4) + (key & 7) * 2) = 0;
+      }
+      __syncthreads();
+    }
+    // S^T for 64 keys x 32 queries: two 32-key tiles
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      s[t] = f32x16{0};
+      const int krow = t * 32 + l32;
+#pragma unroll
+      for (int st = 0; st < KS; st++) {
+        const u32x4 kf = *reinterpret_cast<const u32x4 *>(cur + krow * C::KROW + (((2 * st + hsel) ^ (krow & 7)) << 4));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[st]),
+                                                       s[t], 0, 0, 0);
+      }
+    }
+    // online softmax over this block (lane = one query; rows r are keys)
+    float mb = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int key = t * 32 + 8 * (r / 4) + 4 * hsel + (r % 4);
+        const float v = key < valid ? s[t][r] * c2 : -INFINITY;
+        s[t][r] = v;
+        mb = fmaxf(mb, v);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float m_new = fmaxf(m_run, mb);
+    const float corr = exp2f(m_run - m_new);
+    float ls = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float p = exp2f(s[t][r] - m_new);
+        s[t][r] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = l_run * corr + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < DT; t++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[t][r] *= corr;
+    // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int ps = 0; ps < 4; ps++) {
+      const int t = ps >> 1, rb = 8 * (ps & 1);
+      bf16x8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; j++) pf[j] = (__bf16)s[t][rb + j];
+      const int key0 = 16 * ps + 4 * hsel;   // keys key0..key0+3 and key0+8..key0+11
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) {
+        const int row = dt * 32 + l32;
+        const uint8_t *vr = cur + C::KBYTES + row * C::VROW;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(vr + (((key0 >> 3) ^ (row & 7)) << 4) + (key0 & 7) * 2);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(vr + ((((key0 + 8) >> 3) ^ (row & 7)) << 4) + (key0 & 7) * 2);
+        u32x4 vf;
+        vf[0] = lo.x; vf[1] = lo.y; vf[2] = hi.x; vf[3] = hi.y;
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf), pf, acc[dt], 0, 0, 0);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // O[h][q][dim] = O^T / l; lane holds dims dt*32 + 8(r/4) + 4 hsel + r%4 of query qrow
+  if (qrow < N) {
+    const float inv = 1.0f / l_run;
+    uint16_t *dst = o + (head_rows + qrow) * HD;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int dim = dt * 32 + 8 * g + 4 * hsel;
+        uint2 v;
+        v.x = pack_bf2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv);
+        v.y = pack_bf2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+        *reinterpret_cast<uint2 *>(dst + dim) = v;
+      }
+    if (row_max && hsel == 0) {
+      row_max[head_rows + qrow] = m_run * 0.6931471805599453f;
+      row_sum[head_rows + qrow] = l_run;
+    }
+  }
+}
+
+hipError_t launch_attention(int heads, int64_t n, int hd, const uint16_t *q, const uint16_t *k, const uint16_t *vt,
+                            uint16_t *o, float *row_max, float *row_sum, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int ldv = (int)((n + 7) / 8 * 8);
+  dim3 grid((unsigned)((n + AQ - 1) / AQ), (unsigned)heads);
+  if (hd == 128)
+    k_attention<128><<<grid, ATHREADS, 0, st>>>(q, k, vt, o, n, ldv, heads, row_max, row_sum);
+  else
+    k_attention<64><<<grid, ATHREADS, 0, st>>>(q, k, vt, o, n, ldv, heads, row_max, row_sum);
+  return hipGetLastError();
+}
+
+}  // namespace h3

@@ -1,0 +1,113 @@
+// Shared device helpers of the gfx950 H3 DiT kernels: vector types, bf16 conversion,
+// buffer resources for direct-to-LDS loads, wave reductions and the launch table shared by
+// the host orchestration.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "../../include/h3dit.h"
+#include "../../include/h3dit_stages.h"
+
+namespace h3 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// 8 bf16 held in a 16-byte vector
+__device__ __forceinline__ void unpack8(u32x4 v, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ u32x4 pack8(const float *f) {
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; i++) v[i] = pack_bf2(f[2 * i], f[2 * i + 1]);
+  return v;
+}
+
+// raw buffer resource over `bytes` bytes: loads past the end return zeros
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer byte offset `voff` into LDS at lds_base + lane*16
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, lds_void *lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_base, 16, (int)voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))
+__device__ __forceinline__ float gelu_tanh(float u) {
+  float u3 = u * u * u;
+  float z = 0.7978845608f * (u + 0.044715f * u3);
+  return 0.5f * u * (1.0f + tanhf(z));
+}
+
+// int8 code of v with scale s (s > 0): round-half-even(v / s), clamped to +-127
+__device__ __forceinline__ int8_t q8_code(float v, float s) {
+  if (s == 0.0f) return 0;
+  float c = rintf(v / s);
+  c = fminf(fmaxf(c, -127.0f), 127.0f);
+  return (int8_t)(int)c;
+}
+
+}  // namespace h3
+
+// ---------------------------------------------------------------- launchers (internal)
+namespace h3 {
+
+hipError_t launch_rope_tables(const h3dit_layout &L, int hd, int reduced, float *cos_t, float *sin_t,
+                              hipStream_t st);
+hipError_t launch_row(int64_t n, int d, float eps, const uint16_t *x, const uint16_t *gate,
+                      const uint16_t *y, uint16_t *x_out, const uint16_t *shift, const uint16_t *scale,
+                      uint16_t *h, int8_t *q, float *s, hipStream_t st);
+hipError_t launch_quant_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v, int hm_hd,
+                             int8_t *q, float *s, hipStream_t st);
+hipError_t launch_gelu(int64_t count, const uint16_t *u, uint16_t *gl, hipStream_t st);
+hipError_t launch_rope_split(int64_t n, int heads, int hd, const uint16_t *t, const float *cos_t,
+                             const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *vt, hipStream_t st);
+hipError_t launch_token_pair(const h3dit_layout &L, int d, const uint16_t *x, uint16_t *r, uint16_t *r_in,
+                             hipStream_t st);
+hipError_t launch_token_restore(const h3dit_layout &L, int d, uint16_t *x, const uint16_t *y,
+                                const uint16_t *r_in, hipStream_t st);
+hipError_t launch_linear(const h3dit_linear_args &a, hipStream_t st);
+hipError_t launch_attention(int heads, int64_t n, int hd, const uint16_t *q, const uint16_t *k,
+                            const uint16_t *vt, uint16_t *o, float *row_max, float *row_sum, hipStream_t st);
+
+}  // namespace h3

@@ -1,0 +1,294 @@
+"""Benchmark of the MiniMax-H3 DiT hot path on one MI355X.
+
+A step is one denoising evaluation: the whole stack of DiT blocks (AdaLN, QKV with rotary,
+full attention, output projection, gate + AdaLN, FC1 + GELU, FC2, gate) over one batch of
+synthetic tokens.  Default workload: 50 blocks, 4096 tokens (3520 video 5x22x32 + 512 text +
+64 audio), hidden 5120, 40 heads x 128, MLP 20480, bf16, independent seeded weights per block
+resident in HBM.  `value` is the algorithmic TFLOP/s of the timed steps:
+FLOP per block = 2 N (4 d^2 + 2 d f) + 4 N^2 d.
+
+Besides the JSON line's required fields it reports: the same stack on the int8 path; a
+per-kernel breakdown of one block measured with HIP events on the launch stream (the
+dominant kernel gives `roofline`); and the CPU oracle timed on a bounded sample of the same
+workload (`cpu_baseline`).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "int8": 5000.0}     # dense MFMA, TFLOP/s or TOP/s
+HBM_PEAK = 8000.0                           # GB/s
+
+
+def block_flops(N, d, f):
+    return 2.0 * N * (4 * d * d + 2 * d * f) + 4.0 * N * N * d
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3, help="workload index in synth.WORKLOADS (3 or 4)")
+    ap.add_argument("--blocks", type=int, default=None, help="override the block count")
+    ap.add_argument("--no-int8", action="store_true", help="skip the int8 leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--only-kernels", action="store_true", help="per-kernel timing only (profiling runs)")
+    return ap.parse_args()
+
+
+def make_blocks(w, n_blocks, seed, device, int8):
+    import synth
+    import audio_diffusion_transformer_dit_amd as h3
+    blocks = []
+    for b in range(n_blocks):
+        p = synth.make_block(w, seed, b, device)
+        if int8:
+            q = h3.quantize_block(p)
+            del p
+            p = q
+        blocks.append(p)
+        print(f"[bench] block {b + 1}/{n_blocks} generated", file=sys.stderr, flush=True) if (b + 1) % 10 == 0 else None
+    return blocks
+
+
+def time_stack(w, blocks, x, steps, warmup, reduction=None):
+    import torch
+    import audio_diffusion_transformer_dit_amd as h3
+    stack = h3.Stack(w, blocks, 0, reduction)
+    ws = h3.alloc_workspace(stack.workspace_bytes, x.device)
+    for _ in range(warmup):
+        stack(x, ws)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(steps):
+        stack(x, ws)
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall, stack.workspace_bytes
+
+
+def kernel_breakdown(w, p, x, iters, int8):
+    """Times each kernel of one block on its own (HIP events on the current stream)."""
+    import torch
+    import audio_diffusion_transformer_dit_amd as h3
+    dev = x.device
+    N, d, f, H, hd = w.n_tokens, w.hidden, w.mlp, w.heads, w.head_dim
+    mod = p["mod"]
+    cos, sin = h3.rope_tables(w, device=dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    h1 = torch.empty((N, d), **bf)
+    q = torch.empty((H, N, hd), **bf)
+    k = torch.empty_like(q)
+    vt = torch.empty((H, hd, h3.ldv(N)), **bf)
+    o = torch.empty_like(q)
+    y1 = torch.empty((N, d), **bf)
+    x1 = torch.empty((N, d), **bf)
+    h2 = torch.empty((N, d), **bf)
+    gl = torch.empty((N, f), **bf)
+    y2 = torch.empty((N, d), **bf)
+    x2 = torch.empty((N, d), **bf)
+    i8 = dict(dtype=torch.int8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    q1, s1 = torch.empty((N, d), **i8), torch.empty(N, **f32)
+    qo, so = torch.empty((N, d), **i8), torch.empty(N, **f32)
+    q2, s2 = torch.empty((N, d), **i8), torch.empty(N, **f32)
+    qg, sg = torch.empty((N, f), **i8), torch.empty((N, f // w.fc2_group), **f32)
+
+    if not int8:
+        ops = {
+            "adaln": (lambda: h3.row_gate_adaln(x, shift=mod[0], scale=mod[1], h=h1), 0, 4.0 * N * d),
+            "qkv_rope_gemm": (lambda: h3.linear(N, 3 * d, d, h1, p["wqkv"], h3.OUT_QKV, None, cos=cos, sin=sin,
+                                                heads=H, head_dim=hd, out_q=q, out_k=k, out_v=vt),
+                              2.0 * N * d * 3 * d, 0),
+            "attention": (lambda: h3.attention(H, N, hd, q, k, vt, o), 4.0 * N * N * d, 0),
+            "out_proj_gemm": (lambda: h3.linear(N, d, d, o, p["wo"], h3.OUT_BF16, y1, a_headmajor_hd=hd),
+                              2.0 * N * d * d, 0),
+            "gate_adaln": (lambda: h3.row_gate_adaln(x, gate=mod[2], y=y1, x_out=x1, shift=mod[3], scale=mod[4], h=h2),
+                           0, 8.0 * N * d),
+            "fc1_gelu_gemm": (lambda: h3.linear(N, f, d, h2, p["w1"], h3.OUT_GELU, gl), 2.0 * N * d * f, 0),
+            "fc2_gemm": (lambda: h3.linear(N, d, f, gl, p["w2"], h3.OUT_BF16, y2), 2.0 * N * f * d, 0),
+            "gate": (lambda: h3.row_gate_adaln(x1, gate=mod[5], y=y2, x_out=x2), 0, 6.0 * N * d),
+        }
+    else:
+        ops = {
+            "adaln_q8": (lambda: h3.row_gate_adaln(x, shift=mod[0], scale=mod[1], q=q1, s=s1), 0, 3.0 * N * d + 4 * N),
+            "qkv_rope_gemm_i8": (lambda: h3.linear(N, 3 * d, d, q1, p["qqkv"], h3.OUT_QKV, None, precision=h3.INT8,
+                                                   a_scale=s1, w_scale=p["sqkv"], cos=cos, sin=sin, heads=H,
+                                                   head_dim=hd, out_q=q, out_k=k, out_v=vt),
+                                 2.0 * N * d * 3 * d, 0),
+            "attention": (lambda: h3.attention(H, N, hd, q, k, vt, o), 4.0 * N * N * d, 0),
+            "quant_o": (lambda: h3.lib().h3dit_quantize_rows(N, d, d, o.data_ptr(), hd, qo.data_ptr(), so.data_ptr(),
+                                                             torch.cuda.current_stream().cuda_stream),
+                        0, 3.0 * N * d + 4 * N),
+            "out_proj_gemm_i8": (lambda: h3.linear(N, d, d, qo, p["qo"], h3.OUT_BF16, y1, precision=h3.INT8,
+                                                   a_scale=so, w_scale=p["so"]), 2.0 * N * d * d, 0),
+            "gate_adaln_q8": (lambda: h3.row_gate_adaln(x, gate=mod[2], y=y1, x_out=x1, shift=mod[3], scale=mod[4],
+                                                        q=q2, s=s2), 0, 7.0 * N * d + 4 * N),
+            "fc1_gelu_gemm_i8": (lambda: h3.linear(N, f, d, q2, p["q1"], h3.OUT_GELU, gl, precision=h3.INT8,
+                                                   a_scale=s2, w_scale=p["s1"]), 2.0 * N * d * f, 0),
+            "quant_fc2_in": (lambda: h3.lib().h3dit_quantize_rows(N, f, w.fc2_group, gl.data_ptr(), 0, qg.data_ptr(),
+                                                                  sg.data_ptr(),
+                                                                  torch.cuda.current_stream().cuda_stream),
+                             0, 3.0 * N * f + 4.0 * N * f / w.fc2_group),
+            "fc2_gemm_i8": (lambda: h3.linear(N, d, f, qg, p["q2"], h3.OUT_BF16, y2, precision=h3.INT8, a_scale=sg,
+                                              a_group=w.fc2_group, w_scale=p["s2"]), 2.0 * N * f * d, 0),
+            "gate": (lambda: h3.row_gate_adaln(x1, gate=mod[5], y=y2, x_out=x2), 0, 6.0 * N * d),
+        }
+    # one pass in order so that every kernel reads realistic data
+    for fn, _, _ in ops.values():
+        fn()
+    torch.cuda.synchronize()
+    res = {}
+    for name, (fn, flop, nbytes) in ops.items():
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / iters
+        r = {"ms": round(ms, 4)}
+        if flop:
+            r["tflops"] = round(flop / ms / 1e9, 1)
+            r["flop"] = flop
+        if nbytes:
+            r["gbps"] = round(nbytes / ms / 1e6, 1)
+            r["bytes"] = nbytes
+        res[name] = r
+    return res
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    ent = t.get(kernel)
+    if not ent:
+        return None
+    h = hashlib.sha256()
+    for src in sorted(ent.get("sources", [])):
+        with open(os.path.join(ROOT, src), "rb") as fh:
+            h.update(fh.read())
+    return ent["bytes_per_launch"] if h.hexdigest() == ent.get("sha256") else None
+
+
+def cpu_baseline(w):
+    """The oracle on a bounded sample: one block at full width over 512 tokens."""
+    import oracle
+    import synth
+    sample = w.replace(video_t=2, video_h=8, video_w=28, n_text=48, n_audio=16, blocks=1)
+    assert sample.n_tokens == 512
+    seed = synth.seed_for(3)
+    x = synth.make_x(sample, seed)
+    p = synth.make_block(sample, seed, 0)
+    cos, sin = oracle.rope_tables(sample)
+    t0 = time.perf_counter()
+    oracle.block_fwd(sample, p, x, cos, sin)
+    dt = time.perf_counter() - t0
+    fl = block_flops(sample.n_tokens, sample.hidden, sample.mlp)
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one bf16 block at full width (d={sample.hidden}, H={sample.heads}x{sample.head_dim}, "
+                      f"f={sample.mlp}) over {sample.n_tokens} tokens (2x8x28 video + 48 text + 16 audio): "
+                      f"{fl / 1e9:.1f} GFLOP in {dt:.2f} s; extrapolated 50-block step at 4096 tokens "
+                      f"{50 * block_flops(4096, 5120, 20480) / (fl / dt) :.0f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single "
+              "MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import audio_diffusion_transformer_dit_amd as h3
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    if args.blocks:
+        w = w.replace(blocks=args.blocks)
+    seed = synth.seed_for(args.workload)
+    int8_main = w.precision == "int8"
+    red = (w.reduce_after, w.restore_before) if w.reduce_after >= 0 else None
+    N, d, f = w.n_tokens, w.hidden, w.mlp
+    print(f"[bench] workload {w.name}: {w.blocks} blocks, N={N}, d={d}, f={f}, {w.precision}", file=sys.stderr,
+          flush=True)
+
+    x = synth.make_x(w, seed, dev)
+    out = {}
+    if args.only_kernels:
+        p = make_blocks(w, 1, seed, dev, int8_main)[0]
+        out["kernels"] = kernel_breakdown(w, p, x, args.kernel_iters, int8_main)
+        print(json.dumps(out))
+        return
+
+    blocks = make_blocks(w, w.blocks, seed, dev, int8_main)
+    torch.cuda.synchronize()
+    print("[bench] weights resident; timing the stack", file=sys.stderr, flush=True)
+    ms, wall, ws_bytes = time_stack(w, blocks, x, args.steps, args.warmup, red)
+    if red:
+        nr = w.video_t * w.video_h * (w.video_w // 2 + w.video_w % 2) + w.n_text + w.n_audio
+        full = red[0] + 1 + max(0, w.blocks - red[1])
+        step_flop = full * block_flops(N, d, f) + (w.blocks - full) * block_flops(nr, d, f)
+    else:
+        step_flop = w.blocks * block_flops(N, d, f)
+    value = step_flop / (ms / 1e3) / 1e12
+    print(f"[bench] {ms:.2f} ms/step, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    kern = kernel_breakdown(w, blocks[0], x, args.kernel_iters, int8_main)
+    mm = {k: v for k, v in kern.items() if "flop" in v}
+    dom = max(mm, key=lambda k: mm[k]["ms"])
+    prec = "int8" if int8_main else "bf16"
+    roof = {"bound": "mfma", "kernel": dom, "achieved": mm[dom]["tflops"], "peak": PEAK[prec],
+            "unit": "TFLOP/s" if prec == "bf16" else "TOP/s", "frac": round(mm[dom]["tflops"] / PEAK[prec], 4),
+            "traffic": traffic_for(dom)}
+    extra = {"ms_per_block": round(ms / w.blocks, 3), "tflop_per_step": round(step_flop / 1e12, 2),
+             "workspace_bytes": ws_bytes, "kernels": kern, "wall_s_timed": round(wall, 3)}
+
+    if not args.no_int8 and not int8_main:
+        del blocks
+        torch.cuda.empty_cache()
+        blocks8 = make_blocks(w, w.blocks, seed, dev, True)
+        ms8, _, _ = time_stack(w, blocks8, x, args.steps, args.warmup, red)
+        extra["int8"] = {"ms_per_step": round(ms8, 3), "ms_per_block": round(ms8 / w.blocks, 3),
+                         "tops": round(step_flop / (ms8 / 1e3) / 1e12, 1),
+                         "kernels": kernel_breakdown(w, blocks8[0], x, args.kernel_iters, True)}
+        del blocks8
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": "DiT block TFLOP/s (bf16, int8) + ms per 50-block step, 4096 tokens",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": prec, "data": "synthetic (seeded Philox-4x32-10 normals; random-init weights per block)",
+        "config": {"workload": w.name, "n_tokens": N, "video": [w.video_t, w.video_h, w.video_w],
+                   "text": w.n_text, "audio": w.n_audio, "hidden": d, "heads": w.heads, "head_dim": w.head_dim,
+                   "mlp": f, "blocks": w.blocks, "token_reduction": list(red) if red else None,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w)
+    line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

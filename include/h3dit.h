@@ -1,0 +1,140 @@
+/*
+ * h3dit.h — C ABI of the MI355X (gfx950) library for the MiniMax-H3 single-stream Omni DiT
+ * block: the forward pass of one block, and of a stack of blocks for one denoising
+ * evaluation, over a joint video + text + audio token sequence, in a bf16 path and an int8
+ * path.  Every step runs in hand-written HIP kernels; the library never allocates.
+ *
+ * Sources (web pages about antirez's h3.c / h3-metal engine for MiniMax-H3):
+ *   [RV] alphalab.site, "h3-metal 把 MiniMax-H3 搬上 Apple Silicon：突破與代價（2026）",
+ *        section "h3.c README" (components: 50-layer single-stream Omni Transformer, full
+ *        attention in the first public release).
+ *   [DD] linlog.top article 1265 (h3.c deep dive), sections "MiniMax H3：原生音频视频一体化
+ *        生成" (dense Omni Transformer, precomputable AdaLN branches), "h3.c 的核心设计"
+ *        (QKV and attention-output projections, Q/K/V routed head-major), "int8 量化：从 36
+ *        秒到 19 秒" (int8 scheme and its table), "DiT 融合内核：减少全局内存往返" (gate +
+ *        AdaLN fusion, cross-block AdaLN, activation aliasing, byte-identical fallbacks),
+ *        "Token 缩减：28% 的去噪时间消减" (horizontal pairing after block 3, bypass,
+ *        restore before block 40).
+ * The pages give the block in prose only; widths, activation, eps and rotary layout are
+ * parameters here, and each reading of an unstated detail is named where it applies.
+ *
+ * Common rules for every entry point:
+ *  - Pointers marked "device" must be device memory of the current HIP device; "host"
+ *    pointers (the argument structs, the block array) are read during the call only.
+ *  - The caller owns every buffer.  Calls are asynchronous on `stream` (a hipStream_t;
+ *    NULL means the default stream); nothing is allocated and the host never waits.
+ *  - bf16 is passed as uint16_t bit patterns.  Matrices are row-major; weights are
+ *    [out][in].  Device pointers must be 16-byte aligned.
+ *  - Return: H3DIT_OK, or a negative status.  Arguments are validated before any launch;
+ *    on a validation error nothing is launched and no buffer is touched.
+ *  - NaN/Inf in the inputs are not checked; they propagate.
+ */
+#ifndef H3DIT_H
+#define H3DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3DIT_OK 0
+#define H3DIT_EINVAL (-1)       /* bad sizes, NULL or misaligned pointer, bad schedule */
+#define H3DIT_EWORKSPACE (-2)   /* workspace too small; required size written back */
+#define H3DIT_EUNSUPPORTED (-3) /* head_dim not 64/128, or device is not gfx950 */
+#define H3DIT_EHIP (-4)         /* a HIP launch failed */
+
+#define H3DIT_BF16 0
+#define H3DIT_INT8 1
+
+/* Fusion switches ([DD] "DiT 融合内核": every fusion can be turned back into its step-wise
+ * form for a byte-identical A/B).  Each flag selects the unfused sequence; the results are
+ * byte-identical to the fused default. */
+#define H3DIT_NOFUSE_GATE_ADALN 1u  /* gated residual and the following AdaLN as two kernels */
+#define H3DIT_NOFUSE_ROPE 2u        /* QKV projection written token-major, then rotary + head split */
+#define H3DIT_NOFUSE_GELU 4u        /* FC1 output written, then GELU as its own kernel */
+#define H3DIT_NOFUSE_QUANT 8u       /* int8 path: AdaLN written in bf16, then quantised */
+#define H3DIT_NOFUSE_CROSS_BLOCK 16u /* final gate does not produce the next block's AdaLN1 */
+#define H3DIT_NO_ALIAS 32u          /* every activation in its own workspace region */
+
+/* Widths.  hidden = heads * head_dim; head_dim 64 or 128; hidden % 256 == 0;
+ * mlp % 256 == 0, and on the int8 path mlp % fc2_group == 0 with fc2_group % 128 == 0
+ * (1024 is the pages' group).  ln_eps: LayerNorm epsilon (1e-6). */
+typedef struct {
+  int32_t n_tokens, hidden, heads, head_dim, mlp, fc2_group;
+  float ln_eps;
+} h3dit_dims;
+
+/* Token layout: video tokens (t, h, w) row-major, then n_text text tokens, then n_audio
+ * audio tokens; n_tokens must equal video_t*video_h*video_w + n_text + n_audio.
+ * Rotary embedding (the pages only say spatial rotary positions exist, [DD] "h3.c 的核心
+ * 设计" and the preview-mode note of the daily.steinslab.io article): video tokens rotate
+ * head-dim pairs (2j, 2j+1) by their t, h and w position in three consecutive sections of
+ * rope_t, rope_h, rope_w dims (even, summing to head_dim) with frequencies
+ * theta^(-2j/section); text and audio use 1-D rotary over the whole head dim at their
+ * index within their own segment.  Tables are built on the device in double precision. */
+typedef struct {
+  int32_t video_t, video_h, video_w, n_text, n_audio;
+  int32_t rope_t, rope_h, rope_w;
+  float rope_theta;
+} h3dit_layout;
+
+/* One block's parameters (device pointers).
+ * precision H3DIT_BF16: w_* are bf16 [3d][d] (rows q | k | v, head h = rows h*hd..),
+ *   [d][d], [mlp][d], [d][mlp]; s_* unused.
+ * precision H3DIT_INT8: w_* are int8 codes of the same shapes and s_* fp32 per-output-row
+ *   scales, as written by h3dit_quantize_weights.
+ * mod: bf16 [6][d] modulation rows shift1, scale1, gate1, shift2, scale2, gate2, broadcast
+ *   over tokens ([DD] AdaLN branches are precomputable per block). */
+typedef struct {
+  int32_t precision;
+  const void *w_qkv, *w_o, *w_fc1, *w_fc2;
+  const float *s_qkv, *s_o, *s_fc1, *s_fc2;
+  const uint16_t *mod;
+} h3dit_block_w;
+
+/* Token reduction ([DD] "Token 缩减"): after block index reduce_after (0-based) adjacent
+ * horizontal video tokens (t,h,2k),(t,h,2k+1) are averaged into one token (the odd last
+ * column, text and audio pass through); the full-resolution residual stays in x as the
+ * bypass.  Before block index restore_before (or after the last block, whichever comes
+ * first) each paired token becomes bypass + (reduced output - reduced input) and every
+ * other token takes its reduced output.  Requires 0 <= reduce_after < restore_before and
+ * reduce_after < n_blocks. */
+typedef struct {
+  int32_t reduce_after, restore_before;
+} h3dit_token_reduction;
+
+/* Per-output-channel int8 weight codes ([DD] "int8 量化"): for each row r of w (bf16
+ * [rows][cols], device), s[r] = max|w[r][:]| / 127 (IEEE division) and
+ * q[r][c] = round-half-even(w[r][c] / s[r]) clamped to +-127 (0 when s[r] == 0).
+ * q: int8 [rows][cols] device; s: fp32 [rows] device.  cols % 8 == 0, rows < 2^31. */
+int h3dit_quantize_weights(const uint16_t *w, int64_t rows, int64_t cols, int8_t *q, float *s,
+                           void *stream);
+
+/* One block, x <- block(x), with no cross-block fusion ([DD] "DiT 融合内核" for the order):
+ *   h1 = AdaLN(x; shift1, scale1); [q|k|v] = h1 Wqkv^T; rotary on q, k; O = softmax(q k^T /
+ *   sqrt(hd)) v per head (non-causal); y1 = O Wo^T; x1 = x + gate1*y1; h2 = AdaLN(x1; shift2,
+ *   scale2); y2 = GELU_tanh(h2 W1^T) W2^T; x = x1 + gate2*y2,
+ * with AdaLN(v; s, c) = LN(v)(1 + c) + s (no learned affine) and every intermediate rounded
+ * to bf16.  int8 path: each projection input is quantised per token (FC2 input per
+ * fc2_group channels), accumulated in int32 and dequantised as (acc * s_act) * s_w.
+ * x: bf16 [n_tokens][hidden] device, in/out.  layout: token layout and rotary (host).
+ * workspace: device scratch of *workspace_bytes bytes; with workspace == NULL the required
+ * size is written to *workspace_bytes and H3DIT_OK returned without launching. */
+int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_block_w *blk,
+                    uint16_t *x, uint32_t flags, void *workspace, size_t *workspace_bytes,
+                    void *stream);
+
+/* A stack of n_blocks blocks for one denoising evaluation ([RV] README: 50-layer DiT;
+ * [DD] fusion of each block's final gate with the next block's AdaLN1, and activation
+ * arenas reused across lifetimes).  blocks: host array of n_blocks entries (device
+ * pointers inside).  tr: NULL for no token reduction.  Other arguments as h3dit_block_fwd. */
+int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
+                    const h3dit_block_w *blocks, const h3dit_token_reduction *tr, uint16_t *x,
+                    uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -48,6 +48,7 @@ def lib():
         _lib = C.CDLL(_LIB_PATH)
         _lib.orc_gelu_tanh_f32.restype = C.c_float
         _lib.orc_gelu_tanh_f32.argtypes = [C.c_float]
+        _lib.orc_num_threads.restype = C.c_int32
         for name in ("orc_layout_tokens", "orc_rope_tables", "orc_token_pair", "orc_token_restore",
                      "orc_block_fwd", "orc_stack_fwd"):
             getattr(_lib, name).restype = C.c_int32
@@ -86,6 +87,10 @@ def f32_to_bf16(x: torch.Tensor) -> torch.Tensor:
     out = bf16(x.shape)
     lib().orc_f32_to_bf16(_p(x), _p(out), _i64(x.numel()))
     return out
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
 
 
 def gelu_tanh(u: float) -> float:
@@ -178,11 +183,13 @@ def rope_split(t, cos, sin, heads, head_dim):
 
 
 def attention(q, k, v, stats=False):
-    H, N, hd = q.shape
-    o = bf16((H, N, hd))
-    mx = torch.empty((H, N), dtype=torch.float32)
-    sm = torch.empty((H, N), dtype=torch.float32)
-    lib().orc_attention(C.c_int32(H), _i64(N), C.c_int32(hd), _p(q.contiguous()), _p(k.contiguous()),
+    """q: [H][Nq][hd] query rows (all tokens or a subset), k, v: [H][N][hd]."""
+    H, Nq, hd = q.shape
+    N = k.shape[1]
+    o = bf16((H, Nq, hd))
+    mx = torch.empty((H, Nq), dtype=torch.float32)
+    sm = torch.empty((H, Nq), dtype=torch.float32)
+    lib().orc_attention(C.c_int32(H), _i64(Nq), _i64(N), C.c_int32(hd), _p(q.contiguous()), _p(k.contiguous()),
                         _p(v.contiguous()), _p(o), _p(mx), _p(sm))
     return (o, mx, sm) if stats else o
 

@@ -33,6 +33,7 @@
 #include "h3dit_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -51,6 +52,17 @@ static uint16_t f2bf(float f) {
   memcpy(&u, &f, 4);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+/* OpenMP threads the oracle's parallel loops use (the host cores it runs on). */
+int32_t orc_num_threads(void) {
+  int32_t n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = (int32_t)omp_get_num_threads();
+  }
+  return n;
 }
 
 void orc_f32_to_bf16(const float *in, uint16_t *out, int64_t n) {
@@ -304,8 +316,9 @@ void orc_rope_split(int64_t N, int32_t d, int32_t H, int32_t hd, const uint16_t 
 
 /* Full non-causal attention per head ([RV] README: the public release uses full attention):
  * s_m = (1/sqrt(hd)) * <q_n, k_m>, M = max s, e_m = exp(s_m - M), L = sum e,
- * o_n = bf16( (sum_m e_m v_m) / L ).  Sums ascend in m and i. */
-void orc_attention(int32_t H, int64_t N, int32_t hd, const uint16_t *q, const uint16_t *k,
+ * o_n = bf16( (sum_m e_m v_m) / L ).  Sums ascend in m and i.  q / o hold Nq query rows
+ * per head (all N tokens, or any subset of them), k / v hold all N key rows. */
+void orc_attention(int32_t H, int64_t Nq, int64_t N, int32_t hd, const uint16_t *q, const uint16_t *k,
                    const uint16_t *v, uint16_t *o, float *row_max, float *row_sum) {
   float alpha = 1.0f / sqrtf((float)hd);
   float *kf = xmalloc(sizeof(float) * (size_t)(H * N * hd));
@@ -320,8 +333,8 @@ void orc_attention(int32_t H, int64_t N, int32_t hd, const uint16_t *q, const ui
     float *acc = xmalloc(sizeof(float) * (size_t)hd);
     float *qf = xmalloc(sizeof(float) * (size_t)hd);
 #pragma omp for schedule(static)
-    for (int64_t hn = 0; hn < (int64_t)H * N; hn++) {
-      int64_t h = hn / N;
+    for (int64_t hn = 0; hn < (int64_t)H * Nq; hn++) {
+      int64_t h = hn / Nq;
       for (int32_t i = 0; i < hd; i++) qf[i] = bf2f(q[hn * hd + i]);
       float mx = -INFINITY;
       for (int64_t m = 0; m < N; m++) {
@@ -499,7 +512,7 @@ static int32_t block_body(const orc_dims *D, const orc_block *B, const float *co
   project(N, 3 * d, d, h1, B->int8, B->wqkv, B->qqkv, B->sqkv, t);
   orc_rope_split(N, d, H, hd, t, cosv, sinv, q, k, v);
   /* attention, then the head-major output read as [N][d] (column h*hd + i) */
-  orc_attention(H, N, hd, q, k, v, o, T ? T->att_max : NULL, T ? T->att_sum : NULL);
+  orc_attention(H, N, N, hd, q, k, v, o, T ? T->att_max : NULL, T ? T->att_sum : NULL);
   for (int64_t n = 0; n < N; n++)
     for (int32_t h = 0; h < H; h++)
       memcpy(ot + n * d + h * hd, o + ((int64_t)h * N + n) * hd, 2 * (size_t)hd);

@@ -51,6 +51,7 @@ typedef struct {                        /* optional stage outputs; any pointer m
 } orc_taps;
 
 /* scalar helpers exposed for the pins */
+int32_t orc_num_threads(void);
 void orc_f32_to_bf16(const float *in, uint16_t *out, int64_t n);
 float orc_gelu_tanh_f32(float u);
 int32_t orc_layout_tokens(const orc_layout *L, int32_t reduced);
@@ -65,7 +66,7 @@ void orc_gemm_f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint
 void orc_gemm_i32(int64_t M, int64_t N, int64_t K, const int8_t *A, const int8_t *W, int32_t *acc);
 void orc_rope_split(int64_t N, int32_t d, int32_t H, int32_t hd, const uint16_t *t,
                     const float *cosv, const float *sinv, uint16_t *q, uint16_t *k, uint16_t *v);
-void orc_attention(int32_t H, int64_t N, int32_t hd, const uint16_t *q, const uint16_t *k,
+void orc_attention(int32_t H, int64_t Nq, int64_t N, int32_t hd, const uint16_t *q, const uint16_t *k,
                    const uint16_t *v, uint16_t *o, float *row_max, float *row_sum);
 void orc_gelu_rows(int64_t n, const uint16_t *u, uint16_t *gl);
 void orc_gate(int64_t n, int32_t d, const uint16_t *x, const uint16_t *gate, const uint16_t *y,

@@ -1,0 +1,160 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every function
+include/*.h declares, answers workspace-size queries, and rejects bad arguments before any
+launch (a call that reached the device here would fail with EHIP, not the code asserted)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import synth
+from synth import WORKLOADS
+
+h3 = pytest.importorskip("audio_diffusion_transformer_dit_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for hdr in ("h3dit.h", "h3dit_stages.h"):
+        with open(os.path.join(ROOT, "include", hdr)) as fh:
+            names.update(re.findall(r"^int\s+(h3dit_\w+)\s*\(", fh.read(), flags=re.M))
+    return sorted(names)
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    assert set(names) == set(h3.EXPORTS)
+    for n in names:
+        assert getattr(h3.lib(), n) is not None
+
+
+def test_struct_sizes_match_header_layout():
+    assert C.sizeof(h3.Dims) == 28
+    assert C.sizeof(h3.Layout) == 36
+    assert C.sizeof(h3.BlockW) == 8 + 9 * 8
+    assert C.sizeof(h3.TokenReduction) == 8
+
+
+def fake_block(precision=h3.BF16):
+    # 16-byte aligned fake addresses: never dereferenced by a size query or a rejected call
+    a = 1 << 20
+    return h3.BlockW(precision, a, a, a, a, a if precision else None, a if precision else None,
+                     a if precision else None, a if precision else None, a)
+
+
+def query(w, blk, flags=0):
+    size = C.c_size_t(0)
+    rc = h3.lib().h3dit_block_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), C.byref(blk), None, flags,
+                                  None, C.byref(size), None)
+    return rc, size.value
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_workspace_query_bf16(cfg):
+    w = WORKLOADS[cfg]
+    rc, size = query(w, fake_block())
+    assert rc == 0
+    N, d, f = w.n_tokens, w.hidden, w.mlp
+    # arenas: A = q|k|V^T, B = [N][d], C = [N][f]; plus rotary tables and per-token scales
+    arenas = (2 * N * d * 2 + d * h3.ldv(N) * 2) + N * d * 2 + N * f * 2
+    assert arenas <= size <= arenas + N * w.head_dim * 4 + N * 4 + 16 * 256
+    rc2, size2 = query(w, fake_block(), h3.NO_ALIAS)
+    assert rc2 == 0 and size2 > size
+
+
+def test_workspace_query_int8_and_unfused():
+    w = WORKLOADS[2]
+    rc, base = query(w, fake_block(h3.INT8))
+    assert rc == 0
+    for flag in (h3.NOFUSE_ROPE, h3.NOFUSE_QUANT):
+        rc, s = query(w, fake_block(h3.INT8), flag)
+        assert rc == 0 and s > base
+
+
+def test_stack_workspace_with_reduction_is_larger():
+    w = WORKLOADS[4]
+    blocks = [fake_block(h3.INT8)] * 50
+    arr = (h3.BlockW * 50)(*blocks)
+    s0, s1 = C.c_size_t(0), C.c_size_t(0)
+    tr = h3.TokenReduction(3, 40)
+    lib = h3.lib()
+    assert lib.h3dit_stack_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), 50, arr, None, None, 0, None,
+                               C.byref(s0), None) == 0
+    assert lib.h3dit_stack_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), 50, arr, C.byref(tr), None, 0, None,
+                               C.byref(s1), None) == 0
+    nr = w.video_t * w.video_h * (w.video_w // 2 + 1) + w.n_text + w.n_audio
+    assert s1.value - s0.value >= 2 * nr * w.hidden * 2
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(hidden=5000), h3.EINVAL),                 # hidden != heads * head_dim
+    (dict(head_dim=96, hidden=40 * 96), h3.EUNSUPPORTED),
+    (dict(mlp=20000), h3.EINVAL),                   # mlp % 256
+    (dict(n_text=255), h3.EINVAL),                  # n_tokens disagrees with the layout
+    (dict(rope_split=(32, 48, 46)), h3.EINVAL),     # rotary sections do not cover head_dim
+    (dict(rope_split=(31, 49, 48)), h3.EINVAL),     # odd section
+])
+def test_bad_dims_rejected(change, code):
+    base = WORKLOADS[1]
+    dims = h3.dims_of(base)
+    w = base.replace(**{k: v for k, v in change.items() if k in ("rope_split",)})
+    layout = h3.layout_of(w)
+    if "hidden" in change:
+        dims.hidden = change["hidden"]
+    if "head_dim" in change:
+        dims.head_dim = change["head_dim"]
+    if "mlp" in change:
+        dims.mlp = change["mlp"]
+    if "n_text" in change:
+        layout.n_text = change["n_text"]
+    size = C.c_size_t(0)
+    blk = fake_block()
+    rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(layout), C.byref(blk), None, 0, None, C.byref(size), None)
+    assert rc == code
+
+
+def test_int8_group_rules():
+    w = WORKLOADS[2]
+    dims = h3.dims_of(w)
+    size = C.c_size_t(0)
+    blk = fake_block(h3.INT8)
+    for g in (1000, 64, 3 * 1024):  # not a multiple of 128 / too small / does not divide mlp
+        dims.fc2_group = g
+        rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(h3.layout_of(w)), C.byref(blk), None, 0, None,
+                                      C.byref(size), None)
+        assert rc == h3.EINVAL, g
+
+
+def test_call_argument_errors_before_launch():
+    w = WORKLOADS[0]
+    lib = h3.lib()
+    blk = fake_block()
+    size = C.c_size_t(1 << 30)
+    ws = 1 << 24
+    x = 1 << 22
+    d, l = C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w))
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), None, 0, ws, C.byref(size), None) == h3.EINVAL     # x NULL
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), x + 2, 0, ws, C.byref(size), None) == h3.EINVAL   # misaligned x
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), x, 0, ws + 16, C.byref(size), None) == h3.EINVAL  # workspace align
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), x, 1 << 9, ws, C.byref(size), None) == h3.EINVAL  # unknown flag
+    small = C.c_size_t(1024)
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), x, 0, ws, C.byref(small), None) == h3.EWORKSPACE
+    assert small.value > 1024                                                                          # size written back
+    bad = fake_block()
+    bad.w_fc1 = None
+    assert lib.h3dit_block_fwd(d, l, C.byref(bad), x, 0, ws, C.byref(size), None) == h3.EINVAL
+    mixed = fake_block(h3.INT8)
+    mixed.s_o = None
+    assert lib.h3dit_block_fwd(d, l, C.byref(mixed), x, 0, ws, C.byref(size), None) == h3.EINVAL
+    arr = (h3.BlockW * 2)(fake_block(), fake_block())
+    for tr in (h3.TokenReduction(3, 3), h3.TokenReduction(-1, 4), h3.TokenReduction(2, 5)):
+        assert lib.h3dit_stack_fwd(d, l, 2, arr, C.byref(tr), x, 0, ws, C.byref(size), None) == h3.EINVAL
+    assert lib.h3dit_quantize_weights(x, 4, 12, x, x, None) == h3.EINVAL      # cols % 8
+    assert lib.h3dit_attention(4, 100, 96, x, x, x, x, None, None, None) == h3.EINVAL
+    args = h3.LinearArgs(M=10, N=100, K=128, precision=h3.BF16, a=x, w=x, out=x, out_kind=h3.OUT_BF16)
+    assert lib.h3dit_linear(C.byref(args), None) == h3.EINVAL                 # N % 128
+    args = h3.LinearArgs(M=10, N=128, K=128, precision=h3.BF16, a=x, w=x, out=x, out_kind=h3.OUT_I32)
+    assert lib.h3dit_linear(C.byref(args), None) == h3.EINVAL                 # int32 output on the bf16 path

@@ -1,0 +1,192 @@
+"""Block and stack parity of the HIP path (h3dit_block_fwd / h3dit_stack_fwd through the C ABI)
+against the CPU oracle on the tiny workload and on ragged and token-reduction layouts; every
+fusion switch and the unaliased workspace byte-identical to the default; gates of zero an
+exact identity; run-to-run determinism."""
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import WORKLOADS
+from parity import BF16_TOL, assert_bitexact, relerr
+
+pytestmark = pytest.mark.gpu
+
+h3 = pytest.importorskip("audio_diffusion_transformer_dit_amd")
+DEV = "cuda"
+W0 = WORKLOADS[0]
+
+
+def cpu(t):
+    torch.cuda.synchronize()
+    return t.to("cpu")
+
+
+def dev_block(p):
+    return {k: v.to(DEV).contiguous() for k, v in p.items()}
+
+
+def zero_gates(p):
+    p = dict(p)
+    mod = p["mod"].clone()
+    mod[2] = 0
+    mod[5] = 0
+    p["mod"] = mod
+    return p
+
+
+def inputs(w, seed=1000, blocks=1):
+    x = synth.make_x(w, seed)
+    ps = [synth.make_block(w, seed, b) for b in range(blocks)]
+    return x, ps
+
+
+def gpu_params(ps, int8):
+    out = []
+    for p in ps:
+        g = dev_block(p)
+        out.append(h3.quantize_block(g) if int8 else g)
+    return out
+
+
+def cpu_params(ps, int8):
+    return [oracle.quantize_block(p) if int8 else p for p in ps]
+
+
+def check_residual(out, ref, x):
+    """Block output at the bf16 bar, and its update out - x close on average (the update is
+    small next to x, so single-step bf16 flips of the residual dominate its max norm)."""
+    assert relerr(out, ref) <= BF16_TOL
+    du = out.double() - x.double()
+    dr = ref.double() - x.double()
+    assert float((du - dr).abs().mean()) <= 0.05 * float(dr.abs().mean())
+
+
+RAGGED = W0.replace(video_t=3, video_h=5, video_w=7, n_text=11, n_audio=5)   # 121 tokens
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("w", [W0, RAGGED], ids=["tiny", "ragged121"])
+def test_block_matches_oracle(w, int8):
+    x, ps = inputs(w)
+    pg = gpu_params(ps, int8)[0]
+    pc = cpu_params(ps, int8)[0]
+    if int8:  # the GPU's weight codes are the oracle's, bit for bit
+        for k in ("qqkv", "sqkv", "qo", "so", "q1", "s1", "q2", "s2"):
+            assert_bitexact(cpu(pg[k]), pc[k], k)
+    xg = x.to(DEV)
+    h3.block_fwd(w, pg, xg)
+    ref = oracle.block_fwd(w, pc, x)
+    check_residual(cpu(xg), ref, x)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_block_zero_gates_is_identity(int8):
+    x, ps = inputs(W0)
+    pg = gpu_params([zero_gates(ps[0])], int8)[0]
+    xg = x.to(DEV)
+    h3.block_fwd(W0, pg, xg)
+    assert_bitexact(cpu(xg), x)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_block_fusion_switches_byte_identical(int8):
+    x, ps = inputs(RAGGED)
+    pg = gpu_params(ps, int8)[0]
+    base = x.to(DEV)
+    h3.block_fwd(RAGGED, pg, base)
+    flags = [h3.NOFUSE_GATE_ADALN, h3.NOFUSE_ROPE, h3.NOFUSE_GELU, h3.NO_ALIAS,
+             h3.NOFUSE_GATE_ADALN | h3.NOFUSE_ROPE | h3.NOFUSE_GELU | h3.NO_ALIAS]
+    if int8:
+        flags += [h3.NOFUSE_QUANT, 63]
+    for f in flags:
+        xg = x.to(DEV)
+        h3.block_fwd(RAGGED, pg, xg, flags=f)
+        assert_bitexact(cpu(xg), cpu(base), f"flags {f}")
+
+
+def test_block_deterministic_and_workspace_reuse():
+    x, ps = inputs(W0)
+    pg = gpu_params(ps, False)[0]
+    ws = h3.alloc_workspace(h3.block_workspace(W0, pg))
+    outs = []
+    for fill in (0, 255, 0x7F):
+        ws.fill_(fill)                 # whatever the workspace held before must not matter
+        xg = x.to(DEV)
+        h3.block_fwd(W0, pg, xg, workspace=ws)
+        outs.append(cpu(xg))
+    assert_bitexact(outs[1], outs[0])
+    assert_bitexact(outs[2], outs[0])
+
+
+SMALL_TR = WORKLOADS[4].replace(video_t=2, video_h=3, video_w=7, n_text=9, n_audio=5, hidden=256, heads=4,
+                                head_dim=64, mlp=1024)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_stack_matches_oracle(int8):
+    w = W0
+    x, ps = inputs(w, blocks=3)
+    pg = gpu_params(ps, int8)
+    xg = x.to(DEV)
+    h3.stack_fwd(w, pg, xg)
+    ref = oracle.stack_fwd(w, cpu_params(ps, int8), x, fused=True)
+    check_residual(cpu(xg), ref, x)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_stack_token_reduction_matches_oracle(int8):
+    w = SMALL_TR
+    x, ps = inputs(w, blocks=6)
+    pg = gpu_params(ps, int8)
+    xg = x.to(DEV)
+    h3.stack_fwd(w, pg, xg, reduction=(1, 4))
+    ref = oracle.stack_fwd(w, cpu_params(ps, int8), x, reduce_after=1, restore_before=4, fused=True)
+    check_residual(cpu(xg), ref, x)
+
+
+def test_stack_cross_block_fusion_byte_identical():
+    x, ps = inputs(SMALL_TR, blocks=6)
+    pg = gpu_params(ps, False)
+    outs = []
+    for f in (0, h3.NOFUSE_CROSS_BLOCK, h3.NOFUSE_GATE_ADALN, h3.NO_ALIAS):
+        xg = x.to(DEV)
+        h3.stack_fwd(SMALL_TR, pg, xg, flags=f, reduction=(1, 4))
+        outs.append(cpu(xg))
+    for o in outs[1:]:
+        assert_bitexact(o, outs[0])
+
+
+def test_stack_equals_block_sequence():
+    x, ps = inputs(W0, blocks=3)
+    pg = gpu_params(ps, False)
+    xs = x.to(DEV)
+    h3.stack_fwd(W0, pg, xs)
+    xb = x.to(DEV)
+    for p in pg:
+        h3.block_fwd(W0, p, xb)
+    assert_bitexact(cpu(xs), cpu(xb))
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_stack_reduction_identity_middle(int8):
+    # gates 0 in the reduced span: pair then restore is the identity on every token
+    x, ps = inputs(SMALL_TR, blocks=5)
+    for b in (2, 3):
+        ps[b] = zero_gates(ps[b])
+    pg = gpu_params(ps, int8)
+    xr = x.to(DEV)
+    h3.stack_fwd(SMALL_TR, pg, xr, reduction=(1, 4))
+    xp = x.to(DEV)
+    h3.stack_fwd(SMALL_TR, [pg[0], pg[1], pg[4]], xp)
+    assert_bitexact(cpu(xr), cpu(xp))
+
+
+def test_stack_reduction_restore_after_last_block():
+    # the stack ends inside the reduced span: every token is restored at the end
+    x, ps = inputs(SMALL_TR, blocks=3)
+    pg = gpu_params(ps, False)
+    xg = x.to(DEV)
+    h3.stack_fwd(SMALL_TR, pg, xg, reduction=(0, 40))
+    ref = oracle.stack_fwd(SMALL_TR, ps, x, reduce_after=0, restore_before=40, fused=True)
+    check_residual(cpu(xg), ref, x)

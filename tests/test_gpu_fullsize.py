@@ -1,0 +1,238 @@
+"""Parity at the production sizes, in the launch configuration the benchmark times.
+
+One block of each production workload runs stage by stage through the C ABI (the same
+kernels, shapes and launch parameters the block and stack calls use).  Every stage is then
+checked on sampled token rows against the CPU oracle fed that stage's own GPU inputs
+(teacher forcing), so each check is exact or at the stated tolerance independently of the
+stages before it; the composed stages equal h3dit_block_fwd byte for byte.  Stack-level
+properties (zero gates, block sequencing, token reduction with an identity middle) are
+checked at full size too."""
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import WORKLOADS
+from parity import BF16_TOL, assert_bitexact, assert_close_bf16, relerr, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+h3 = pytest.importorskip("audio_diffusion_transformer_dit_amd")
+DEV = "cuda"
+
+
+def cpu(t):
+    torch.cuda.synchronize()
+    return t.to("cpu")
+
+
+def run_stages(w, p, x, cos, sin, int8):
+    """One block as separate stage calls; returns every intermediate (device tensors)."""
+    N, d, f, H, hd, G = x.shape[0], w.hidden, w.mlp, w.heads, w.head_dim, w.fc2_group
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    mod = p["mod"]
+    T = {"x": x}
+    T["h1"] = torch.empty((N, d), **bf)
+    T["q"] = torch.empty((H, N, hd), **bf)
+    T["k"] = torch.empty_like(T["q"])
+    T["vt"] = torch.empty((H, hd, h3.ldv(N)), **bf)
+    T["o"] = torch.empty_like(T["q"])
+    T["y1"] = torch.empty((N, d), **bf)
+    T["x1"] = torch.empty((N, d), **bf)
+    T["h2"] = torch.empty((N, d), **bf)
+    T["gl"] = torch.empty((N, f), **bf)
+    T["y2"] = torch.empty((N, d), **bf)
+    T["x2"] = torch.empty((N, d), **bf)
+    T["t"] = torch.empty((N, 3 * d), **bf)
+    T["u"] = torch.empty((N, f), **bf)
+    qkv = dict(cos=cos, sin=sin, heads=H, head_dim=hd, out_q=T["q"], out_k=T["k"], out_v=T["vt"])
+    # t and u: the same projections with the plain epilogue (the value the fused rotary and
+    # GELU epilogues start from), so each epilogue is checked from its own input
+    if not int8:
+        h3.row_gate_adaln(x, shift=mod[0], scale=mod[1], h=T["h1"])
+        h3.linear(N, 3 * d, d, T["h1"], p["wqkv"], h3.OUT_BF16, T["t"])
+        h3.linear(N, 3 * d, d, T["h1"], p["wqkv"], h3.OUT_QKV, None, **qkv)
+        h3.attention(H, N, hd, T["q"], T["k"], T["vt"], T["o"])
+        h3.linear(N, d, d, T["o"], p["wo"], h3.OUT_BF16, T["y1"], a_headmajor_hd=hd)
+        h3.row_gate_adaln(x, gate=mod[2], y=T["y1"], x_out=T["x1"], shift=mod[3], scale=mod[4], h=T["h2"])
+        h3.linear(N, f, d, T["h2"], p["w1"], h3.OUT_BF16, T["u"])
+        h3.linear(N, f, d, T["h2"], p["w1"], h3.OUT_GELU, T["gl"])
+        h3.linear(N, d, f, T["gl"], p["w2"], h3.OUT_BF16, T["y2"])
+    else:
+        i8 = dict(dtype=torch.int8, device=DEV)
+        f32 = dict(dtype=torch.float32, device=DEV)
+        T["q1"], T["s1"] = torch.empty((N, d), **i8), torch.empty(N, **f32)
+        T["q2"], T["s2"] = torch.empty((N, d), **i8), torch.empty(N, **f32)
+        h3.row_gate_adaln(x, shift=mod[0], scale=mod[1], h=T["h1"], q=T["q1"], s=T["s1"])
+        h3.linear(N, 3 * d, d, T["q1"], p["qqkv"], h3.OUT_BF16, T["t"], precision=h3.INT8, a_scale=T["s1"],
+                  w_scale=p["sqkv"])
+        h3.linear(N, 3 * d, d, T["q1"], p["qqkv"], h3.OUT_QKV, None, precision=h3.INT8, a_scale=T["s1"],
+                  w_scale=p["sqkv"], **qkv)
+        h3.attention(H, N, hd, T["q"], T["k"], T["vt"], T["o"])
+        T["qo"], T["so"] = h3.quantize_rows(T["o"], N, d, d, hd)
+        h3.linear(N, d, d, T["qo"], p["qo"], h3.OUT_BF16, T["y1"], precision=h3.INT8, a_scale=T["so"],
+                  w_scale=p["so"])
+        h3.row_gate_adaln(x, gate=mod[2], y=T["y1"], x_out=T["x1"], shift=mod[3], scale=mod[4], h=T["h2"],
+                          q=T["q2"], s=T["s2"])
+        h3.linear(N, f, d, T["q2"], p["q1"], h3.OUT_BF16, T["u"], precision=h3.INT8, a_scale=T["s2"],
+                  w_scale=p["s1"])
+        h3.linear(N, f, d, T["q2"], p["q1"], h3.OUT_GELU, T["gl"], precision=h3.INT8, a_scale=T["s2"],
+                  w_scale=p["s1"])
+        T["qg"], T["sg"] = h3.quantize_rows(T["gl"], N, f, G)
+        h3.linear(N, d, f, T["qg"], p["q2"], h3.OUT_BF16, T["y2"], precision=h3.INT8, a_scale=T["sg"], a_group=G,
+                  w_scale=p["s2"])
+    h3.row_gate_adaln(T["x1"], gate=mod[5], y=T["y2"], x_out=T["x2"])
+    torch.cuda.synchronize()
+    return T
+
+
+def check_stages(w, T, pc, cos, sin, int8, R):
+    """Teacher-forced checks of every stage on rows R against the oracle."""
+    H, hd, d, G = w.heads, w.head_dim, w.hidden, w.fc2_group
+    N = T["x"].shape[0]
+    mod = pc["mod"]
+    g = {k: cpu(v) for k, v in T.items()}
+    x = g["x"][R]
+    # AdaLN1 (+ int8 codes of the GPU's own bf16 row)
+    assert_close_bf16(g["h1"][R], oracle.adaln(x, mod[0], mod[1]), "AdaLN1")
+    cs, sn = cos[R], sin[R]
+    # QKV projection + rotary + head split
+    if not int8:
+        assert_close_bf16(g["t"][R], oracle.f32_to_bf16(oracle.gemm_f32(g["h1"][R], pc["wqkv"])), "QKV projection")
+    else:
+        q_ref, s_ref = oracle.q8_rows(g["h1"][R])
+        assert_bitexact(g["q1"][R], q_ref, "AdaLN1 int8 codes")
+        assert_bitexact(g["s1"][R], s_ref[:, 0], "AdaLN1 scales")
+        assert_bitexact(g["t"][R], oracle.dequant_bf16(oracle.gemm_i32(g["q1"][R], pc["qqkv"]), g["s1"][R],
+                                                       pc["sqkv"]), "QKV projection (int8)")
+    # the fused rotary + head-major epilogue, from the projection value it starts from
+    qr, kr, vr = oracle.rope_split(g["t"][R], cs, sn, H, hd)
+    vt_rows = g["vt"][:, :, :N][:, :, R].transpose(1, 2)
+    for name, got, ref in (("q", g["q"][:, R], qr), ("k", g["k"][:, R], kr), ("v", vt_rows, vr)):
+        assert_bitexact(got, ref, f"{name} (rotary + head split epilogue)")
+    # attention: sampled queries against all keys
+    v_all = g["vt"][:, :, :N].transpose(1, 2).contiguous()
+    o_ref = oracle.attention(g["q"][:, R].contiguous(), g["k"], v_all)
+    assert relerr(g["o"][:, R], o_ref) <= BF16_TOL
+    assert float((g["o"][:, R].double() - o_ref.double()).abs().mean()) <= 2e-3 * float(o_ref.double().abs().mean()) + 1e-6
+    # output projection from the head-major attention output
+    o_tok = g["o"][:, R].permute(1, 0, 2).reshape(len(R), d).contiguous()
+    if not int8:
+        assert_close_bf16(g["y1"][R], oracle.f32_to_bf16(oracle.gemm_f32(o_tok, pc["wo"])), "out-proj")
+    else:
+        qo_ref, so_ref = oracle.q8_rows(o_tok)
+        assert_bitexact(g["qo"][R], qo_ref, "attention-output codes")
+        assert_bitexact(g["so"][R], so_ref, "attention-output scales")
+        assert_bitexact(g["y1"][R], oracle.dequant_bf16(oracle.gemm_i32(g["qo"][R], pc["qo"]), g["so"][R, 0], pc["so"]),
+                        "out-proj (int8)")
+    # gate1 + AdaLN2
+    assert_bitexact(g["x1"][R], oracle.gate(x, mod[2], g["y1"][R]), "gate1")
+    assert_close_bf16(g["h2"][R], oracle.adaln(g["x1"][R], mod[3], mod[4]), "AdaLN2")
+    # FC1 + GELU
+    if not int8:
+        assert_close_bf16(g["u"][R], oracle.f32_to_bf16(oracle.gemm_f32(g["h2"][R], pc["w1"])), "FC1")
+    else:
+        q_ref, s_ref = oracle.q8_rows(g["h2"][R])
+        assert_bitexact(g["q2"][R], q_ref, "AdaLN2 int8 codes")
+        assert_bitexact(g["s2"][R], s_ref[:, 0], "AdaLN2 scales")
+        assert_bitexact(g["u"][R], oracle.dequant_bf16(oracle.gemm_i32(g["q2"][R], pc["q1"]), g["s2"][R], pc["s1"]),
+                        "FC1 (int8)")
+    assert_close_bf16(g["gl"][R], oracle.gelu_rows(g["u"][R]), "GELU epilogue")
+    # FC2
+    if not int8:
+        assert_close_bf16(g["y2"][R], oracle.f32_to_bf16(oracle.gemm_f32(g["gl"][R], pc["w2"])), "FC2")
+    else:
+        qg_ref, sg_ref = oracle.q8_rows(g["gl"][R], G)
+        assert_bitexact(g["qg"][R], qg_ref, "FC2 input group codes")
+        assert_bitexact(g["sg"][R], sg_ref, "FC2 input group scales")
+        assert_bitexact(g["y2"][R], oracle.fc2_int8(g["qg"][R], g["sg"][R], pc["q2"], pc["s2"], G), "FC2 (int8 groups)")
+    # gate2
+    assert_bitexact(g["x2"][R], oracle.gate(g["x1"][R], mod[5], g["y2"][R]), "gate2")
+
+
+def block_params(w, seed, int8, block=0):
+    pg = synth.make_block(w, seed, block, DEV)
+    if int8:
+        pg = h3.quantize_block(pg)
+    pc = {k: cpu(v) for k, v in pg.items()}
+    if int8:  # the GPU's weight codes equal the oracle's
+        raw = synth.make_block(w, seed, block, DEV)
+        for src, qk, sk in (("wqkv", "qqkv", "sqkv"), ("w2", "q2", "s2")):
+            q_ref, s_ref = oracle.quantize_weights(cpu(raw[src]))
+            assert_bitexact(pc[qk], q_ref, qk)
+            assert_bitexact(pc[sk], s_ref, sk)
+    return pg, pc
+
+
+CASES = [(1, False, False), (2, True, False), (3, False, False), (3, True, False), (4, True, False), (4, True, True)]
+
+
+@pytest.mark.parametrize("cfg,int8,reduced", CASES, ids=[f"cfg{c}-{'int8' if i else 'bf16'}{'-reduced' if r else ''}"
+                                                        for c, i, r in CASES])
+def test_block_stages_full_size(cfg, int8, reduced):
+    w = WORKLOADS[cfg]
+    seed = synth.seed_for(cfg)
+    x = synth.make_x(w, seed, DEV)
+    cos, sin = h3.rope_tables(w, reduced=reduced, device=DEV)
+    if reduced:
+        nr = cos.shape[0]
+        r = torch.empty((nr, w.hidden), dtype=torch.bfloat16, device=DEV)
+        h3.token_pair(w, x, r)
+        x = r
+    pg, pc = block_params(w, seed, int8)
+    T = run_stages(w, pg, x, cos, sin, int8)
+    N = x.shape[0]
+    R = sample_rows(N, 24, seed=cfg)
+    check_stages(w, T, pc, cpu(cos), cpu(sin), int8, R)
+    if not reduced:
+        # the block call composes exactly these launches
+        xb = x.clone()
+        h3.block_fwd(w, pg, xb)
+        assert_bitexact(cpu(xb), cpu(T["x2"]), "h3dit_block_fwd == stage sequence")
+
+
+def zero_gates(p):
+    p = dict(p)
+    mod = p["mod"].clone()
+    mod[2] = 0
+    mod[5] = 0
+    p["mod"] = mod
+    return p
+
+
+def test_stack50_zero_gates_identity_full_size():
+    w = WORKLOADS[3]
+    seed = synth.seed_for(3)
+    x = synth.make_x(w, seed, DEV)
+    p = zero_gates(synth.make_block(w, seed, 0, DEV))
+    xs = x.clone()
+    h3.stack_fwd(w, [p] * 50, xs)
+    assert_bitexact(cpu(xs), cpu(x))
+
+
+def test_stack_equals_block_calls_full_size():
+    w = WORKLOADS[3]
+    seed = synth.seed_for(3)
+    x = synth.make_x(w, seed, DEV)
+    ps = [synth.make_block(w, seed, b, DEV) for b in range(3)]
+    xs = x.clone()
+    h3.stack_fwd(w, ps, xs)
+    xb = x.clone()
+    for p in ps:
+        h3.block_fwd(w, p, xb)
+    assert_bitexact(cpu(xs), cpu(xb))
+
+
+def test_int8_token_reduction_identity_middle_full_size():
+    w = WORKLOADS[4]
+    seed = synth.seed_for(4)
+    x = synth.make_x(w, seed, DEV)
+    raw = [synth.make_block(w, seed, b, DEV) for b in range(5)]
+    raw[2], raw[3] = zero_gates(raw[2]), zero_gates(raw[3])
+    ps = [h3.quantize_block(p) for p in raw]
+    del raw
+    xr = x.clone()
+    h3.stack_fwd(w, ps, xr, reduction=(1, 4))
+    xp = x.clone()
+    h3.stack_fwd(w, [ps[0], ps[1], ps[4]], xp)
+    assert_bitexact(cpu(xr), cpu(xp))
