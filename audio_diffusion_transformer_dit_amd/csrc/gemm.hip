@@ -2,22 +2,27 @@
 // W [N][K] (out x in) ([DD] "h3.c 的核心设计" and "int8 量化": QKV, attention output, FC1, FC2
 // in bf16 or int8 with per-token / per-channel / per-1024-group scales).
 //
-// Tiling: a workgroup of 4 waves owns a 256 x BN output tile (BN = 256 or 128); waves are
-// 2 x 2, each owning 128 x BN/2 as a grid of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16 or
-// v_mfma_i32_32x32x32_i8; both read 16 bytes of K per lane, so one LDS layout serves both).
-// K advances 128 bytes per step: every row of a step is 8 chunks of 16 B.  Both operands go
-// global -> LDS with buffer_load ... lds (no VGPR staging), double-buffered, chunk c of row r
-// stored at slot c ^ (r & 7) so that the 8 lanes of an LDS read phase hit 8 distinct bank
-// groups.  Rows past M read as zeros (buffer range check).  The epilogue stages the bf16 tile
-// in LDS and writes 16-byte row chunks (or, for V, 16-byte token chunks of V^T).
-// Workgroups are dealt round-robin to the 8 XCDs; the tile order is remapped so that each
-// XCD sweeps a contiguous band of tiles, 8 tile-rows at a time, sharing A and W in its L2.
+// Tiling: a workgroup owns a BM x BN output tile split over a WGM x WGN grid of waves, each
+// wave a grid of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16 or v_mfma_i32_32x32x32_i8; both
+// read 16 bytes of K per lane, so one LDS layout serves both).  The main shape is 256 x 256
+// with 8 waves (two per SIMD, 128 x 64 each): operand streaming from L2 is the bound on
+// gfx950, so the tile is as large as the register file allows, and a second wave per SIMD
+// keeps the matrix pipe busy while the other wave's memory instructions wait for issue.
+// K advances in 128-byte slices (full cache lines per row).  Slices travel global -> VGPR ->
+// LDS: while slice k is multiplied from LDS, slice k+1 waits in the other LDS stage and the
+// loads of slice k+2 are spread between the MFMAs, so each load has a whole iteration to
+// arrive.  Chunk c of row r sits at LDS slot c ^ ((r >> 1) & 7): the 16 lanes of one LDS
+// read phase (16 rows, one chunk) cover all 64 banks.  Fragment reads of the next 16-byte K
+// step overlap the MFMAs of the current one.
+// Rows past M read as zeros (buffer range check).  The epilogue stages the bf16 tile in LDS
+// and writes 16-byte row chunks (or, for V, 16-byte token chunks of V^T).  Workgroups are
+// dealt round-robin to the 8 XCDs; the tile order is remapped so that each XCD sweeps a
+// contiguous band of tiles, 8 tile-rows at a time, sharing A and W in its L2.
 #include "common.hpp"
 
 namespace h3 {
 
-constexpr int GKB = 128;        // bytes of K per step and row
-constexpr int GTHREADS = 256;   // 4 waves
+constexpr int GKB = 128;        // bytes of K per slice and row
 
 struct GemmP {
   const uint8_t *a;
@@ -35,14 +40,19 @@ struct GemmP {
   int tiles_m, tiles_n;
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 struct GemmCfg {
-  static constexpr int FM = BM / 64;                    // 32-row MFMA blocks per wave
-  static constexpr int FN = BN / 64;                    // 32-col MFMA blocks per wave
-  static constexpr int STAGE = (BM + BN) * GKB;         // bytes per LDS stage
+  static constexpr int NW = WGM * WGN;                  // waves
+  static constexpr int NT = NW * 64;                    // threads
+  static constexpr int FM = BM / WGM / 32;              // 32-row MFMA blocks per wave
+  static constexpr int FN = BN / WGN / 32;              // 32-col MFMA blocks per wave
+  static constexpr int STAGE = (BM + BN) * GKB;         // bytes per LDS slice
+  static constexpr int LA = BM / (8 * NW);              // loads per lane per slice (A)
+  static constexpr int LW = BN / (8 * NW);              // loads per lane per slice (W)
   static constexpr int CPITCH = BN * 2 + 16;            // bytes per row of the staged C tile
   static constexpr int CTILE = BM * CPITCH;
   static constexpr int LDS = (2 * STAGE > CTILE) ? 2 * STAGE : CTILE;
+  static_assert(LA >= 1 && LW >= 1 && FM >= 1 && FN >= 1, "tile shape");
 };
 
 __device__ __forceinline__ void tile_coords(int &tm, int &tn, int tiles_m, int tiles_n) {
@@ -59,56 +69,70 @@ __device__ __forceinline__ void tile_coords(int &tm, int &tn, int tiles_m, int t
   tn = r / gsize;
 }
 
-// Issues the loads of one K step (rows m0.. of A, n0.. of W) into LDS stage `st`.
-template <int BM, int BN, bool INT8>
-__device__ __forceinline__ void load_stage(const GemmP &p, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rw,
-                                           uint8_t *st, int64_t m0, int64_t n0, int kt) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int rl = lane >> 3;           // row within the 8-row group of this instruction
-  const int slot = lane & 7;          // LDS slot of this lane
-  const int chunk = slot ^ rl;        // global chunk it fetches
-  const int64_t esz = INT8 ? 1 : 2;
-  const int64_t kel = (int64_t)kt * (GKB / esz) + chunk * (16 / esz);   // K element index
-#pragma unroll
-  for (int i = 0; i < BM / 32; i++) {
-    const int rb = i * 4 + wid;                 // 8-row block
-    const int64_t m = m0 + rb * 8 + rl;
-    uint32_t off;
-    if (!INT8 && p.hm_hd > 0)
-      off = (uint32_t)((((kel / p.hm_hd) * p.M + m) * p.hm_hd + kel % p.hm_hd) * 2);
-    else
-      off = (uint32_t)((m * p.K + kel) * esz);
-    buffer_load_lds16(ra, (lds_void *)(st + rb * 8 * GKB), off);
-  }
-#pragma unroll
-  for (int i = 0; i < BN / 32; i++) {
-    const int rb = i * 4 + wid;
-    const int64_t n = n0 + rb * 8 + rl;
-    const uint32_t off = (uint32_t)((n * p.K + kel) * esz);
-    buffer_load_lds16(rw, (lds_void *)(st + BM * GKB + rb * 8 * GKB), off);
-  }
-}
-
 __device__ __forceinline__ u32x4 lds_frag(const uint8_t *base, int row, int chunk) {
-  return *reinterpret_cast<const u32x4 *>(base + row * GKB + ((chunk ^ (row & 7)) << 4));
+  return *reinterpret_cast<const u32x4 *>(base + row * GKB + ((chunk ^ ((row >> 1) & 7)) << 4));
 }
 
 // out_kind: H3DIT_OUT_*.  GROUPED: int8 FC2 with per-(row, group) activation scales.
-template <int BM, int BN, bool INT8, int OUT, bool GROUPED>
-__global__ __launch_bounds__(GTHREADS, 1) void k_gemm(GemmP p) {
-  using C = GemmCfg<BM, BN>;
-  constexpr int FM = C::FM, FN = C::FN;
+template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
+  using C = GemmCfg<BM, BN, WGM, WGN>;
+  constexpr int FM = C::FM, FN = C::FN, NW = C::NW, NT = C::NT, LA = C::LA, LW = C::LW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
 
   int tm, tn;
   tile_coords(tm, tn, p.tiles_m, p.tiles_n);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  const int esz = INT8 ? 1 : 2;
+  const int wm = wid / WGN, wn = wid % WGN;
+  constexpr int esz = INT8 ? 1 : 2;
   const uint32_t a_bytes = (uint32_t)(p.M * p.K * esz), w_bytes = (uint32_t)(p.N * p.K * esz);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, a_bytes), rw = make_rsrc(p.w, w_bytes);
   const int KT = (int)(p.K * esz / GKB);
+
+  // Per-lane load offsets.  A slice of the tile is (BM + BN) rows x 128 B; lanes take it in
+  // 1 KiB blocks of 8 rows (8 consecutive lanes = one row's 8 chunks), so every global load
+  // instruction reads whole 128-byte lines.  Block i of wave w covers rows (i*NW + w)*8 .. +7.
+  // Within a lane all blocks share the row-in-block and chunk, and (NW even) the
+  // swizzle too, so each operand needs one per-lane offset; the block stride and the slice
+  // offset go into the scalar offset of the buffer load.
+  static_assert(NW % 2 == 0, "blocks of one lane share the swizzle when the block stride is a multiple of 16 rows");
+  const int rl = lane >> 3, cl = lane & 7;
+  const bool hm = !INT8 && p.hm_hd > 0;
+  const int r0 = wid * 8 + rl;                         // row of block 0
+  const int sw = (cl ^ ((r0 >> 1) & 7)) << 4;          // swizzled 16-byte slot (same for every block)
+  const uint32_t a_voff = hm ? (uint32_t)((m0 + r0) * p.hm_hd * 2 + cl * 16) : (uint32_t)((m0 + r0) * p.K * esz + cl * 16);
+  const uint32_t w_voff = (uint32_t)((n0 + r0) * p.K * esz + cl * 16);
+  const uint32_t a_bstride = hm ? (uint32_t)(NW * 8 * p.hm_hd * 2) : (uint32_t)(NW * 8 * p.K * esz);
+  const uint32_t w_bstride = (uint32_t)(NW * 8 * p.K * esz);
+  const uint32_t lds0 = (uint32_t)(r0 * GKB + sw);     // LDS byte offset of block 0 (A); blocks step NW*1 KiB
+  // Offset of K slice kt inside an A row, without branches: head-major bf16 input places
+  // element k at (k / hd) * (M*hd*2) + (k % hd) * 2 bytes past the row start; token-major is
+  // the same formula with shift 31, head stride 0 and a full mask (k * 2 bytes).
+  const uint32_t hm_head = hm ? (uint32_t)(p.M * p.hm_hd * 2) : 0u;
+  const uint32_t hm_shift = hm ? (p.hm_hd == 128 ? 7u : 6u) : 31u;
+  const uint32_t hm_mask = hm ? (uint32_t)(p.hm_hd - 1) : 0xFFFFFFFFu;
+
+  // Slices travel global -> registers -> LDS: registers hold slice kt+2 while LDS holds slices
+  // kt (multiplied) and kt+1 (ready), so each load has a whole iteration to arrive.
+  constexpr int NL = LA + LW;                       // 16-byte loads per lane per slice
+  u32x4 stage_reg[2][NL];
+  auto load_one = [&](u32x4 *dst, int kt, int li) {
+    const uint32_t kb = (uint32_t)kt * GKB;   // byte offset of the slice inside a W row
+    if (li < LA) {
+      const uint32_t kel = kb >> 1;           // a slice never crosses a head
+      const uint32_t ka = INT8 ? kb : (kel >> hm_shift) * hm_head + ((kel & hm_mask) << 1);
+      dst[li] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff, ka + li * a_bstride, 0));
+    } else {
+      dst[li] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, kb + (li - LA) * w_bstride, 0));
+    }
+  };
+  auto store_slice = [&](const u32x4 *src, int kt) {
+    uint8_t *st = smem + (kt & 1) * C::STAGE + lds0;
+#pragma unroll
+    for (int li = 0; li < NL; li++)
+      *reinterpret_cast<u32x4 *>(st + (li < LA ? li * NW * 1024 : BM * GKB + (li - LA) * NW * 1024)) = src[li];
+  };
 
   using AccT = typename std::conditional<INT8, i32x16, f32x16>::type;
   AccT acc[FM][FN];
@@ -123,37 +147,60 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(GemmP p) {
 #pragma unroll
       for (int j = 0; j < FN; j++) sum[i][j] = f32x16{0};
   }
-  const int kt_per_group = GROUPED ? p.a_group / GKB : 0;
+  const int kt_per_group = GROUPED ? p.a_group * esz / GKB : 0;
   const int n_groups = GROUPED ? (int)(p.K / p.a_group) : 0;
 
-  load_stage<BM, BN, INT8>(p, ra, rw, smem, m0, n0, 0);
-  wait_vmem();
+  const int arow0 = wm * (BM / WGM) + (lane & 31);
+  const int brow0 = wn * (BN / WGN) + (lane & 31);
+  const int hsel = lane >> 5;
+  auto read_step = [&](const uint8_t *sa, int ks, u32x4 *fa, u32x4 *fb) {
+    const uint8_t *sb = sa + BM * GKB;
+#pragma unroll
+    for (int i = 0; i < FM; i++) fa[i] = lds_frag(sa, arow0 + 32 * i, 2 * ks + hsel);
+#pragma unroll
+    for (int j = 0; j < FN; j++) fb[j] = lds_frag(sb, brow0 + 32 * j, 2 * ks + hsel);
+  };
+
+  // prologue: slice 0 into LDS stage 0, slice 1 in registers
+#pragma unroll
+  for (int li = 0; li < NL; li++) load_one(stage_reg[0], 0, li);
+#pragma unroll
+  for (int li = 0; li < NL; li++) load_one(stage_reg[1], KT > 1 ? 1 : 0, li);
+  store_slice(stage_reg[0], 0);
   __syncthreads();
 
-  const int arow0 = wm * (BM / 2) + (lane & 31);
-  const int brow0 = wn * (BN / 2) + (lane & 31);
-  const int hsel = lane >> 5;
-  for (int kt = 0; kt < KT; kt++) {
-    uint8_t *cur = smem + (kt & 1) * C::STAGE;
-    if (kt + 1 < KT) load_stage<BM, BN, INT8>(p, ra, rw, smem + ((kt + 1) & 1) * C::STAGE, m0, n0, kt + 1);
-    const uint8_t *sa = cur, *sb = cur + BM * GKB;
+  // Iteration kt: registers of slice kt+1 -> LDS stage (kt+1)&1 (last read in iteration kt-1),
+  // loads of slice kt+2 spread between the MFMAs of slice kt, barrier.  Past the end the loads
+  // repeat the last slice (in range, never stored).  sched_barrier fixes the issue order.
+  constexpr int NMMA = 4 * FM * FN;                 // MFMAs per slice; load li follows MFMA li*NMMA/NL
+  auto iteration = [&](int kt, const u32x4 *cur, u32x4 *nxt) {
+    if (kt + 1 < KT) store_slice(cur, kt + 1);
+    const int ktl = kt + 2 < KT ? kt + 2 : KT - 1;
+    const uint8_t *sa = smem + (kt & 1) * C::STAGE;
+    u32x4 fa[2][FM], fb[2][FN];
+    read_step(sa, 0, fa[0], fb[0]);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-      u32x4 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; i++) af[i] = lds_frag(sa, arow0 + 32 * i, 2 * ks + hsel);
-#pragma unroll
-      for (int j = 0; j < FN; j++) bfr[j] = lds_frag(sb, brow0 + 32 * j, 2 * ks + hsel);
+      if (ks < 3) read_step(sa, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; i++)
 #pragma unroll
         for (int j = 0; j < FN; j++) {
+          const int m = (ks * FM + i) * FN + j;
           if constexpr (INT8)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, af[i]),
-                                                              __builtin_bit_cast(i32x4, bfr[j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa[ks & 1][i]),
+                                                              __builtin_bit_cast(i32x4, fb[ks & 1][j]), acc[i][j], 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
-                                                                __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[ks & 1][i]),
+                                                                __builtin_bit_cast(bf16x8, fb[ks & 1][j]), acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int li = 0; li < NL; li++)
+            if (li * NMMA / NL == m) {
+              __builtin_amdgcn_sched_barrier(0);
+              load_one(nxt, ktl, li);
+              __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     if constexpr (GROUPED) {
@@ -163,7 +210,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(GemmP p) {
         for (int i = 0; i < FM; i++)
 #pragma unroll
           for (int r = 0; r < 16; r++) {
-            const int64_t row = m0 + wm * (BM / 2) + 32 * i + 8 * (r / 4) + 4 * hsel + (r % 4);
+            const int64_t row = m0 + wm * (BM / WGM) + 32 * i + 8 * (r / 4) + 4 * hsel + (r % 4);
             const float s = row < p.M ? p.a_scale[row * n_groups + g] : 0.0f;
 #pragma unroll
             for (int j = 0; j < FN; j++) {
@@ -173,15 +220,20 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(GemmP p) {
           }
       }
     }
-    wait_vmem();
     __syncthreads();
+  };
+  // two iterations per trip so that each register set is addressed statically
+  for (int kt = 0; kt < KT; kt += 2) {
+    iteration(kt, stage_reg[1], stage_reg[0]);
+    if (kt + 1 < KT) iteration(kt + 1, stage_reg[0], stage_reg[1]);
   }
+  wait_vmem();   // the register loads past the end
 
   // ---------------------------------------------------------------- epilogue
-  // value of accumulator (i, j, r): row = m0 + wm*BM/2 + 32 i + 8 (r/4) + 4 hsel + r%4,
-  //                                 col = n0 + wn*BN/2 + 32 j + lane%32
-  const int rbase = wm * (BM / 2) + 4 * hsel;
-  const int cbase = wn * (BN / 2) + (lane & 31);
+  // value of accumulator (i, j, r): row = m0 + wm*BM/WGM + 32 i + 8 (r/4) + 4 hsel + r%4,
+  //                                 col = n0 + wn*BN/WGN + 32 j + lane%32
+  const int rbase = wm * (BM / WGM) + 4 * hsel;
+  const int cbase = wn * (BN / WGN) + (lane & 31);
   if constexpr (OUT == H3DIT_OUT_F32 || OUT == H3DIT_OUT_I32) {
 #pragma unroll
     for (int i = 0; i < FM; i++)
@@ -239,7 +291,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(GemmP p) {
       if (part < 2) {
         uint16_t *dst = part == 0 ? p.oq : p.ok;
         const int half = p.hd / 2;
-        for (int idx = tid; idx < BM * CH; idx += GTHREADS) {
+        for (int idx = tid; idx < BM * CH; idx += NT) {
           const int r = idx / CH, c = idx % CH;
           const int64_t row = m0 + r;
           if (row >= p.M) continue;
@@ -260,7 +312,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(GemmP p) {
       } else {
         // V^T[h][i][m]: one lane per (feature column, block of 8 tokens)
         const bool vec = (p.ldv % 8) == 0;
-        for (int idx = tid; idx < BN * (BM / 8); idx += GTHREADS) {
+        for (int idx = tid; idx < BN * (BM / 8); idx += NT) {
           const int c = idx % BN, rb = idx / BN;
           const int col = (int)(n0 % d) + c;
           const int h = col / p.hd, i = col % p.hd;
@@ -283,7 +335,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(GemmP p) {
       }
     } else {
       uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
-      for (int idx = tid; idx < BM * CH; idx += GTHREADS) {
+      for (int idx = tid; idx < BM * CH; idx += NT) {
         const int r = idx / CH, c = idx % CH;
         const int64_t row = m0 + r;
         if (row >= p.M) continue;
@@ -301,12 +353,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(GemmP p) {
   }
 }
 
-template <int BM, int BN, bool INT8, int OUT, bool GROUPED>
+template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED>
 static hipError_t run_gemm(GemmP p, hipStream_t st) {
   p.tiles_m = (int)((p.M + BM - 1) / BM);
   p.tiles_n = (int)(p.N / BN);
   const unsigned nwg = (unsigned)p.tiles_m * p.tiles_n;
-  k_gemm<BM, BN, INT8, OUT, GROUPED><<<nwg, GTHREADS, 0, st>>>(p);
+  k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED><<<nwg, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -320,11 +372,12 @@ static int pick_bn(int64_t M, int64_t N) {
 template <bool INT8, int OUT, bool GROUPED>
 static hipError_t dispatch_bn(const GemmP &p, int bn, hipStream_t st) {
   if constexpr (GROUPED) {
-    // two accumulator sets (int32 per group, fp32 across groups) per lane: 128 x 128 tiles
-    return run_gemm<128, 128, INT8, OUT, GROUPED>(p, st);
+    // two accumulator sets (int32 per group, fp32 across groups) per lane: 128 x 128 tiles,
+    // 4 waves of 64 x 64
+    return run_gemm<128, 128, 2, 2, INT8, OUT, GROUPED>(p, st);
   } else {
-    if (bn == 256) return run_gemm<256, 256, INT8, OUT, GROUPED>(p, st);
-    return run_gemm<256, 128, INT8, OUT, GROUPED>(p, st);
+    if (bn == 256) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED>(p, st);
+    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED>(p, st);
   }
 }
 
