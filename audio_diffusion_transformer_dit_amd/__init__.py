@@ -123,8 +123,28 @@ def layout_of(w) -> Layout:
 
 
 def ldv(n: int) -> int:
-    """Row pitch of V^T [H][hd][ldv]: tokens rounded up to a multiple of 8."""
-    return (int(n) + 7) // 8 * 8
+    """Row pitch of V^T [H][hd][ldv]: tokens rounded up to a multiple of 16."""
+    return (int(n) + 15) // 16 * 16
+
+
+def vt_positions(n: int) -> torch.Tensor:
+    """Column of token t inside a V^T row: keys are permuted within groups of 16 (bits 2 and
+    3 of the index swapped), the layout the attention kernel reads."""
+    t = torch.arange(int(n), dtype=torch.int64)
+    return (t & ~15) | (t & 3) | ((t & 4) << 1) | ((t & 8) >> 1)
+
+
+def vt_from_v(v: torch.Tensor) -> torch.Tensor:
+    """V^T [H][hd][ldv] (padding zero) from head-major values [H][n][hd]."""
+    H, n, hd = v.shape
+    out = torch.zeros((H, hd, ldv(n)), dtype=v.dtype, device=v.device)
+    out[:, :, vt_positions(n).to(v.device)] = v.transpose(1, 2)
+    return out
+
+
+def v_from_vt(vt: torch.Tensor, n: int) -> torch.Tensor:
+    """Head-major values [H][n][hd] read back from V^T."""
+    return vt[:, :, vt_positions(n).to(vt.device)].transpose(1, 2)
 
 
 # ------------------------------------------------------------------ h3dit.h

@@ -92,7 +92,7 @@ struct Plan {
 
 Plan make_plan(const h3dit_dims &D, const h3dit_layout &L, int precision, uint32_t flags, bool reduction) {
   const size_t N = (size_t)D.n_tokens, d = (size_t)D.hidden, f = (size_t)D.mlp, hd = (size_t)D.head_dim;
-  const size_t ldv = (N + 7) / 8 * 8;
+  const size_t ldv = (size_t)vt_pitch((int64_t)N);
   const bool i8 = precision == H3DIT_INT8;
   const size_t Nd2 = N * d * 2;
   Plan p;
@@ -459,7 +459,7 @@ int h3dit_attention(int32_t heads, int64_t n, int32_t head_dim, const uint16_t *
   if (!q || !k || !vt || !o || !aligned(q, 16) || !aligned(k, 16) || !aligned(vt, 16) || !aligned(o, 16))
     return H3DIT_EINVAL;
   if ((row_max == nullptr) != (row_sum == nullptr)) return H3DIT_EINVAL;
-  const int64_t ldv = (n + 7) / 8 * 8;
+  const int64_t ldv = vt_pitch(n);
   if ((int64_t)heads * (n + 64) * head_dim * 2 >= ((int64_t)1 << 32) ||
       (int64_t)heads * head_dim * (ldv + 64) * 2 >= ((int64_t)1 << 32))
     return H3DIT_EINVAL;

@@ -7,9 +7,11 @@
 // one query column: the row max and row sum are 16 lane-local values plus one exchange with
 // the other half-wave, and the rescale of the output is a per-lane scalar.  O^T = V^T P^T
 // reuses the score registers as the B operand; the key order inside a 16-key step is the
-// score layout's (4 keys from each 8-key half), and the A operand (V^T, stored [hd][keys])
-// is read in that same order, two 8-byte LDS reads per step.  K and V^T tiles go global ->
-// LDS with buffer_load ... lds, double-buffered, chunk c of row r at slot c ^ (r & 7).
+// score layout's (4 keys from each 8-key half), and V^T is stored with keys permuted inside
+// each 16-key group (vt_pos) so that those 8 keys are adjacent: one 16-byte LDS read per step.
+// K and V^T tiles go global -> LDS with buffer_load ... lds, double-buffered; the 16-byte
+// chunks of a row are XOR-swizzled so that the 16 lanes of an LDS read phase (16 rows, one
+// chunk) cover all 64 banks: c ^ (r & 15) for 256-byte rows, c ^ ((r >> 1) & 7) for 128.
 #include "common.hpp"
 
 namespace h3 {
@@ -27,6 +29,11 @@ struct AttCfg {
   static constexpr int STAGE = KBYTES + VBYTES;
 };
 
+// LDS slot of 16-byte chunk c in row r of a tile whose rows are `chunks` chunks long
+__device__ __forceinline__ int att_slot(int c, int r, int chunks) {
+  return chunks >= 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
 template <int HD>
 __device__ __forceinline__ void att_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint8_t *st,
                                          int64_t kbase_row, int64_t vbase_row, int ldv, int kb) {
@@ -41,7 +48,7 @@ __device__ __forceinline__ void att_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
     for (int i = 0; i < AKV / (KRPI * 4); i++) {
       const int rb = i * 4 + wid;
       const int row = rb * KRPI + rl;
-      const int chunk = slot ^ (row & 7);
+      const int chunk = att_slot(slot, row, KCH);
       const uint32_t off = (uint32_t)(((kbase_row + (int64_t)kb * AKV + row) * HD + chunk * 8) * 2);
       buffer_load_lds16(rk, (lds_void *)(st + rb * 1024), off);
     }
@@ -53,7 +60,7 @@ __device__ __forceinline__ void att_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
     for (int i = 0; i < HD / 32; i++) {
       const int rb = i * 4 + wid;
       const int row = rb * 8 + rl;
-      const int chunk = slot ^ (row & 7);
+      const int chunk = att_slot(slot, row, 8);
       const uint32_t off = (uint32_t)((((vbase_row + row) * (int64_t)ldv) + (int64_t)kb * AKV + chunk * 8) * 2);
       buffer_load_lds16(rv, (lds_void *)(st + C::KBYTES + rb * 1024), off);
     }
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; t++) acc[t] = f32x16{0};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;   // running max of raw scores, running sum
 
   wait_vmem();
   __syncthreads();
@@ -108,8 +115,10 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
       // keys past the end: zero their values so that 0-weight * garbage stays 0
       for (int idx = threadIdx.x; idx < HD * AKV; idx += ATHREADS) {
         const int row = idx / AKV, key = idx % AKV;
-        if (key >= valid)
-          *reinterpret_cast<uint16_t *>(cur + C::KBYTES + row * C::VROW + (((key >> 3) ^ (row & 7)) << 4) + (key & 7) * 2) = 0;
+        if (key >= valid) {
+          const int ps = (int)vt_pos(key);   // physical position of the key in the row
+          *reinterpret_cast<uint16_t *>(cur + C::KBYTES + row * C::VROW + (att_slot(ps >> 3, row, 8) << 4) + (ps & 7) * 2) = 0;
+        }
       }
       __syncthreads();
     }
@@ -121,41 +130,51 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
       const int krow = t * 32 + l32;
 #pragma unroll
       for (int st = 0; st < KS; st++) {
-        const u32x4 kf = *reinterpret_cast<const u32x4 *>(cur + krow * C::KROW + (((2 * st + hsel) ^ (krow & 7)) << 4));
+        const u32x4 kf = *reinterpret_cast<const u32x4 *>(cur + krow * C::KROW + (att_slot(2 * st + hsel, krow, HD / 8) << 4));
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[st]),
                                                        s[t], 0, 0, 0);
       }
     }
-    // online softmax over this block (lane = one query; rows r are keys)
-    float mb = -INFINITY;
+    // online softmax over this block (lane = one query; rows r are keys).  The max is taken
+    // on raw scores (the scale c2 > 0 keeps the order); p = 2^(s*c2 - m*c2) with one fma.
+    // Keys past the end exist only in the last block.
+    if (valid < AKV) {
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int key = t * 32 + 8 * (r / 4) + 4 * hsel + (r % 4);
+          if (key >= valid) s[t][r] = -INFINITY;
+        }
+    }
+    float mb = s[0][0];
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int key = t * 32 + 8 * (r / 4) + 4 * hsel + (r % 4);
-        const float v = key < valid ? s[t][r] * c2 : -INFINITY;
-        s[t][r] = v;
-        mb = fmaxf(mb, v);
-      }
+      for (int r = 0; r < 16; r++) mb = fmaxf(mb, s[t][r]);
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);
-    const float corr = exp2f(m_run - m_new);
+    const float m_new = fmaxf(m_run, mb);          // raw units
+    const float mc = m_new * c2;
+    const float corr = __builtin_amdgcn_exp2f(m_run * c2 - mc);   // 0 on the first block
     float ls = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const float p = exp2f(s[t][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c2, -mc));
         s[t][r] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, 64);
     l_run = l_run * corr + ls;
     m_run = m_new;
+    // rescale the output only if some query's max moved (corr == 1 exactly otherwise)
+    if (__any(corr != 1.0f)) {
 #pragma unroll
-    for (int t = 0; t < DT; t++)
+      for (int t = 0; t < DT; t++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) acc[t][r] *= corr;
+        for (int r = 0; r < 16; r++) acc[t][r] *= corr;
+    }
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
     for (int ps = 0; ps < 4; ps++) {
@@ -163,15 +182,11 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
       bf16x8 pf;
 #pragma unroll
       for (int j = 0; j < 8; j++) pf[j] = (__bf16)s[t][rb + j];
-      const int key0 = 16 * ps + 4 * hsel;   // keys key0..key0+3 and key0+8..key0+11
+      // keys 16ps+4h..+3 and 16ps+8+4h..+3 sit at positions 16ps+8h..+7: chunk 2ps+h of the row
 #pragma unroll
       for (int dt = 0; dt < DT; dt++) {
         const int row = dt * 32 + l32;
-        const uint8_t *vr = cur + C::KBYTES + row * C::VROW;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vr + (((key0 >> 3) ^ (row & 7)) << 4) + (key0 & 7) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vr + ((((key0 + 8) >> 3) ^ (row & 7)) << 4) + (key0 & 7) * 2);
-        u32x4 vf;
-        vf[0] = lo.x; vf[1] = lo.y; vf[2] = hi.x; vf[3] = hi.y;
+        const u32x4 vf = *reinterpret_cast<const u32x4 *>(cur + C::KBYTES + row * C::VROW + (att_slot(2 * ps + hsel, row, 8) << 4));
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf), pf, acc[dt], 0, 0, 0);
       }
     }
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
         *reinterpret_cast<uint2 *>(dst + dim) = v;
       }
     if (row_max && hsel == 0) {
-      row_max[head_rows + qrow] = m_run * 0.6931471805599453f;
+      row_max[head_rows + qrow] = m_run * (1.0f / sqrtf((float)HD));
       row_sum[head_rows + qrow] = l_run;
     }
   }
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
 hipError_t launch_attention(int heads, int64_t n, int hd, const uint16_t *q, const uint16_t *k, const uint16_t *vt,
                             uint16_t *o, float *row_max, float *row_sum, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  const int ldv = (int)((n + 7) / 8 * 8);
+  const int ldv = (int)vt_pitch(n);
   dim3 grid((unsigned)((n + AQ - 1) / AQ), (unsigned)heads);
   if (hd == 128)
     k_attention<128><<<grid, ATHREADS, 0, st>>>(q, k, vt, o, n, ldv, heads, row_max, row_sum);

@@ -72,6 +72,15 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// V^T layout: row pitch (tokens rounded up to 16) and the position of token n in a row.  Keys
+// are permuted inside each group of 16 (bits 2 and 3 of the index swapped) so that the 8 keys
+// one lane contributes to a 16-key MFMA step of the attention value product - keys
+// 4h..4h+3 and 8+4h..8+4h+3 of the step - are adjacent (one 16-byte LDS read).
+__host__ __device__ __forceinline__ int64_t vt_pitch(int64_t n) { return (n + 15) / 16 * 16; }
+__host__ __device__ __forceinline__ int64_t vt_pos(int64_t n) {
+  return (n & ~(int64_t)15) | (n & 3) | ((n & 4) << 1) | ((n & 8) >> 1);
+}
+
 // GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))
 __device__ __forceinline__ float gelu_tanh(float u) {
   float u3 = u * u * u;

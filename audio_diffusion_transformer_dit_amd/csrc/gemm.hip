@@ -149,6 +149,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   }
   const int kt_per_group = GROUPED ? p.a_group * esz / GKB : 0;
   const int n_groups = GROUPED ? (int)(p.K / p.a_group) : 0;
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.a_scale, GROUPED ? (uint32_t)(p.M * n_groups * 4) : 0u);
+  const uint32_t sc_voff =
+      (uint32_t)((m0 + wm * (BM / WGM) + 4 * (lane >> 5)) * n_groups * 4);   // this lane's first row
 
   const int arow0 = wm * (BM / WGM) + (lane & 31);
   const int brow0 = wn * (BN / WGN) + (lane & 31);
@@ -206,18 +209,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
     if constexpr (GROUPED) {
       if ((kt + 1) % kt_per_group == 0) {
         const int g = kt / kt_per_group;
+        // one 32-row block at a time, so that only 16 row scales are live; scales are read
+        // through a buffer resource (rows past M read 0): per-lane row base in the vector
+        // offset, row-in-block and group in the scalar offset
 #pragma unroll
-        for (int i = 0; i < FM; i++)
+        for (int i = 0; i < FM; i++) {
+          float sc[16];
 #pragma unroll
           for (int r = 0; r < 16; r++) {
-            const int64_t row = m0 + wm * (BM / WGM) + 32 * i + 8 * (r / 4) + 4 * hsel + (r % 4);
-            const float s = row < p.M ? p.a_scale[row * n_groups + g] : 0.0f;
+            const uint32_t soff = (uint32_t)(((32 * i + 8 * (r / 4) + (r % 4)) * n_groups + g) * 4);
+            sc[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, sc_voff, soff, 0));
+          }
+#pragma unroll
+          for (int r = 0; r < 16; r++)
 #pragma unroll
             for (int j = 0; j < FN; j++) {
-              sum[i][j][r] = sum[i][j][r] + (float)acc[i][j][r] * s;
+              sum[i][j][r] = sum[i][j][r] + (float)acc[i][j][r] * sc[r];
               acc[i][j][r] = 0;
             }
-          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     __syncthreads();
@@ -310,26 +321,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
           *reinterpret_cast<u32x4 *>(dst + ((int64_t)h * p.M + row) * p.hd + i0) = pack8(o);
         }
       } else {
-        // V^T[h][i][m]: one lane per (feature column, block of 8 tokens)
-        const bool vec = (p.ldv % 8) == 0;
-        for (int idx = tid; idx < BN * (BM / 8); idx += NT) {
+        // V^T[h][i][vt_pos(m)]: one lane per (feature column, group of 16 tokens); inside a
+        // group, tokens 0-3 | 8-11 | 4-7 | 12-15 land at slots 0-15 (two 16-byte stores)
+        for (int idx = tid; idx < BN * (BM / 16); idx += NT) {
           const int c = idx % BN, rb = idx / BN;
           const int col = (int)(n0 % d) + c;
           const int h = col / p.hd, i = col % p.hd;
-          uint16_t v8[8];
+          uint16_t v16[16];
 #pragma unroll
-          for (int e = 0; e < 8; e++) v8[e] = *reinterpret_cast<const uint16_t *>(smem + (rb * 8 + e) * C::CPITCH + c * 2);
-          const int64_t row = m0 + rb * 8;
+          for (int e = 0; e < 16; e++)
+            v16[vt_pos(e)] = *reinterpret_cast<const uint16_t *>(smem + (rb * 16 + e) * C::CPITCH + c * 2);
+          const int64_t row = m0 + rb * 16;
           uint16_t *dst = p.ov + ((int64_t)h * p.hd + i) * p.ldv + row;
-          if (vec && row + 8 <= p.M) {
-            u32x4 v;
+          if (row + 16 <= p.M) {
+            u32x4 v0, v1;
 #pragma unroll
-            for (int e = 0; e < 4; e++) v[e] = (uint32_t)v8[2 * e] | ((uint32_t)v8[2 * e + 1] << 16);
-            *reinterpret_cast<u32x4 *>(dst) = v;
+            for (int e = 0; e < 4; e++) {
+              v0[e] = (uint32_t)v16[2 * e] | ((uint32_t)v16[2 * e + 1] << 16);
+              v1[e] = (uint32_t)v16[8 + 2 * e] | ((uint32_t)v16[8 + 2 * e + 1] << 16);
+            }
+            reinterpret_cast<u32x4 *>(dst)[0] = v0;
+            reinterpret_cast<u32x4 *>(dst)[1] = v1;
           } else {
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-              if (row + e < p.M) dst[e] = v8[e];
+            for (int e = 0; e < 16; e++)
+              if (row + e < p.M) dst[vt_pos(e)] = v16[vt_pos(e)];
           }
         }
       }
@@ -372,9 +388,9 @@ static int pick_bn(int64_t M, int64_t N) {
 template <bool INT8, int OUT, bool GROUPED>
 static hipError_t dispatch_bn(const GemmP &p, int bn, hipStream_t st) {
   if constexpr (GROUPED) {
-    // two accumulator sets (int32 per group, fp32 across groups) per lane: 128 x 128 tiles,
-    // 4 waves of 64 x 64
-    return run_gemm<128, 128, 2, 2, INT8, OUT, GROUPED>(p, st);
+    // two accumulator sets (int32 per group, fp32 across groups) per lane: 256 x 128 tiles,
+    // 8 waves of 64 x 64
+    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED>(p, st);
   } else {
     if (bn == 256) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED>(p, st);
     return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED>(p, st);
@@ -401,7 +417,7 @@ hipError_t launch_linear(const h3dit_linear_args &a, hipStream_t st) {
   p.oq = a.out_q;
   p.ok = a.out_k;
   p.ov = a.out_v;
-  p.ldv = (int)((a.M + 7) / 8 * 8);
+  p.ldv = (int)vt_pitch(a.M);
   int bn = pick_bn(a.M, a.N);
   if (a.out_kind == H3DIT_OUT_QKV) {
     const int64_t d = (int64_t)a.heads * a.head_dim;

@@ -310,7 +310,7 @@ hipError_t launch_rope_tables(const h3dit_layout &L, int hd, int reduced, float 
 // ---------------------------------------------------------------- rotary + head split (unfused form)
 
 // One lane per (token, chunk of 8 features) of t[n][3d].  q and k: pairs (2j, 2j+1) become
-// (a c - b s, a s + b c); v goes to V^T[h][i][tok] with row pitch ldv = n rounded up to 8.
+// (a c - b s, a s + b c); v goes to V^T[h][i][vt_pos(tok)] (row pitch vt_pitch(n)).
 __global__ void k_rope_split(int64_t n, int heads, int hd, const uint16_t *__restrict__ t,
                              const float *__restrict__ cos_t, const float *__restrict__ sin_t,
                              uint16_t *__restrict__ q, uint16_t *__restrict__ k, uint16_t *__restrict__ vt) {
@@ -336,9 +336,9 @@ __global__ void k_rope_split(int64_t n, int heads, int hd, const uint16_t *__res
     uint16_t *dst = part == 0 ? q : k;
     *reinterpret_cast<u32x4 *>(dst + ((int64_t)h * n + tok) * hd + i) = pack8(o);
   } else {
-    const int64_t ldv = (n + 7) / 8 * 8;
+    const int64_t ldv = vt_pitch(n), pos = vt_pos(tok);
 #pragma unroll
-    for (int e = 0; e < 8; e++) vt[((int64_t)h * hd + i + e) * ldv + tok] = f2bf(f[e]);
+    for (int e = 0; e < 8; e++) vt[((int64_t)h * hd + i + e) * ldv + pos] = f2bf(f[e]);
   }
 }
 

@@ -10,7 +10,10 @@
  *   token-major  [n][d]       row n holds the d features of token n
  *   head-major   [H][n][hd]   Q, K and the attention output O
  *   V^T          [H][hd][ldv] values, transposed so the attention kernel reads them along
- *                             tokens, row pitch ldv = n rounded up to a multiple of 8
+ *                             tokens; row pitch ldv = n rounded up to a multiple of 16, and
+ *                             token t at column (t & ~15) | (t & 3) | (t & 4) << 1 | (t & 8) >> 1
+ *                             (bits 2 and 3 swapped inside each group of 16), the order in
+ *                             which one MFMA step of the value product consumes keys
  *                             ([DD] "h3.c 的核心设计": the projection writes the attention
  *                             inputs directly in the layout attention wants)
  */

@@ -107,11 +107,11 @@ def check_stages(w, T, pc, cos, sin, int8, R):
                                                        pc["sqkv"]), "QKV projection (int8)")
     # the fused rotary + head-major epilogue, from the projection value it starts from
     qr, kr, vr = oracle.rope_split(g["t"][R], cs, sn, H, hd)
-    vt_rows = g["vt"][:, :, :N][:, :, R].transpose(1, 2)
+    vt_rows = h3.v_from_vt(g["vt"], N)[:, R]
     for name, got, ref in (("q", g["q"][:, R], qr), ("k", g["k"][:, R], kr), ("v", vt_rows, vr)):
         assert_bitexact(got, ref, f"{name} (rotary + head split epilogue)")
     # attention: sampled queries against all keys
-    v_all = g["vt"][:, :, :N].transpose(1, 2).contiguous()
+    v_all = h3.v_from_vt(g["vt"], N).contiguous()
     o_ref = oracle.attention(g["q"][:, R].contiguous(), g["k"], v_all)
     assert relerr(g["o"][:, R], o_ref) <= BF16_TOL
     assert float((g["o"][:, R].double() - o_ref.double()).abs().mean()) <= 2e-3 * float(o_ref.double().abs().mean()) + 1e-6

@@ -229,7 +229,7 @@ def test_linear_qkv_rope_headmajor(M, H, hd, int8):
     qr, kr, vr = oracle.rope_split(cpu(t), cpu(cos), cpu(sin), H, hd)
     assert_bitexact(cpu(q), qr, "q")
     assert_bitexact(cpu(k), kr, "k")
-    assert_bitexact(cpu(vt)[:, :, :M], vr.transpose(1, 2), "V^T")
+    assert_bitexact(h3.v_from_vt(cpu(vt), M), vr, "V^T")
     # the unfused rotary + head split kernel gives the same bytes
     q2, k2, vt2 = torch.empty_like(q), torch.empty_like(k), torch.zeros_like(vt)
     h3.rope_split(M, H, hd, t, cos, sin, q2, k2, vt2)
@@ -254,8 +254,7 @@ def test_attention(H, N, hd):
     q = bf_randn((H, N, hd), 23, 2.0)
     k = bf_randn((H, N, hd), 24, 2.0)
     v = bf_randn((H, N, hd), 25)
-    vt = torch.zeros((H, hd, h3.ldv(N)), dtype=torch.bfloat16)
-    vt[:, :, :N] = v.transpose(1, 2)
+    vt = h3.vt_from_v(v)
     qg = to_dev(q)
     o = torch.empty_like(qg)
     mx = torch.empty((H, N), dtype=torch.float32, device=DEV)
@@ -276,7 +275,7 @@ def test_attention_garbage_padding_is_ignored():
     H, N, hd = 2, 100, 64
     q, k, v = bf_randn((H, N, hd), 26), bf_randn((H, N, hd), 27), bf_randn((H, N, hd), 28)
     vt = torch.full((H, hd, h3.ldv(N)), float("nan"), dtype=torch.bfloat16)
-    vt[:, :, :N] = v.transpose(1, 2)
+    vt[:, :, h3.vt_positions(N)] = v.transpose(1, 2)
     o = torch.empty((H, N, hd), dtype=torch.bfloat16, device=DEV)
     h3.attention(H, N, hd, to_dev(q), to_dev(k), to_dev(vt), o)
     assert relerr(cpu(o), oracle.attention(q, k, v)) <= BF16_TOL
