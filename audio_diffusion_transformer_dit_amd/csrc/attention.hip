@@ -1,8 +1,8 @@
 // Full non-causal attention of the H3 DiT block on gfx950 MFMA ([RV] README: the first public
 // release uses full attention over the whole joint token sequence).
 //
-// One workgroup = 4 waves = 128 queries of one head; each wave owns 32 queries and walks all
-// keys in blocks of 64 with an online softmax in the exp2 domain.  Scores are computed
+// One workgroup = 4 waves = 128 queries of one head (two workgroups per CU); each wave owns 32
+// queries and walks all keys in blocks of 64 with an online softmax in the exp2 domain.  Scores are computed
 // transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16 with keys as rows), so each lane holds
 // one query column: the row max and row sum are 16 lane-local values plus one exchange with
 // the other half-wave, and the rescale of the output is a per-lane scalar.  O^T = V^T P^T
@@ -16,9 +16,10 @@
 
 namespace h3 {
 
-constexpr int AQ = 128;    // queries per workgroup
-constexpr int AKV = 64;    // keys per block
-constexpr int ATHREADS = 256;
+constexpr int ANW = 4;             // waves per workgroup
+constexpr int AQ = 32 * ANW;       // queries per workgroup
+constexpr int AKV = 64;            // keys per block
+constexpr int ATHREADS = 64 * ANW;
 
 template <int HD>
 struct AttCfg {
@@ -45,8 +46,8 @@ __device__ __forceinline__ void att_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
   {
     const int rl = lane / KCH, slot = lane % KCH;
 #pragma unroll
-    for (int i = 0; i < AKV / (KRPI * 4); i++) {
-      const int rb = i * 4 + wid;
+    for (int i = 0; i < AKV / (KRPI * ANW); i++) {
+      const int rb = i * ANW + wid;
       const int row = rb * KRPI + rl;
       const int chunk = att_slot(slot, row, KCH);
       const uint32_t off = (uint32_t)(((kbase_row + (int64_t)kb * AKV + row) * HD + chunk * 8) * 2);
@@ -57,8 +58,8 @@ __device__ __forceinline__ void att_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
   {
     const int rl = lane >> 3, slot = lane & 7;
 #pragma unroll
-    for (int i = 0; i < HD / 32; i++) {
-      const int rb = i * 4 + wid;
+    for (int i = 0; i < HD / (8 * ANW); i++) {
+      const int rb = i * ANW + wid;
       const int row = rb * 8 + rl;
       const int chunk = att_slot(slot, row, 8);
       const uint32_t off = (uint32_t)((((vbase_row + row) * (int64_t)ldv) + (int64_t)kb * AKV + chunk * 8) * 2);

@@ -369,11 +369,13 @@ void orc_attention(int32_t H, int64_t Nq, int64_t N, int32_t hd, const uint16_t 
 /* ---------------------------------------------------------------- MLP activation + gate */
 
 /* GELU, tanh form (the pages leave the activation unnamed; a reading):
- * 0.5 u (1 + tanh( sqrt(2/pi) (u + 0.044715 u^3) )). */
+ * gelu(u) = 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3), evaluated in double and
+ * rounded once to fp32.  0.5 (1 + tanh z) = 1 / (1 + e^(-2z)) exactly; that form is used
+ * because 1 + tanh(z) cancels for z << 0 (in fp32 it loses every bit below u ~ -3). */
 float orc_gelu_tanh_f32(float u) {
-  float u3 = u * u * u;
-  float z = 0.7978845608f * (u + 0.044715f * u3);
-  return 0.5f * u * (1.0f + tanhf(z));
+  double x = u;
+  double z = 0.7978845608 * (x + 0.044715 * x * x * x);
+  return (float)(x / (1.0 + exp(-2.0 * z)));
 }
 
 void orc_gelu_rows(int64_t n, const uint16_t *u, uint16_t *gl) {

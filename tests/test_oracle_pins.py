@@ -84,20 +84,36 @@ def test_gelu_tanh_closed_forms_and_library():
     # gelu(x) - gelu(-x) = x
     assert float((ours - neg - xs).abs().max()) < 1e-5
     # large |x|: gelu -> x for x >> 0, -> 0 for x << 0
-    assert oracle.gelu_tanh(10.0) == 10.0 and oracle.gelu_tanh(-10.0) == 0.0
+    assert oracle.gelu_tanh(10.0) == 10.0 and abs(oracle.gelu_tanh(-10.0)) < 1e-30
+    # accurate in the negative tail too, where 1 + tanh(z) cancels: against the float64
+    # library down to u = -4 (its 1 + tanh(z) keeps > 35 bits there) ...
+    tail = torch.linspace(-4, -2, 401, dtype=torch.float32).to(torch.float64)
+    ot = torch.tensor([oracle.gelu_tanh(float(v)) for v in tail], dtype=torch.float64)
+    rt = F.gelu(tail, approximate="tanh")
+    assert torch.all((ot - rt).abs() <= rt.abs() * 2.0 ** -22)
+    # ... and below it against the series gelu(u) = u (e^(2z) - e^(4z) + O(e^(6z))), e^(4z) < 2^-30
+    deep = torch.linspace(-12, -4, 801, dtype=torch.float32).to(torch.float64)
+    od = torch.tensor([oracle.gelu_tanh(float(v)) for v in deep], dtype=torch.float64)
+    z = math.sqrt(2 / math.pi) * (deep + 0.044715 * deep ** 3)
+    ra = deep * (torch.exp(2 * z) - torch.exp(4 * z))
+    keep = ra.abs() > 1e-37  # normal fp32 range
+    assert torch.all((od - ra).abs()[keep] <= ra.abs()[keep] * 2.0 ** -22)
 
 
 def test_gelu_rows_rounding():
-    u = bf(torch.randn(4096, dtype=torch.float64) * 3)
+    g = torch.Generator().manual_seed(11)
+    u = bf(torch.randn(4096, generator=g, dtype=torch.float64) * 3)
+    u = torch.cat([u, bf(torch.tensor([-9.5, -10.0, -11.0, -12.0], dtype=torch.float64))])
     got = oracle.gelu_rows(u)
-    ref64 = F.gelu(u.to(torch.float64), approximate="tanh")
-    ref = bf(ref64)
-    # away from the negative tail: within one bf16 step of the float64 value
-    ok = u.to(torch.float64) > -3
-    assert int(ulp_diff(got[ok], ref[ok]).max()) <= 1
-    # in the tail 1 + tanh(z) cancels in fp32: absolute error stays below |u| * 2^-22
-    err = (got.to(torch.float64) - ref64).abs()
-    assert torch.all(err <= u.to(torch.float64).abs() * 2.0 ** -22 + ref64.abs() * 2.0 ** -8)
+    u64 = u.to(torch.float64)
+    ref64 = F.gelu(u64, approximate="tanh")
+    z = math.sqrt(2 / math.pi) * (u64 + 0.044715 * u64 ** 3)
+    series = u64 * (torch.exp(2 * z) - torch.exp(4 * z))
+    ref64 = torch.where(u64 < -4, series, ref64)  # the library's 1 + tanh(z) cancels below -4
+    # fp64 evaluation rounded to fp32 then bf16: at most one bf16 step from the float64 value
+    tiny = ref64.abs() < 1e-37
+    assert int(ulp_diff(got[~tiny], bf(ref64)[~tiny]).max()) <= 1
+    assert float(got[tiny].to(torch.float64).abs().max()) < 1e-37
 
 
 # ----------------------------------------------------------------------------- AdaLN
