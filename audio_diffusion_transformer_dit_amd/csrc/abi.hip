@@ -409,7 +409,8 @@ int h3dit_linear(const h3dit_linear_args *a, void *stream) {
   if (!i8 && a->precision != H3DIT_BF16) return H3DIT_EINVAL;
   const int esz = i8 ? 1 : 2;
   if ((a->M + 255) * a->K * esz >= ((int64_t)1 << 32) || a->N * a->K * esz >= ((int64_t)1 << 32)) return H3DIT_EINVAL;
-  if (a->a_headmajor_hd && (i8 || (a->a_headmajor_hd != 64 && a->a_headmajor_hd != 128) || a->K % a->a_headmajor_hd))
+  if (a->a_headmajor_hd && (i8 || (a->a_headmajor_hd != 64 && a->a_headmajor_hd != 128) || a->K % a->a_headmajor_hd ||
+                            (a->out_kind != H3DIT_OUT_BF16 && a->out_kind != H3DIT_OUT_F32)))
     return H3DIT_EINVAL;
   if (i8) {
     if (!a->a_scale || !a->w_scale) return H3DIT_EINVAL;

@@ -74,7 +74,8 @@ __device__ __forceinline__ u32x4 lds_frag(const uint8_t *base, int row, int chun
 }
 
 // out_kind: H3DIT_OUT_*.  GROUPED: int8 FC2 with per-(row, group) activation scales.
-template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED>
+// HM: A is the head-major attention output [K/hd][M][hd] (bf16 only).
+template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   using C = GemmCfg<BM, BN, WGM, WGN>;
   constexpr int FM = C::FM, FN = C::FN, NW = C::NW, NT = C::NT, LA = C::LA, LW = C::LW;
@@ -98,7 +99,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   // offset go into the scalar offset of the buffer load.
   static_assert(NW % 2 == 0, "blocks of one lane share the swizzle when the block stride is a multiple of 16 rows");
   const int rl = lane >> 3, cl = lane & 7;
-  const bool hm = !INT8 && p.hm_hd > 0;
+  static_assert(!(HM && INT8), "head-major input is bf16");
+  constexpr bool hm = HM;
   const int r0 = wid * 8 + rl;                         // row of block 0
   const int sw = (cl ^ ((r0 >> 1) & 7)) << 4;          // swizzled 16-byte slot (same for every block)
   const uint32_t a_voff = hm ? (uint32_t)((m0 + r0) * p.hm_hd * 2 + cl * 16) : (uint32_t)((m0 + r0) * p.K * esz + cl * 16);
@@ -369,12 +371,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED>
+template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM>
 static hipError_t run_gemm(GemmP p, hipStream_t st) {
   p.tiles_m = (int)((p.M + BM - 1) / BM);
   p.tiles_n = (int)(p.N / BN);
   const unsigned nwg = (unsigned)p.tiles_m * p.tiles_n;
-  k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED><<<nwg, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+  k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM><<<nwg, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -385,15 +387,15 @@ static int pick_bn(int64_t M, int64_t N) {
   return tiles256 >= 512 ? 256 : 128;
 }
 
-template <bool INT8, int OUT, bool GROUPED>
+template <bool INT8, int OUT, bool GROUPED, bool HM = false>
 static hipError_t dispatch_bn(const GemmP &p, int bn, hipStream_t st) {
   if constexpr (GROUPED) {
     // two accumulator sets (int32 per group, fp32 across groups) per lane: 256 x 128 tiles,
     // 8 waves of 64 x 64
-    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED>(p, st);
+    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, false>(p, st);
   } else {
-    if (bn == 256) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED>(p, st);
-    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED>(p, st);
+    if (bn == 256) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, st);
+    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, HM>(p, st);
   }
 }
 
@@ -425,6 +427,12 @@ hipError_t launch_linear(const h3dit_linear_args &a, hipStream_t st) {
   }
   const bool i8 = a.precision == H3DIT_INT8;
   if (i8 && a.a_group > 0) return dispatch_bn<true, H3DIT_OUT_BF16, true>(p, bn, st);
+  if (a.a_headmajor_hd > 0) {
+    if (i8) return hipErrorInvalidValue;
+    if (a.out_kind == H3DIT_OUT_BF16) return dispatch_bn<false, H3DIT_OUT_BF16, false, true>(p, bn, st);
+    if (a.out_kind == H3DIT_OUT_F32) return dispatch_bn<false, H3DIT_OUT_F32, false, true>(p, bn, st);
+    return hipErrorInvalidValue;
+  }
   switch (a.out_kind) {
     case H3DIT_OUT_BF16:
       return i8 ? dispatch_bn<true, H3DIT_OUT_BF16, false>(p, bn, st) : dispatch_bn<false, H3DIT_OUT_BF16, false>(p, bn, st);

@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--only-kernels", action="store_true", help="per-kernel timing only (profiling runs)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="with --only-kernels: also run one plain device copy of this many bytes, the reference "
+                         "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
     return ap.parse_args()
 
 
@@ -188,11 +191,12 @@ def traffic_for(kernel):
 
 
 def cpu_baseline(w):
-    """The oracle on a bounded sample: one block at full width over 512 tokens."""
+    """The oracle on a bounded sample: one block at full width over 2688 tokens (the workload's
+    22 x 32 spatial grid with 3 frames, its 512 text and 64 audio tokens)."""
     import oracle
     import synth
-    sample = w.replace(video_t=2, video_h=8, video_w=28, n_text=48, n_audio=16, blocks=1)
-    assert sample.n_tokens == 512
+    sample = w.replace(video_t=3, video_h=22, video_w=32, n_text=512, n_audio=64, blocks=1)
+    assert sample.n_tokens == 2688
     seed = synth.seed_for(3)
     x = synth.make_x(sample, seed)
     p = synth.make_block(sample, seed, 0)
@@ -203,7 +207,7 @@ def cpu_baseline(w):
     fl = block_flops(sample.n_tokens, sample.hidden, sample.mlp)
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"one bf16 block at full width (d={sample.hidden}, H={sample.heads}x{sample.head_dim}, "
-                      f"f={sample.mlp}) over {sample.n_tokens} tokens (2x8x28 video + 48 text + 16 audio): "
+                      f"f={sample.mlp}) over {sample.n_tokens} tokens (3x22x32 video + 512 text + 64 audio): "
                       f"{fl / 1e9:.1f} GFLOP in {dt:.2f} s; extrapolated 50-block step at 4096 tokens "
                       f"{50 * block_flops(4096, 5120, 20480) / (fl / dt) :.0f} s"}
 
@@ -235,6 +239,13 @@ def main():
     if args.only_kernels:
         p = make_blocks(w, 1, seed, dev, int8_main)[0]
         out["kernels"] = kernel_breakdown(w, p, x, args.kernel_iters, int8_main)
+        if args.copy_bytes:
+            src = torch.ones(args.copy_bytes // 2, dtype=torch.bfloat16, device=dev)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            out["copy_bytes"] = args.copy_bytes
         print(json.dumps(out))
         return
 

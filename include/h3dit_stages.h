@@ -54,7 +54,8 @@ int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, const uint16_
                         int32_t headmajor_hd, int8_t *q, float *s, void *stream);
 
 /* Projection out = A W^T on MFMA ([DD] "h3.c 的核心设计", "int8 量化").
- *   precision H3DIT_BF16: A bf16 [M][K] (or head-major with a_headmajor_hd > 0), W bf16 [N][K],
+ *   precision H3DIT_BF16: A bf16 [M][K] (or, with a_headmajor_hd = 64 or 128, the head-major
+ *     attention output [K/hd][M][hd]; out_kind BF16 or F32 only), W bf16 [N][K],
  *     fp32 accumulation; acc value = the fp32 sum.
  *   precision H3DIT_INT8: A int8 [M][K] with a_scale fp32 [M] (a_group == 0), W int8 [N][K]
  *     with w_scale fp32 [N]; int32 accumulation; value = ((float)acc * a_scale) * w_scale.

@@ -158,3 +158,8 @@ def test_call_argument_errors_before_launch():
     assert lib.h3dit_linear(C.byref(args), None) == h3.EINVAL                 # N % 128
     args = h3.LinearArgs(M=10, N=128, K=128, precision=h3.BF16, a=x, w=x, out=x, out_kind=h3.OUT_I32)
     assert lib.h3dit_linear(C.byref(args), None) == h3.EINVAL                 # int32 output on the bf16 path
+    args = h3.LinearArgs(M=10, N=128, K=128, precision=h3.BF16, a=x, a_headmajor_hd=64, w=x, out=x,
+                         out_kind=h3.OUT_GELU)
+    assert lib.h3dit_linear(C.byref(args), None) == h3.EINVAL                 # head-major A feeds BF16/F32 only
+    args.a_headmajor_hd, args.out_kind = 96, h3.OUT_BF16
+    assert lib.h3dit_linear(C.byref(args), None) == h3.EINVAL                 # head dim 96
