@@ -30,7 +30,7 @@ OUT_BF16, OUT_F32, OUT_I32, OUT_GELU, OUT_QKV = 0, 1, 2, 3, 4
 
 EXPORTS = ("h3dit_quantize_weights", "h3dit_block_fwd", "h3dit_stack_fwd", "h3dit_rope_tables",
            "h3dit_row_gate_adaln", "h3dit_quantize_rows", "h3dit_linear", "h3dit_rope_split", "h3dit_gelu",
-           "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore")
+           "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore", "h3dit_linear_workspace")
 
 
 class H3Error(RuntimeError):
@@ -66,7 +66,8 @@ class LinearArgs(C.Structure):
                 ("a", C.c_void_p), ("a_headmajor_hd", C.c_int32), ("a_scale", C.c_void_p), ("a_group", C.c_int32),
                 ("w", C.c_void_p), ("w_scale", C.c_void_p), ("out_kind", C.c_int32), ("out", C.c_void_p),
                 ("cos_t", C.c_void_p), ("sin_t", C.c_void_p), ("heads", C.c_int32), ("head_dim", C.c_int32),
-                ("out_q", C.c_void_p), ("out_k", C.c_void_p), ("out_v", C.c_void_p)]
+                ("out_q", C.c_void_p), ("out_k", C.c_void_p), ("out_v", C.c_void_p), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_uint64)]
 
 
 _P = C.c_void_p
@@ -77,6 +78,7 @@ _lib.h3dit_rope_tables.argtypes = [_P, C.c_int32, C.c_int32, _P, _P, _P]
 _lib.h3dit_row_gate_adaln.argtypes = [C.c_int64, C.c_int32, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_quantize_rows.argtypes = [C.c_int64, C.c_int64, C.c_int64, _P, C.c_int32, _P, _P, _P]
 _lib.h3dit_linear.argtypes = [_P, _P]
+_lib.h3dit_linear_workspace.argtypes = [_P, _P]
 _lib.h3dit_rope_split.argtypes = [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_gelu.argtypes = [C.c_int64, _P, _P, _P]
 _lib.h3dit_attention.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
@@ -263,11 +265,33 @@ def quantize_rows(v, rows, cols, group, headmajor_hd=0, stream=None):
 
 
 def linear(M, N, K, a, w, out_kind=OUT_BF16, out=None, precision=BF16, a_headmajor_hd=0, a_scale=None, a_group=0,
-           w_scale=None, cos=None, sin=None, heads=0, head_dim=0, out_q=None, out_k=None, out_v=None, stream=None):
+           w_scale=None, cos=None, sin=None, heads=0, head_dim=0, out_q=None, out_k=None, out_v=None, stream=None,
+           workspace=None):
+    """out = a w^T through h3dit_linear.  The split-K workspace the call needs (if any) is taken
+    from `workspace` (a uint8 device tensor) when it is large enough, else allocated."""
     args = LinearArgs(M, N, K, precision, _ptr(a), a_headmajor_hd, _ptr(a_scale), a_group, _ptr(w), _ptr(w_scale),
                       out_kind, _ptr(out), _ptr(cos), _ptr(sin), heads, head_dim, _ptr(out_q), _ptr(out_k),
                       _ptr(out_v))
+    need = C.c_uint64(0)
+    _check("h3dit_linear_workspace", _lib.h3dit_linear_workspace(C.byref(args), C.byref(need)))
+    if need.value:
+        if workspace is None or workspace.numel() < need.value:
+            import torch
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=a.device)
+        args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel()
     _check("h3dit_linear", _lib.h3dit_linear(C.byref(args), _stream(stream)))
+
+
+def linear_workspace(M, N, K, precision=BF16, a_group=0, out_kind=OUT_BF16, heads=0, head_dim=0):
+    """Split-K workspace bytes h3dit_linear needs for this shape (0 when it splits nothing).
+    Validation needs non-NULL operand pointers; the query only reads the shape fields."""
+    dummy = 1 << 20
+    args = LinearArgs(M=M, N=N, K=K, precision=precision, a=dummy, a_scale=dummy, a_group=a_group, w=dummy,
+                      w_scale=dummy, out_kind=out_kind, out=dummy, cos_t=dummy, sin_t=dummy, heads=heads,
+                      head_dim=head_dim, out_q=dummy, out_k=dummy, out_v=dummy)
+    need = C.c_uint64(0)
+    _check("h3dit_linear_workspace", _lib.h3dit_linear_workspace(C.byref(args), C.byref(need)))
+    return need.value
 
 
 def rope_split(n, heads, head_dim, t, cos, sin, q, k, vt, stream=None):

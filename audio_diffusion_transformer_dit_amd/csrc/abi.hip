@@ -88,7 +88,29 @@ struct Plan {
   size_t t = 0, hb = 0;                               // unfused-only regions
   size_t sa = 0, sg = 0;                              // per-token / per-group scales
   size_t red = 0, r_in = 0;                           // token reduction
+  size_t sk = 0, sk_bytes = 0;                        // split-K partial tiles of the projections
 };
+
+// Largest split-K workspace of the block's four projections at n tokens.
+size_t block_splitk_bytes(const h3dit_dims &D, int precision, int64_t n) {
+  const bool i8 = precision == H3DIT_INT8;
+  h3dit_linear_args la{};
+  la.M = n;
+  la.precision = precision;
+  size_t m = 0;
+  auto take = [&](int64_t N, int64_t K, int out_kind, int group) {
+    la.N = N; la.K = K; la.out_kind = out_kind; la.a_group = group;
+    la.heads = D.heads; la.head_dim = D.head_dim;
+    const size_t b = linear_workspace(la);
+    if (b > m) m = b;
+  };
+  take(3 * (int64_t)D.hidden, D.hidden, H3DIT_OUT_QKV, 0);
+  take(3 * (int64_t)D.hidden, D.hidden, H3DIT_OUT_BF16, 0);
+  take(D.hidden, D.hidden, H3DIT_OUT_BF16, 0);
+  take(D.mlp, D.hidden, H3DIT_OUT_GELU, 0);
+  take(D.hidden, D.mlp, H3DIT_OUT_BF16, i8 ? D.fc2_group : 0);
+  return m;
+}
 
 Plan make_plan(const h3dit_dims &D, const h3dit_layout &L, int precision, uint32_t flags, bool reduction) {
   const size_t N = (size_t)D.n_tokens, d = (size_t)D.hidden, f = (size_t)D.mlp, hd = (size_t)D.head_dim;
@@ -111,6 +133,12 @@ Plan make_plan(const h3dit_dims &D, const h3dit_layout &L, int precision, uint32
     p.red = take(Nr * d * 2);
     p.r_in = take(Nr * d * 2);
   }
+  p.sk_bytes = block_splitk_bytes(D, precision, (int64_t)N);
+  if (reduction) {
+    const size_t r = block_splitk_bytes(D, precision, layout_tokens(L, true));
+    if (r > p.sk_bytes) p.sk_bytes = r;
+  }
+  if (p.sk_bytes) p.sk = take(p.sk_bytes);
   p.sa = take(N * 4);
   if (i8) p.sg = take(N * (f / (size_t)D.fc2_group) * 4);
   if (flags & H3DIT_NOFUSE_ROPE) p.t = take(3 * Nd2);
@@ -189,6 +217,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
   la.w = b.w_qkv;
   la.w_scale = b.s_qkv;
   la.cos_t = cos_t; la.sin_t = sin_t; la.heads = H; la.head_dim = hd;
+  la.workspace = c.at<void>(P.sk); la.workspace_bytes = P.sk_bytes;
   if (!(F & H3DIT_NOFUSE_ROPE)) {
     la.out_kind = H3DIT_OUT_QKV;
     la.out_q = c.at<uint16_t>(P.q); la.out_k = c.at<uint16_t>(P.k); la.out_v = c.at<uint16_t>(P.vt);
@@ -209,6 +238,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
   la = h3dit_linear_args{};
   la.M = n; la.N = d; la.K = d; la.precision = b.precision; la.w = b.w_o; la.w_scale = b.s_o;
   la.out_kind = H3DIT_OUT_BF16; la.out = c.at<void>(P.y1);
+  la.workspace = c.at<void>(P.sk); la.workspace_bytes = P.sk_bytes;
   if (!i8) {
     la.a = c.at<void>(P.o);
     la.a_headmajor_hd = hd;
@@ -233,6 +263,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
   la.a = c.at<void>(P.h2); la.a_scale = i8 ? c.at<float>(P.sa) : nullptr;
   la.out = c.at<void>(P.gl);
   la.out_kind = (F & H3DIT_NOFUSE_GELU) ? H3DIT_OUT_BF16 : H3DIT_OUT_GELU;
+  la.workspace = c.at<void>(P.sk); la.workspace_bytes = P.sk_bytes;
   TRY(launch_linear(la, c.st));
   if (F & H3DIT_NOFUSE_GELU) TRY(launch_gelu((int64_t)n * f, c.at<uint16_t>(P.gl), c.at<uint16_t>(P.gl), c.st));
 
@@ -240,6 +271,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
   la = h3dit_linear_args{};
   la.M = n; la.N = d; la.K = f; la.precision = b.precision; la.w = b.w_fc2; la.w_scale = b.s_fc2;
   la.out_kind = H3DIT_OUT_BF16; la.out = c.at<void>(P.y2);
+  la.workspace = c.at<void>(P.sk); la.workspace_bytes = P.sk_bytes;
   if (!i8) {
     la.a = c.at<void>(P.gl);
   } else {
@@ -402,7 +434,7 @@ int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, const uint16_
   return H3DIT_OK;
 }
 
-int h3dit_linear(const h3dit_linear_args *a, void *stream) {
+static int check_linear(const h3dit_linear_args *a) {
   if (!a || a->M < 0 || a->N < 128 || a->N % 128 || a->K < 128 || a->K % 128) return H3DIT_EINVAL;
   if (!a->a || !a->w || !aligned(a->a, 16) || !aligned(a->w, 16)) return H3DIT_EINVAL;
   const bool i8 = a->precision == H3DIT_INT8;
@@ -429,8 +461,24 @@ int h3dit_linear(const h3dit_linear_args *a, void *stream) {
   } else if (a->out_kind < 0 || a->out_kind > H3DIT_OUT_QKV || !a->out || !aligned(a->out, 16)) {
     return H3DIT_EINVAL;
   }
-  int rc = check_device();
+  if (a->workspace && !aligned(a->workspace, ALIGN)) return H3DIT_EINVAL;
+  return H3DIT_OK;
+}
+
+int h3dit_linear_workspace(const h3dit_linear_args *a, uint64_t *bytes) {
+  if (!bytes) return H3DIT_EINVAL;
+  int rc = check_linear(a);
   if (rc) return rc;
+  *bytes = linear_workspace(*a);
+  return H3DIT_OK;
+}
+
+int h3dit_linear(const h3dit_linear_args *a, void *stream) {
+  int rc = check_linear(a);
+  if (rc) return rc;
+  const size_t need = linear_workspace(*a);
+  if (need && (!a->workspace || a->workspace_bytes < need)) return H3DIT_EWORKSPACE;
+  if ((rc = check_device())) return rc;
   TRY(launch_linear(*a, (hipStream_t)stream));
   return H3DIT_OK;
 }

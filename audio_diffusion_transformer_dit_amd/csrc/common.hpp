@@ -119,6 +119,17 @@ hipError_t launch_token_pair(const h3dit_layout &L, int d, const uint16_t *x, ui
                              hipStream_t st);
 hipError_t launch_token_restore(const h3dit_layout &L, int d, uint16_t *x, const uint16_t *y,
                                 const uint16_t *r_in, hipStream_t st);
+// Work plan of a projection: tile width, whole tiles, and the split-K of the last round.
+struct LinearPlan {
+  int bn;           // tile width (rows: 256)
+  int n_dp;         // tiles computed whole
+  int split;        // K segments per split tile
+  int kt_seg;       // 128-byte K slices per segment
+  int n_split;      // split tiles
+  size_t part_bytes;  // workspace for their partial tiles
+};
+LinearPlan plan_linear(const h3dit_linear_args &a);
+size_t linear_workspace(const h3dit_linear_args &a);
 hipError_t launch_linear(const h3dit_linear_args &a, hipStream_t st);
 hipError_t launch_attention(int heads, int64_t n, int hd, const uint16_t *q, const uint16_t *k,
                             const uint16_t *vt, uint16_t *o, float *row_max, float *row_sum, hipStream_t st);

@@ -38,6 +38,12 @@ struct GemmP {
   uint16_t *oq, *ok, *ov;
   int ldv;
   int tiles_m, tiles_n;
+  // split-K of the last, partial round: tiles [n_dp, tiles_m*tiles_n) are computed as `split`
+  // K segments of kt_seg slices each, whose fp32 / int32 partial tiles go to `part`; a second
+  // launch (fixup != 0, one workgroup per split tile) sums them in segment order and runs
+  // the epilogue
+  int n_dp, split, kt_seg, fixup;
+  uint8_t *part;
 };
 
 template <int BM, int BN, int WGM, int WGN>
@@ -55,10 +61,14 @@ struct GemmCfg {
   static_assert(LA >= 1 && LW >= 1 && FM >= 1 && FN >= 1, "tile shape");
 };
 
-__device__ __forceinline__ void tile_coords(int &tm, int &tn, int tiles_m, int tiles_n) {
-  const int nwg = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if ((nwg & 7) == 0) b = (b & 7) * (nwg >> 3) + (b >> 3);
+// Workgroups are dealt round-robin to the 8 XCDs: renumber a range of n launch indices so that
+// each XCD gets a contiguous run of work items.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  return (n & 7) == 0 ? (b & 7) * (n >> 3) + (b >> 3) : b;
+}
+
+// tile index -> (tile row, tile column), 8 tile rows at a time
+__device__ __forceinline__ void tile_coords(int b, int &tm, int &tn, int tiles_m, int tiles_n) {
   constexpr int GROUP = 8;
   const int per_group = GROUP * tiles_n;
   const int g = b / per_group;
@@ -81,15 +91,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   constexpr int FM = C::FM, FN = C::FN, NW = C::NW, NT = C::NT, LA = C::LA, LW = C::LW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
 
+  // work item: a whole tile, one K segment of a split tile, or (fixup) the sum of a split tile
+  int tile, seg = -1;
+  const int KT = (int)(p.K * (INT8 ? 1 : 2) / GKB);
+  int kt0 = 0, kt1 = KT;
+  if (p.fixup) {
+    tile = p.n_dp + (int)blockIdx.x;
+  } else if ((int)blockIdx.x < p.n_dp) {
+    tile = xcd_remap((int)blockIdx.x, p.n_dp);
+  } else {
+    const int n_units = (int)gridDim.x - p.n_dp;
+    const int u = xcd_remap((int)blockIdx.x - p.n_dp, n_units);
+    tile = p.n_dp + u / p.split;
+    seg = u % p.split;
+    kt0 = seg * p.kt_seg;
+    kt1 = kt0 + p.kt_seg;
+  }
   int tm, tn;
-  tile_coords(tm, tn, p.tiles_m, p.tiles_n);
+  tile_coords(tile, tm, tn, p.tiles_m, p.tiles_n);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
   constexpr int esz = INT8 ? 1 : 2;
   const uint32_t a_bytes = (uint32_t)(p.M * p.K * esz), w_bytes = (uint32_t)(p.N * p.K * esz);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, a_bytes), rw = make_rsrc(p.w, w_bytes);
-  const int KT = (int)(p.K * esz / GKB);
 
   // Per-lane load offsets.  A slice of the tile is (BM + BN) rows x 128 B; lanes take it in
   // 1 KiB blocks of 8 rows (8 consecutive lanes = one row's 8 chunks), so every global load
@@ -166,12 +191,38 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
     for (int j = 0; j < FN; j++) fb[j] = lds_frag(sb, brow0 + 32 * j, 2 * ks + hsel);
   };
 
-  // prologue: slice 0 into LDS stage 0, slice 1 in registers
+  // partial tile of (split tile, segment): each lane's 16 accumulators of block (i, j) are 64
+  // contiguous bytes; a wave's block is 4 KiB
+  auto part_ptr = [&](int sg, int i, int j) {
+    const int64_t slot = (int64_t)(tile - p.n_dp) * p.split + sg;
+    return reinterpret_cast<i32x4 *>(p.part + slot * (BM * BN * 4) + ((wid * FM + i) * FN + j) * 4096 + lane * 64);
+  };
+  if (!GROUPED && p.fixup) {
+    // sum of the segments' partial tiles, in segment order.  (Vectors are reinterpreted
+    // whole: clang's __builtin_bit_cast of a single ext_vector element reads element 0.)
+    for (int sg = 0; sg < p.split; sg++)
 #pragma unroll
-  for (int li = 0; li < NL; li++) load_one(stage_reg[0], 0, li);
+      for (int i = 0; i < FM; i++)
 #pragma unroll
-  for (int li = 0; li < NL; li++) load_one(stage_reg[1], KT > 1 ? 1 : 0, li);
-  store_slice(stage_reg[0], 0);
+        for (int j = 0; j < FN; j++) {
+          const i32x4 *src = part_ptr(sg, i, j);
+          i32x16 bits;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const i32x4 v = src[q];
+#pragma unroll
+            for (int e = 0; e < 4; e++) bits[4 * q + e] = v[e];
+          }
+          const AccT val = __builtin_bit_cast(AccT, bits);
+          acc[i][j] = sg == 0 ? val : acc[i][j] + val;
+        }
+  } else {
+  // prologue: slice kt0 into its LDS stage, slice kt0+1 in registers
+#pragma unroll
+  for (int li = 0; li < NL; li++) load_one(stage_reg[0], kt0, li);
+#pragma unroll
+  for (int li = 0; li < NL; li++) load_one(stage_reg[1], kt0 + 1 < kt1 ? kt0 + 1 : kt0, li);
+  store_slice(stage_reg[0], kt0);
   __syncthreads();
 
   // Iteration kt: registers of slice kt+1 -> LDS stage (kt+1)&1 (last read in iteration kt-1),
@@ -179,8 +230,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   // repeat the last slice (in range, never stored).  sched_barrier fixes the issue order.
   constexpr int NMMA = 4 * FM * FN;                 // MFMAs per slice; load li follows MFMA li*NMMA/NL
   auto iteration = [&](int kt, const u32x4 *cur, u32x4 *nxt) {
-    if (kt + 1 < KT) store_slice(cur, kt + 1);
-    const int ktl = kt + 2 < KT ? kt + 2 : KT - 1;
+    if (kt + 1 < kt1) store_slice(cur, kt + 1);
+    const int ktl = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
     const uint8_t *sa = smem + (kt & 1) * C::STAGE;
     u32x4 fa[2][FM], fb[2][FN];
     read_step(sa, 0, fa[0], fb[0]);
@@ -236,11 +287,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
     __syncthreads();
   };
   // two iterations per trip so that each register set is addressed statically
-  for (int kt = 0; kt < KT; kt += 2) {
+  for (int kt = kt0; kt < kt1; kt += 2) {
     iteration(kt, stage_reg[1], stage_reg[0]);
-    if (kt + 1 < KT) iteration(kt + 1, stage_reg[0], stage_reg[1]);
+    if (kt + 1 < kt1) iteration(kt + 1, stage_reg[0], stage_reg[1]);
   }
   wait_vmem();   // the register loads past the end
+  if (!GROUPED && seg >= 0) {
+    // one K segment of a split tile: store the raw partial, the fixup launch finishes it
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN; j++) {
+        i32x4 *dst = part_ptr(seg, i, j);
+        const i32x16 bits = __builtin_bit_cast(i32x16, acc[i][j]);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          i32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; e++) v[e] = bits[4 * q + e];
+          dst[q] = v;
+        }
+      }
+    return;
+  }
+  }
 
   // ---------------------------------------------------------------- epilogue
   // value of accumulator (i, j, r): row = m0 + wm*BM/WGM + 32 i + 8 (r/4) + 4 hsel + r%4,
@@ -372,35 +442,95 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
 }
 
 template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM>
-static hipError_t run_gemm(GemmP p, hipStream_t st) {
+static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
   p.tiles_m = (int)((p.M + BM - 1) / BM);
   p.tiles_n = (int)(p.N / BN);
-  const unsigned nwg = (unsigned)p.tiles_m * p.tiles_n;
-  k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM><<<nwg, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+  p.n_dp = pl.n_dp;
+  p.split = pl.split;
+  p.kt_seg = pl.kt_seg;
+  p.fixup = 0;
+  const unsigned grid = (unsigned)(pl.n_dp + pl.n_split * pl.split);
+  k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM><<<grid, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+  if (pl.n_split > 0) {
+    p.fixup = 1;
+    k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM><<<(unsigned)pl.n_split, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 
-// Tile width: 256 when that still gives every CU work for about two rounds, else 128.
-static int pick_bn(int64_t M, int64_t N) {
-  if (N % 256 != 0) return 128;
-  const int64_t tiles256 = ((M + 255) / 256) * (N / 256);
-  return tiles256 >= 512 ? 256 : 128;
+// Work plan of one projection on a chip of kCUs compute units holding one workgroup each.
+// Candidates, costed in units of one 256 x 256 tile over the whole K (about K * 28 ps per
+// byte of K row on gfx950):
+//   256 x 256 tiles: rounds = ceil(tiles / kCUs);
+//   256 x 128 tiles: rounds of half tiles, each ~0.52 of a whole one;
+//   256 x 256 with the last partial round cut into `split` K segments: full rounds +
+//     ceil(segments / kCUs) / split, plus the partial tiles (measured on MI355X: ~50 us for
+//     64 tiles x 4 segments, modelled as 16 us per round of segments + 10 us + 6 us per
+//     segment read back by the fixup launch).
+// The grouped int8 FC2 keeps 256 x 128 tiles (its second accumulator set does not fit 256 wide).
+constexpr int kCUs = 256;
+
+LinearPlan plan_linear(const h3dit_linear_args &a) {
+  LinearPlan pl{};
+  const bool i8 = a.precision == H3DIT_INT8;
+  const bool grouped = i8 && a.a_group > 0;
+  const int64_t d = (int64_t)a.heads * a.head_dim;
+  const int KT = (int)(a.K * (i8 ? 1 : 2) / 128);
+  bool wide = a.N % 256 == 0 && !grouped;
+  if (a.out_kind == H3DIT_OUT_QKV && d % 256) wide = false;
+  const int64_t tm = (a.M + 255) / 256;
+  pl.split = 1;
+  pl.kt_seg = KT;
+  pl.n_split = 0;
+  pl.part_bytes = 0;
+  pl.bn = 128;
+  pl.n_dp = (int)(tm * (a.N / 128));
+  if (!wide) return pl;
+  const int64_t tiles = tm * (a.N / 256), full = tiles / kCUs, rem = tiles % kCUs;
+  const double t_tile_us = (double)KT * 128 * 0.0277 / 2;   // one 256 x 256 tile over the whole K
+  const double c256 = (double)(full + (rem ? 1 : 0));
+  const double c128 = (double)((2 * tiles + kCUs - 1) / kCUs) * 0.52;
+  double best = c256;
+  int best_s = 1;
+  for (int sp = 2; sp <= 8 && rem; sp++) {
+    if (KT % sp || KT / sp < 2) continue;
+    const int64_t seg_rounds = (rem * sp + kCUs - 1) / kCUs;
+    const double cost = (double)full + (double)seg_rounds / sp + (16.0 * seg_rounds + 10.0 + 6.0 * sp) / t_tile_us;
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_s = sp;
+    }
+  }
+  if (c128 < best - 1e-9) return pl;
+  pl.bn = 256;
+  pl.n_dp = (int)tiles;
+  if (best_s == 1) return pl;
+  pl.split = best_s;
+  pl.kt_seg = KT / best_s;
+  pl.n_split = (int)rem;
+  pl.n_dp = (int)(tiles - rem);
+  pl.part_bytes = (size_t)rem * best_s * 256 * 256 * 4;
+  return pl;
 }
 
 template <bool INT8, int OUT, bool GROUPED, bool HM = false>
-static hipError_t dispatch_bn(const GemmP &p, int bn, hipStream_t st) {
+static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st) {
   if constexpr (GROUPED) {
     // two accumulator sets (int32 per group, fp32 across groups) per lane: 256 x 128 tiles,
     // 8 waves of 64 x 64
-    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, false>(p, st);
+    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, false>(p, pl, st);
   } else {
-    if (bn == 256) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, st);
-    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, HM>(p, st);
+    if (pl.bn == 256) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, pl, st);
+    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, HM>(p, pl, st);
   }
 }
 
+size_t linear_workspace(const h3dit_linear_args &a) { return plan_linear(a).part_bytes; }
+
 hipError_t launch_linear(const h3dit_linear_args &a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  const LinearPlan pl = plan_linear(a);
+  if (pl.part_bytes > 0 && (a.workspace == nullptr || a.workspace_bytes < pl.part_bytes)) return hipErrorInvalidValue;
   GemmP p{};
   p.a = reinterpret_cast<const uint8_t *>(a.a);
   p.w = reinterpret_cast<const uint8_t *>(a.w);
@@ -420,30 +550,26 @@ hipError_t launch_linear(const h3dit_linear_args &a, hipStream_t st) {
   p.ok = a.out_k;
   p.ov = a.out_v;
   p.ldv = (int)vt_pitch(a.M);
-  int bn = pick_bn(a.M, a.N);
-  if (a.out_kind == H3DIT_OUT_QKV) {
-    const int64_t d = (int64_t)a.heads * a.head_dim;
-    if (d % bn) bn = 128;
-  }
+  p.part = reinterpret_cast<uint8_t *>(a.workspace);
   const bool i8 = a.precision == H3DIT_INT8;
-  if (i8 && a.a_group > 0) return dispatch_bn<true, H3DIT_OUT_BF16, true>(p, bn, st);
+  if (i8 && a.a_group > 0) return dispatch<true, H3DIT_OUT_BF16, true>(p, pl, st);
   if (a.a_headmajor_hd > 0) {
     if (i8) return hipErrorInvalidValue;
-    if (a.out_kind == H3DIT_OUT_BF16) return dispatch_bn<false, H3DIT_OUT_BF16, false, true>(p, bn, st);
-    if (a.out_kind == H3DIT_OUT_F32) return dispatch_bn<false, H3DIT_OUT_F32, false, true>(p, bn, st);
+    if (a.out_kind == H3DIT_OUT_BF16) return dispatch<false, H3DIT_OUT_BF16, false, true>(p, pl, st);
+    if (a.out_kind == H3DIT_OUT_F32) return dispatch<false, H3DIT_OUT_F32, false, true>(p, pl, st);
     return hipErrorInvalidValue;
   }
   switch (a.out_kind) {
     case H3DIT_OUT_BF16:
-      return i8 ? dispatch_bn<true, H3DIT_OUT_BF16, false>(p, bn, st) : dispatch_bn<false, H3DIT_OUT_BF16, false>(p, bn, st);
+      return i8 ? dispatch<true, H3DIT_OUT_BF16, false>(p, pl, st) : dispatch<false, H3DIT_OUT_BF16, false>(p, pl, st);
     case H3DIT_OUT_F32:
-      return dispatch_bn<false, H3DIT_OUT_F32, false>(p, bn, st);
+      return dispatch<false, H3DIT_OUT_F32, false>(p, pl, st);
     case H3DIT_OUT_I32:
-      return dispatch_bn<true, H3DIT_OUT_I32, false>(p, bn, st);
+      return dispatch<true, H3DIT_OUT_I32, false>(p, pl, st);
     case H3DIT_OUT_GELU:
-      return i8 ? dispatch_bn<true, H3DIT_OUT_GELU, false>(p, bn, st) : dispatch_bn<false, H3DIT_OUT_GELU, false>(p, bn, st);
+      return i8 ? dispatch<true, H3DIT_OUT_GELU, false>(p, pl, st) : dispatch<false, H3DIT_OUT_GELU, false>(p, pl, st);
     case H3DIT_OUT_QKV:
-      return i8 ? dispatch_bn<true, H3DIT_OUT_QKV, false>(p, bn, st) : dispatch_bn<false, H3DIT_OUT_QKV, false>(p, bn, st);
+      return i8 ? dispatch<true, H3DIT_OUT_QKV, false>(p, pl, st) : dispatch<false, H3DIT_OUT_QKV, false>(p, pl, st);
     default:
       return hipErrorInvalidValue;
   }

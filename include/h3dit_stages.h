@@ -69,7 +69,14 @@ int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, const uint16_
  *   H3DIT_OUT_QKV   N = 3*heads*head_dim; t = bf16(value) split into q | k | v; q and k rotated
  *                   pairwise by cos/sin (fp32 [M][head_dim/2]) and rounded once, written
  *                   head-major to out_q, out_k; v written as V^T to out_v.
- * M >= 1; N % 128 == 0; K % 128 == 0 (int8: K % 128 == 0 and K % a_group == 0). */
+ * M >= 1; N % 128 == 0; K % 128 == 0 (int8: K % 128 == 0 and K % a_group == 0).
+ * Work plan: when the output tiles do not fill whole rounds of the chip, the tiles of the last
+ * round are computed as K segments whose fp32 (int32 on the int8 path) partial tiles go to
+ * `workspace` (device, 256-byte aligned, workspace_bytes long) and are summed in segment
+ * order by a second launch.  h3dit_linear_workspace gives the bytes a call needs (0 when it
+ * splits nothing); a call that needs more than workspace_bytes returns H3DIT_EWORKSPACE.  The
+ * plan depends on M, N, K, precision, a_group and out_kind only, so equal shapes accumulate in
+ * the same order; int8 results do not depend on it at all. */
 #define H3DIT_OUT_BF16 0
 #define H3DIT_OUT_F32 1
 #define H3DIT_OUT_I32 2
@@ -89,8 +96,12 @@ typedef struct {
   const float *cos_t, *sin_t;
   int32_t heads, head_dim;
   uint16_t *out_q, *out_k, *out_v;
+  void *workspace;
+  uint64_t workspace_bytes;
 } h3dit_linear_args;
 int h3dit_linear(const h3dit_linear_args *args, void *stream);
+/* Workspace bytes h3dit_linear needs for these arguments, written to *bytes. */
+int h3dit_linear_workspace(const h3dit_linear_args *args, uint64_t *bytes);
 
 /* Rotary + head split of a token-major projection t bf16 [n][3*heads*head_dim] into q, k
  * head-major and v as V^T; the same arithmetic as H3DIT_OUT_QKV. */

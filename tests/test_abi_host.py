@@ -36,6 +36,7 @@ def test_struct_sizes_match_header_layout():
     assert C.sizeof(h3.Layout) == 36
     assert C.sizeof(h3.BlockW) == 8 + 9 * 8
     assert C.sizeof(h3.TokenReduction) == 8
+    assert C.sizeof(h3.LinearArgs) == 160   # 14 pointer-sized / int64 fields + 4 int32 pairs + 2 padded int32
 
 
 def fake_block(precision=h3.BF16):
@@ -58,9 +59,13 @@ def test_workspace_query_bf16(cfg):
     rc, size = query(w, fake_block())
     assert rc == 0
     N, d, f = w.n_tokens, w.hidden, w.mlp
-    # arenas: A = q|k|V^T, B = [N][d], C = [N][f]; plus rotary tables and per-token scales
+    # arenas: A = q|k|V^T, B = [N][d], C = [N][f]; plus rotary tables, per-token scales and
+    # the largest split-K workspace of the four projections
     arenas = (2 * N * d * 2 + d * h3.ldv(N) * 2) + N * d * 2 + N * f * 2
-    assert arenas <= size <= arenas + N * w.head_dim * 4 + N * 4 + 16 * 256
+    sk = max(h3.linear_workspace(N, 3 * d, d, out_kind=h3.OUT_QKV, heads=w.heads, head_dim=w.head_dim),
+             h3.linear_workspace(N, 3 * d, d), h3.linear_workspace(N, d, d), h3.linear_workspace(N, f, d),
+             h3.linear_workspace(N, d, f))
+    assert arenas + sk <= size <= arenas + sk + N * w.head_dim * 4 + N * 4 + 16 * 256
     rc2, size2 = query(w, fake_block(), h3.NO_ALIAS)
     assert rc2 == 0 and size2 > size
 
@@ -163,3 +168,20 @@ def test_call_argument_errors_before_launch():
     assert lib.h3dit_linear(C.byref(args), None) == h3.EINVAL                 # head-major A feeds BF16/F32 only
     args.a_headmajor_hd, args.out_kind = 96, h3.OUT_BF16
     assert lib.h3dit_linear(C.byref(args), None) == h3.EINVAL                 # head dim 96
+
+
+def test_linear_workspace_plan():
+    """Split-K only where the last round of 256 x 256 tiles is partial and K is long enough to
+    pay for the partial tiles; the grouped int8 FC2 never splits."""
+    ws = h3.linear_workspace
+    assert ws(4096, 5120, 20480) == 64 * 256 * 256 * 4 * 4        # FC2: 64 leftover tiles x 4 segments
+    assert ws(4096, 20480, 5120) == 0                              # FC1: 1280 tiles, whole rounds
+    assert ws(4096, 5120, 20480, h3.INT8, 1024) == 0               # grouped FC2
+    assert ws(64, 256, 2048) == 0
+    args = h3.LinearArgs(M=4096, N=5120, K=20480, precision=h3.BF16, a=1 << 20, w=1 << 20, out=1 << 20,
+                         out_kind=h3.OUT_BF16)
+    assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EWORKSPACE   # no workspace given
+    args.workspace, args.workspace_bytes = 1 << 20, 1 << 20
+    assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EWORKSPACE   # too small
+    args.workspace = (1 << 20) + 16
+    assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EINVAL       # misaligned

@@ -134,8 +134,11 @@ def test_quantize_weights():
 
 # ----------------------------------------------------------------------------- projections
 
-@pytest.mark.parametrize("M,N,K", [(300, 768, 256), (513, 1024, 1024), (64, 256, 2048), (1, 128, 128)])
+@pytest.mark.parametrize("M,N,K", [(300, 768, 256), (513, 1024, 1024), (64, 256, 2048), (1, 128, 128),
+                                   (512, 4096, 8192), (300, 2048, 4096)])
 def test_linear_bf16(M, N, K):
+    # 512 x 4096 x 8192 fills less than a round of tiles: computed as split-K segments
+    assert (h3.linear_workspace(M, N, K) > 0) == (M == 512)
     a = bf_randn((M, K), 12)
     wt = bf_randn((N, K), 13, 0.02)
     ag, wg = to_dev(a), to_dev(wt)
@@ -165,7 +168,7 @@ def test_linear_bf16_headmajor_input():
     assert relerr(cpu(acc), oracle.gemm_f32(tok, wt)) <= F32_TOL
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 768, 256), (257, 1024, 1024), (1, 256, 128)])
+@pytest.mark.parametrize("M,N,K", [(300, 768, 256), (257, 1024, 1024), (1, 256, 128), (512, 4096, 8192)])
 def test_linear_int8(M, N, K):
     a = bf_randn((M, K), 16)
     wt = bf_randn((N, K), 17, 0.02)
@@ -188,6 +191,28 @@ def test_linear_int8(M, N, K):
     assert relerr(cpu(gl), oracle.gelu_rows(deq)) <= BF16_TOL
 
 
+def test_linear_int8_splitk_sampled_rows():
+    """4096 x 5120 x 20480 on the int8 path without groups: 64 of the 320 tiles are summed from
+    4 K segments of int32 partials, which must give the exact accumulators."""
+    M, N, K = 4096, 5120, 20480
+    assert h3.linear_workspace(M, N, K, h3.INT8) > 0
+    qa = torch.randint(-127, 128, (M, K), dtype=torch.int8, generator=torch.Generator().manual_seed(5))
+    qw = torch.randint(-127, 128, (N, K), dtype=torch.int8, generator=torch.Generator().manual_seed(6))
+    sa = torch.rand(M, generator=torch.Generator().manual_seed(7)) * 0.01 + 1e-3
+    sw = torch.rand(N, generator=torch.Generator().manual_seed(8)) * 0.01 + 1e-3
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    h3.linear(M, N, K, to_dev(qa), to_dev(qw), h3.OUT_I32, acc, precision=h3.INT8, a_scale=to_dev(sa),
+              w_scale=to_dev(sw))
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    h3.linear(M, N, K, to_dev(qa), to_dev(qw), h3.OUT_BF16, out, precision=h3.INT8, a_scale=to_dev(sa),
+              w_scale=to_dev(sw))
+    # rows of whole tiles and of split tiles (tile rows 8..15 hold the split ones)
+    rows = torch.tensor([0, 1, 255, 1029, 2048, 2049, 2560, 3071, 3333, 4094, 4095])
+    ref = oracle.gemm_i32(qa[rows].contiguous(), qw)
+    assert_bitexact(cpu(acc)[rows], ref, "int32 accumulators, split tiles included")
+    assert_bitexact(cpu(out)[rows], oracle.dequant_bf16(ref, sa[rows].contiguous(), sw), "dequantised output")
+
+
 @pytest.mark.parametrize("M,N,K,G", [(300, 256, 2048, 1024), (129, 512, 1024, 1024), (64, 256, 3072, 1024),
                                      (200, 256, 1024, 256)])
 def test_fc2_grouped_int8(M, N, K, G):
@@ -202,9 +227,13 @@ def test_fc2_grouped_int8(M, N, K, G):
 
 
 @pytest.mark.parametrize("int8", [False, True])
-@pytest.mark.parametrize("M,H,hd", [(300, 4, 64), (130, 2, 128)])
+@pytest.mark.parametrize("M,H,hd", [(300, 4, 64), (130, 2, 128), (4480, 40, 128)])
 def test_linear_qkv_rope_headmajor(M, H, hd, int8):
     d = H * hd
+    # 4480 tokens at d 5120 (the paired sequence of an 8192-token layout): on the bf16 path the
+    # last round of tiles is split along K and the fixup launch runs the rotary epilogue
+    assert (h3.linear_workspace(M, 3 * d, d, h3.INT8 if int8 else h3.BF16, 0, h3.OUT_QKV, H, hd) > 0) == \
+        (M == 4480 and not int8)
     w = WORKLOADS[0].replace(hidden=d, heads=H, head_dim=hd, video_t=2, video_h=5, video_w=M // 10 - 3,
                              n_text=M - 10 * (M // 10 - 3) - 4, n_audio=4)
     assert w.n_tokens == M
