@@ -110,7 +110,11 @@ def test_gate_fused_int8_codes_of_gated_row():
 
 
 @pytest.mark.parametrize("rows,cols,group,hm", [(300, 2048, 1024, 0), (257, 5120, 5120, 0), (130, 512, 512, 128),
-                                                (33, 256, 256, 64)])
+                                                (33, 256, 256, 64),
+                                                # one wave per group: 20 groups; 6 groups (a half-idle
+                                                # workgroup); one and four chunks per lane
+                                                (300, 20480, 1024, 0), (129, 6144, 1024, 0), (64, 4096, 512, 0),
+                                                (50, 8192, 2048, 0)])
 def test_quantize_rows(rows, cols, group, hm):
     v = bf_randn((rows, cols), 10)
     v[3] = 0                                               # an all-zero row
