@@ -40,9 +40,9 @@ struct GemmP {
   int tiles_m, tiles_n;
   // split-K of the last, partial round: tiles [n_dp, tiles_m*tiles_n) are computed as `split`
   // K segments of kt_seg slices each, whose fp32 / int32 partial tiles go to `part`; a second
-  // launch (fixup != 0, one workgroup per split tile) sums them in segment order and runs
-  // the epilogue
-  int n_dp, split, kt_seg, fixup;
+  // launch (the FIX instantiation, one workgroup per split tile) sums them in segment order
+  // and runs the epilogue
+  int n_dp, split, kt_seg;
   uint8_t *part;
 };
 
@@ -84,8 +84,9 @@ __device__ __forceinline__ u32x4 lds_frag(const uint8_t *base, int row, int chun
 }
 
 // out_kind: H3DIT_OUT_*.  GROUPED: int8 FC2 with per-(row, group) activation scales.
-// HM: A is the head-major attention output [K/hd][M][hd] (bf16 only).
-template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM>
+// HM: A is the head-major attention output [K/hd][M][hd] (bf16 only).  FIX: the split-K fixup
+// launch (sums partial tiles and runs the epilogue; its own kernel so that profiles separate it).
+template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM, bool FIX>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   using C = GemmCfg<BM, BN, WGM, WGN>;
   constexpr int FM = C::FM, FN = C::FN, NW = C::NW, NT = C::NT, LA = C::LA, LW = C::LW;
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   int tile, seg = -1;
   const int KT = (int)(p.K * (INT8 ? 1 : 2) / GKB);
   int kt0 = 0, kt1 = KT;
-  if (p.fixup) {
+  if (FIX) {
     tile = p.n_dp + (int)blockIdx.x;
   } else if ((int)blockIdx.x < p.n_dp) {
     tile = xcd_remap((int)blockIdx.x, p.n_dp);
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
     const int64_t slot = (int64_t)(tile - p.n_dp) * p.split + sg;
     return reinterpret_cast<i32x4 *>(p.part + slot * (BM * BN * 4) + ((wid * FM + i) * FN + j) * 4096 + lane * 64);
   };
-  if (!GROUPED && p.fixup) {
+  if constexpr (!GROUPED && FIX) {
     // sum of the segments' partial tiles, in segment order.  (Vectors are reinterpreted
     // whole: clang's __builtin_bit_cast of a single ext_vector element reads element 0.)
     for (int sg = 0; sg < p.split; sg++)
@@ -448,12 +449,13 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
   p.n_dp = pl.n_dp;
   p.split = pl.split;
   p.kt_seg = pl.kt_seg;
-  p.fixup = 0;
   const unsigned grid = (unsigned)(pl.n_dp + pl.n_split * pl.split);
-  k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM><<<grid, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
-  if (pl.n_split > 0) {
-    p.fixup = 1;
-    k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM><<<(unsigned)pl.n_split, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+  k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM, false><<<grid, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+  if constexpr (!GROUPED && BN == 256) {
+    if (pl.n_split > 0) {
+      k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM, true>
+          <<<(unsigned)pl.n_split, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+    }
   }
   return hipGetLastError();
 }
