@@ -2,7 +2,9 @@
 // release uses full attention over the whole joint token sequence).
 //
 // One workgroup = 4 waves = 128 queries of one head (two workgroups per CU); each wave owns 32
-// queries and walks all keys in blocks of 64 with an online softmax in the exp2 domain.  Scores are computed
+// queries and walks all keys in blocks of 64 with an online softmax in the exp2 domain (the
+// reference max is raised only when it would be exceeded by more than 2^8, so the output is
+// rarely rescaled; all query tiles of a head share one XCD's L2).  Scores are computed
 // transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16 with keys as rows), so each lane holds
 // one query column: the row max and row sum are 16 lane-local values plus one exchange with
 // the other half-wave, and the rescale of the output is a per-lane scalar.  O^T = V^T P^T
@@ -75,12 +77,25 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
   using C = AttCfg<HD>;
   constexpr int KS = HD / 16;   // 16-dim steps of the score product
   constexpr int DT = HD / 32;   // 32-dim output tiles
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  // two LDS stages as separate objects, so that the compiler sees that the prefetch of one
+  // never aliases the reads of the other (and does not wait for the prefetch before them)
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[C::STAGE];
 
-  const int h = blockIdx.y;
+  // Workgroups are dealt round-robin to the 8 XCDs in launch order.  When the head count
+  // allows, all query tiles of one head go to the same XCD, so that its K and V^T are fetched
+  // into one L2 instead of eight.
+  const int QT = (int)gridDim.x;
+  int h = blockIdx.y, qt = blockIdx.x;
+  if ((heads & 7) == 0) {
+    const int b = (int)blockIdx.y * QT + (int)blockIdx.x;
+    const int j = b >> 3;
+    h = (b & 7) + 8 * (j / QT);
+    qt = j % QT;
+  }
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int hsel = lane >> 5, l32 = lane & 31;
-  const int64_t q0 = (int64_t)blockIdx.x * AQ + wid * 32;
+  const int64_t q0 = (int64_t)qt * AQ + wid * 32;
   const int64_t qrow = q0 + l32;
   const int64_t head_rows = (int64_t)h * N;
 
@@ -88,7 +103,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt, (uint32_t)((int64_t)heads * HD * ldv * 2));
 
   const int nkb = (int)((N + AKV - 1) / AKV);
-  att_load<HD>(rk, rv, smem, head_rows, (int64_t)h * HD, ldv, 0);
+  att_load<HD>(rk, rv, stage0, head_rows, (int64_t)h * HD, ldv, 0);
 
   // Q fragments (B operand: column = query, 8 dims per lane and step), kept in registers
   u32x4 qf[KS];
@@ -103,14 +118,18 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; t++) acc[t] = f32x16{0};
-  float m_run = -INFINITY, l_run = 0.0f;   // running max of raw scores, running sum
+  // Lazy rescaling: probabilities are taken relative to a reference m_ref (raw score units)
+  // that is raised only when some lane's block max exceeds it by more than 2^8 in the exp2
+  // domain, so p <= 256 and most blocks skip the output rescale.  m_true tracks the true max
+  // for the row statistics; l_run sums 2^((s - m_ref) c2).
+  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
 
   wait_vmem();
   __syncthreads();
 
-  for (int kb = 0; kb < nkb; kb++) {
-    uint8_t *cur = smem + (kb & 1) * C::STAGE;
-    if (kb + 1 < nkb) att_load<HD>(rk, rv, smem + ((kb + 1) & 1) * C::STAGE, head_rows, (int64_t)h * HD, ldv, kb + 1);
+  // one key block: multiply out of `cur`, prefetch the next block into `nxt`
+  auto block = [&](int kb, uint8_t *cur, uint8_t *nxt) {
+    if (kb + 1 < nkb) att_load<HD>(rk, rv, nxt, head_rows, (int64_t)h * HD, ldv, kb + 1);
     const int valid = (int)min((int64_t)AKV, N - (int64_t)kb * AKV);
     if (valid < AKV) {
       // keys past the end: zero their values so that 0-weight * garbage stays 0
@@ -148,34 +167,42 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
           if (key >= valid) s[t][r] = -INFINITY;
         }
     }
-    float mb = s[0][0];
+    float mq[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) mq[u] = fmaxf(s[u >> 1][(u & 1) * 8], s[u >> 1][(u & 1) * 8 + 1]);
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) mb = fmaxf(mb, s[t][r]);
+      for (int r = 0; r < 16; r++)
+        if ((r & 7) > 1) mq[t * 2 + (r >> 3)] = fmaxf(mq[t * 2 + (r >> 3)], s[t][r]);
+    float mb = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);          // raw units
-    const float mc = m_new * c2;
-    const float corr = __builtin_amdgcn_exp2f(m_run * c2 - mc);   // 0 on the first block
-    float ls = 0.0f;
+    m_true = fmaxf(m_true, mb);
+    // raise the reference (and rescale what was summed against the old one) only when a
+    // lane's scores would exceed it by more than 2^8; the first block always does
+    if (__any((mb - m_ref) * c2 > 8.0f)) {
+      const float m_new = fmaxf(m_ref, mb);
+      const float corr = __builtin_amdgcn_exp2f((m_ref - m_new) * c2);   // 0 on the first block
+      l_run *= corr;
+#pragma unroll
+      for (int t = 0; t < DT; t++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[t][r] *= corr;
+      m_ref = m_new;
+    }
+    const float mc = m_ref * c2;
+    float lq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c2, -mc));
         s[t][r] = p;
-        ls += p;
+        lq[t * 2 + (r >> 3)] += p;
       }
+    float ls = (lq[0] + lq[1]) + (lq[2] + lq[3]);
     ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * corr + ls;
-    m_run = m_new;
-    // rescale the output only if some query's max moved (corr == 1 exactly otherwise)
-    if (__any(corr != 1.0f)) {
-#pragma unroll
-      for (int t = 0; t < DT; t++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[t][r] *= corr;
-    }
+    l_run += ls;
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
     for (int ps = 0; ps < 4; ps++) {
@@ -193,6 +220,10 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int kb = 0; kb < nkb; kb += 2) {
+    block(kb, stage0, stage1);
+    if (kb + 1 < nkb) block(kb + 1, stage1, stage0);
   }
 
   // O[h][q][dim] = O^T / l; lane holds dims dt*32 + 8(r/4) + 4 hsel + r%4 of query qrow
@@ -210,8 +241,8 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__res
         *reinterpret_cast<uint2 *>(dst + dim) = v;
       }
     if (row_max && hsel == 0) {
-      row_max[head_rows + qrow] = m_run * (1.0f / sqrtf((float)HD));
-      row_sum[head_rows + qrow] = l_run;
+      row_max[head_rows + qrow] = m_true * (1.0f / sqrtf((float)HD));
+      row_sum[head_rows + qrow] = l_run * __builtin_amdgcn_exp2f((m_ref - m_true) * c2);
     }
   }
 }

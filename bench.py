@@ -266,8 +266,10 @@ def main():
     mm = {k: v for k, v in kern.items() if "flop" in v}
     dom = max(mm, key=lambda k: mm[k]["ms"])
     prec = "int8" if int8_main else "bf16"
-    roof = {"bound": "mfma", "kernel": dom, "achieved": mm[dom]["tflops"], "peak": PEAK[prec],
-            "unit": "TFLOP/s" if prec == "bf16" else "TOP/s", "frac": round(mm[dom]["tflops"] / PEAK[prec], 4),
+    # attention multiplies bf16 on both paths; the int8 path's projections use the int8 peak
+    kprec = "int8" if (int8_main and dom != "attention") else "bf16"
+    roof = {"bound": "mfma", "kernel": dom, "achieved": mm[dom]["tflops"], "peak": PEAK[kprec],
+            "unit": "TFLOP/s" if kprec == "bf16" else "TOP/s", "frac": round(mm[dom]["tflops"] / PEAK[kprec], 4),
             "traffic": traffic_for(dom)}
     extra = {"ms_per_block": round(ms / w.blocks, 3), "tflop_per_step": round(step_flop / 1e12, 2),
              "workspace_bytes": ws_bytes, "kernels": kern, "wall_s_timed": round(wall, 3)}
