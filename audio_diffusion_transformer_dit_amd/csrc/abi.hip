@@ -36,7 +36,11 @@ int check_dims(const h3dit_dims *D, const h3dit_layout *L, int precision) {
   if (!(D->ln_eps >= 0.0f)) return H3DIT_EINVAL;
   if (precision != H3DIT_BF16 && precision != H3DIT_INT8) return H3DIT_EINVAL;
   if (precision == H3DIT_INT8) {
-    if (D->fc2_group < 128 || D->fc2_group % 128 || D->fc2_group > 8192 || D->mlp % D->fc2_group) return H3DIT_EINVAL;
+    // 1024-channel groups as on the pages, or one code per token over the whole FC2 input
+    // (fc2_group == mlp, the row-level variant)
+    if (D->fc2_group < 128 || D->fc2_group % 128 || (D->fc2_group > 8192 && D->fc2_group != D->mlp) ||
+        D->mlp % D->fc2_group)
+      return H3DIT_EINVAL;
   }
   if (L->video_t < 0 || L->video_h < 0 || L->video_w < 0 || L->n_text < 0 || L->n_audio < 0) return H3DIT_EINVAL;
   if (layout_tokens(*L, false) != D->n_tokens) return H3DIT_EINVAL;
@@ -108,7 +112,7 @@ size_t block_splitk_bytes(const h3dit_dims &D, int precision, int64_t n) {
   take(3 * (int64_t)D.hidden, D.hidden, H3DIT_OUT_BF16, 0);
   take(D.hidden, D.hidden, H3DIT_OUT_BF16, 0);
   take(D.mlp, D.hidden, H3DIT_OUT_GELU, 0);
-  take(D.hidden, D.mlp, H3DIT_OUT_BF16, i8 ? D.fc2_group : 0);
+  take(D.hidden, D.mlp, H3DIT_OUT_BF16, (i8 && D.fc2_group != D.mlp) ? D.fc2_group : 0);
   return m;
 }
 
@@ -278,7 +282,9 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
     TRY(launch_quant_rows(n, f, D.fc2_group, c.at<uint16_t>(P.gl), 0, c.at<int8_t>(P.qg), c.at<float>(P.sg), c.st));
     la.a = c.at<void>(P.qg);
     la.a_scale = c.at<float>(P.sg);
-    la.a_group = D.fc2_group;
+    // one group per token is the per-token formula bit for bit ((0 + acc*s) * s_w): it runs on
+    // the ungrouped kernels (256 x 256 tiles, split-K)
+    la.a_group = D.fc2_group == D.mlp ? 0 : D.fc2_group;
   }
   TRY(launch_linear(la, c.st));
 

@@ -234,7 +234,48 @@ __global__ __launch_bounds__(256) void k_quant_groups(int64_t rows, int64_t cols
   }
 }
 
-// Spans longer than the register-resident kernel holds (weight rows of the FC2 matrix, 20480
+// Token-major spans of 8193..32768 columns (a whole FC2-input row of 20480 channels, the
+// 20480-wide weight rows): one 256-lane workgroup per span, values in registers, one pass
+// over global memory.  Same arithmetic as k_quant_rows.
+constexpr int QWIDE_THREADS = 256;
+constexpr int QWIDE_MAXJ = 16;
+__global__ __launch_bounds__(QWIDE_THREADS) void k_quant_wide(int64_t cols, int group, const uint16_t *__restrict__ v,
+                                                              int8_t *__restrict__ q, float *__restrict__ s) {
+  __shared__ float red[QWIDE_THREADS / 64];
+  const int64_t r = blockIdx.x;
+  const int64_t g = blockIdx.y;
+  const int nch = group >> 3;
+  const int tid = threadIdx.x;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(v + r * cols + g * group);
+  float val[QWIDE_MAXJ][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < QWIDE_MAXJ; j++) {
+    const int c = tid + j * QWIDE_THREADS;
+    if (c < nch) {
+      unpack8(src[c], val[j]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(val[j][e]));
+    }
+  }
+  const float sa = block_max<QWIDE_THREADS / 64>(amax, red) / 127.0f;
+  if (tid == 0) s[r * (cols / group) + g] = sa;
+  uint2 *dst = reinterpret_cast<uint2 *>(q + r * cols + g * group);
+#pragma unroll
+  for (int j = 0; j < QWIDE_MAXJ; j++) {
+    const int c = tid + j * QWIDE_THREADS;
+    if (c < nch) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q8_code(val[j][e], sa) << (8 * e);
+#pragma unroll
+      for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q8_code(val[j][4 + e], sa) << (8 * e);
+      dst[c] = make_uint2(lo, hi);
+    }
+  }
+}
+
+// Spans longer than the register-resident kernels hold (weight rows of the FC2 matrix, 20480
 // wide): one workgroup per span, absmax in a first pass over global memory, codes in a second.
 __global__ __launch_bounds__(ROW_THREADS) void k_quant_long(int64_t cols, int64_t group, const uint16_t *__restrict__ v,
                                                             int8_t *__restrict__ q, float *__restrict__ s) {
@@ -271,7 +312,10 @@ hipError_t launch_quant_rows(int64_t rows, int64_t cols, int64_t group, const ui
   dim3 grid((unsigned)rows, (unsigned)(cols / group)), block(ROW_THREADS);
   if (group > (int64_t)ROW_THREADS * ROW_MAXJ * 8) {
     if (hm_hd > 0) return hipErrorInvalidValue;
-    k_quant_long<<<grid, block, 0, st>>>(cols, group, v, q, s);
+    if (group <= (int64_t)QWIDE_THREADS * QWIDE_MAXJ * 8)
+      k_quant_wide<<<grid, QWIDE_THREADS, 0, st>>>(cols, (int)group, v, q, s);
+    else
+      k_quant_long<<<grid, block, 0, st>>>(cols, group, v, q, s);
   } else if (hm_hd == 0 && group <= 64 * 8 * QW_MAXJ && cols / group >= 4) {
     dim3 g4((unsigned)rows, (unsigned)((cols / group + 3) / 4));
     k_quant_groups<<<g4, 256, 0, st>>>(rows, cols, (int)group, v, q, s);

@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--only-kernels", action="store_true", help="per-kernel timing only (profiling runs)")
+    ap.add_argument("--fc2-group", type=int, default=None,
+                    help="int8 FC2-input group (1024 as on the pages; the MLP width gives one code per token, "
+                         "the row-level variant)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only-kernels: also run one plain device copy of this many bytes, the reference "
                          "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -144,8 +147,10 @@ def kernel_breakdown(w, p, x, iters, int8):
                                                                   sg.data_ptr(),
                                                                   torch.cuda.current_stream().cuda_stream),
                              0, 3.0 * N * f + 4.0 * N * f / w.fc2_group),
-            "fc2_gemm_i8": (lambda: h3.linear(N, d, f, qg, p["q2"], h3.OUT_BF16, y2, precision=h3.INT8, a_scale=sg,
-                                              a_group=w.fc2_group, w_scale=p["s2"]), 2.0 * N * f * d, 0),
+            "fc2_gemm_i8": (lambda: h3.linear(N, d, f, qg, p["q2"], h3.OUT_BF16, y2, precision=h3.INT8,
+                                              a_scale=sg if w.fc2_group < f else sg[:, 0].contiguous(),
+                                              a_group=w.fc2_group if w.fc2_group < f else 0, w_scale=p["s2"]),
+                            2.0 * N * f * d, 0),
             "gate": (lambda: h3.row_gate_adaln(x1, gate=mod[5], y=y2, x_out=x2), 0, 6.0 * N * d),
         }
     # one pass in order so that every kernel reads realistic data
@@ -227,6 +232,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.blocks:
         w = w.replace(blocks=args.blocks)
+    if args.fc2_group:
+        w = w.replace(fc2_group=args.fc2_group)
     seed = synth.seed_for(args.workload)
     int8_main = w.precision == "int8"
     red = (w.reduce_after, w.restore_before) if w.reduce_after >= 0 else None
@@ -280,6 +287,7 @@ def main():
         blocks8 = make_blocks(w, w.blocks, seed, dev, True)
         ms8, _, _ = time_stack(w, blocks8, x, args.steps, args.warmup, red)
         extra["int8"] = {"ms_per_step": round(ms8, 3), "ms_per_block": round(ms8 / w.blocks, 3),
+                         "fc2_group": w.fc2_group,
                          "tops": round(step_flop / (ms8 / 1e3) / 1e12, 1),
                          "kernels": kernel_breakdown(w, blocks8[0], x, args.kernel_iters, True)}
         del blocks8

@@ -15,6 +15,9 @@
  *        AdaLN fusion, cross-block AdaLN, activation aliasing, byte-identical fallbacks),
  *        "Token 缩减：28% 的去噪时间消减" (horizontal pairing after block 3, bypass,
  *        restore before block 40).
+ *   [NS] daily.steinslab.io, "零 Python 依赖：Redis 作者的 3.5 秒端侧实验", sections "算力拆解：如何在
+ *        M5 Max 上把 16.69 秒压到 12.60 秒" (row-level int8 FC2 option) and "极简主控逻辑"
+ *        (spatial rotary positions).
  * The pages give the block in prose only; widths, activation, eps and rotary layout are
  * parameters here, and each reading of an unstated detail is named where it applies.
  *
@@ -59,8 +62,11 @@ extern "C" {
 #define H3DIT_NO_ALIAS 32u          /* every activation in its own workspace region */
 
 /* Widths.  hidden = heads * head_dim; head_dim 64 or 128; hidden % 256 == 0;
- * mlp % 256 == 0, and on the int8 path mlp % fc2_group == 0 with fc2_group % 128 == 0
- * (1024 is the pages' group).  ln_eps: LayerNorm epsilon (1e-6). */
+ * mlp % 256 == 0, and on the int8 path mlp % fc2_group == 0 with fc2_group % 128 == 0 and
+ * fc2_group <= 8192 (1024 is the pages' group), or fc2_group == mlp: one code per token over
+ * the whole FC2 input, the row-level int8 FC2 option of [NS] "算力拆解：如何在 M5 Max 上把
+ * 16.69 秒压到 12.60 秒" (bit for bit the grouped formula with a single group).
+ * ln_eps: LayerNorm epsilon (1e-6). */
 typedef struct {
   int32_t n_tokens, hidden, heads, head_dim, mlp, fc2_group;
   float ln_eps;

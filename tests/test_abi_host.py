@@ -185,3 +185,17 @@ def test_linear_workspace_plan():
     assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EWORKSPACE   # too small
     args.workspace = (1 << 20) + 16
     assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EINVAL       # misaligned
+
+
+def test_int8_row_level_fc2_group_accepted():
+    """fc2_group == mlp (one code per token over the FC2 input) is accepted above 8192;
+    other groups above 8192 are not."""
+    w = WORKLOADS[2]
+    dims = h3.dims_of(w)
+    size = C.c_size_t(0)
+    blk = fake_block(h3.INT8)
+    for g, ok in ((w.mlp, True), (10240, False), (4096, True)):
+        dims.fc2_group = g
+        rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(h3.layout_of(w)), C.byref(blk), None, 0, None,
+                                      C.byref(size), None)
+        assert (rc == 0) == ok, g

@@ -80,6 +80,19 @@ def test_block_matches_oracle(w, int8):
     check_residual(cpu(xg), ref, x)
 
 
+@pytest.mark.parametrize("group", [1024, 4096], ids=["groups1024", "row"])
+def test_block_int8_fc2_grouping(group):
+    """FC2 input codes per 1024-channel group, or per token over the whole 4096-wide input (the
+    row-level variant, run on the ungrouped kernels): each against the oracle's grouped FC2."""
+    w = W0.replace(mlp=4096, fc2_group=group)
+    x, ps = inputs(w)
+    pg = gpu_params(ps, True)[0]
+    pc = cpu_params(ps, True)[0]
+    xg = x.to(DEV)
+    h3.block_fwd(w, pg, xg)
+    check_residual(cpu(xg), oracle.block_fwd(w, pc, x), x)
+
+
 @pytest.mark.parametrize("int8", [False, True])
 def test_block_zero_gates_is_identity(int8):
     x, ps = inputs(W0)

@@ -114,7 +114,9 @@ def test_gate_fused_int8_codes_of_gated_row():
                                                 # one wave per group: 20 groups; 6 groups (a half-idle
                                                 # workgroup); one and four chunks per lane
                                                 (300, 20480, 1024, 0), (129, 6144, 1024, 0), (64, 4096, 512, 0),
-                                                (50, 8192, 2048, 0)])
+                                                (50, 8192, 2048, 0),
+                                                # whole rows of 16384 / 20480 in registers; 40960 in two passes
+                                                (30, 16384, 16384, 0), (64, 20480, 20480, 0), (8, 40960, 40960, 0)])
 def test_quantize_rows(rows, cols, group, hm):
     v = bf_randn((rows, cols), 10)
     v[3] = 0                                               # an all-zero row
@@ -228,6 +230,23 @@ def test_fc2_grouped_int8(M, N, K, G):
     h3.linear(M, N, K, to_dev(qa), to_dev(qw), h3.OUT_BF16, y, precision=h3.INT8, a_scale=to_dev(sa), a_group=G,
               w_scale=to_dev(sw))
     assert_bitexact(cpu(y), oracle.fc2_int8(qa, sa, qw, sw, G), "grouped FC2")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 256, 4096), (257, 512, 20480)])
+def test_fc2_row_codes_on_ungrouped_kernel(M, N, K):
+    """Row-level FC2: one code per token over the whole input, multiplied on the ungrouped
+    int8 kernel, equals the grouped formula with a single group bit for bit."""
+    gl = bf_randn((M, K), 22)
+    wt = bf_randn((N, K), 23, 0.02)
+    qw, sw = oracle.quantize_weights(wt)
+    qa, sa = h3.quantize_rows(to_dev(gl), M, K, K)
+    qa_ref, sa_ref = oracle.q8_rows(gl, K)
+    assert_bitexact(cpu(qa), qa_ref, "codes")
+    assert_bitexact(cpu(sa), sa_ref, "scales")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    h3.linear(M, N, K, qa, to_dev(qw), h3.OUT_BF16, y, precision=h3.INT8, a_scale=sa[:, 0].contiguous(),
+              w_scale=to_dev(sw))
+    assert_bitexact(cpu(y), oracle.fc2_int8(qa_ref, sa_ref, qw, sw, K), "row-level FC2")
 
 
 @pytest.mark.parametrize("int8", [False, True])
