@@ -42,6 +42,9 @@
 extern "C" {
 #endif
 
+/* Exported entry points (the library is built with hidden default visibility). */
+#define H3DIT_API __attribute__((visibility("default")))
+
 #define H3DIT_OK 0
 #define H3DIT_EINVAL (-1)       /* bad sizes, NULL or misaligned pointer, bad schedule */
 #define H3DIT_EWORKSPACE (-2)   /* workspace too small; required size written back */
@@ -115,7 +118,7 @@ typedef struct {
  * [rows][cols], device), s[r] = max|w[r][:]| / 127 (IEEE division) and
  * q[r][c] = round-half-even(w[r][c] / s[r]) clamped to +-127 (0 when s[r] == 0).
  * q: int8 [rows][cols] device; s: fp32 [rows] device.  cols % 8 == 0, rows < 2^31. */
-int h3dit_quantize_weights(const uint16_t *w, int64_t rows, int64_t cols, int8_t *q, float *s,
+H3DIT_API int h3dit_quantize_weights(const uint16_t *w, int64_t rows, int64_t cols, int8_t *q, float *s,
                            void *stream);
 
 /* One block, x <- block(x), with no cross-block fusion ([DD] "DiT 融合内核" for the order):
@@ -128,7 +131,7 @@ int h3dit_quantize_weights(const uint16_t *w, int64_t rows, int64_t cols, int8_t
  * x: bf16 [n_tokens][hidden] device, in/out.  layout: token layout and rotary (host).
  * workspace: device scratch of *workspace_bytes bytes; with workspace == NULL the required
  * size is written to *workspace_bytes and H3DIT_OK returned without launching. */
-int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_block_w *blk,
+H3DIT_API int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_block_w *blk,
                     uint16_t *x, uint32_t flags, void *workspace, size_t *workspace_bytes,
                     void *stream);
 
@@ -136,7 +139,7 @@ int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3
  * [DD] fusion of each block's final gate with the next block's AdaLN1, and activation
  * arenas reused across lifetimes).  blocks: host array of n_blocks entries (device
  * pointers inside).  tr: NULL for no token reduction.  Other arguments as h3dit_block_fwd. */
-int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
+H3DIT_API int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
                     const h3dit_block_w *blocks, const h3dit_token_reduction *tr, uint16_t *x,
                     uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream);
 

@@ -29,7 +29,7 @@ extern "C" {
 /* Rotary tables cos/sin fp32 [n][head_dim/2] (device) for the layout of h3dit.h; reduced != 0
  * gives the paired sequence, where pair token (t,h,k) sits at w = 2k + 0.5.  Returns the
  * token count (>= 0) or a negative status. */
-int h3dit_rope_tables(const h3dit_layout *layout, int32_t head_dim, int32_t reduced, float *cos_t,
+H3DIT_API int h3dit_rope_tables(const h3dit_layout *layout, int32_t head_dim, int32_t reduced, float *cos_t,
                       float *sin_t, void *stream);
 
 /* Row kernel ([DD] "DiT 融合内核", 门控 AdaLN 融合).  Per token row r of d features:
@@ -41,7 +41,7 @@ int h3dit_rope_tables(const h3dit_layout *layout, int32_t head_dim, int32_t redu
  *                     q (int8 [n][d]) / s (fp32 [n]) receive the per-row int8 code of hv
  *                     ([DD] "int8 量化": absmax/127, round-half-even) if non-NULL.
  * gate/shift/scale: bf16 [d].  x_out may equal x (in place).  d % 8 == 0, d <= 8192. */
-int h3dit_row_gate_adaln(int64_t n, int32_t d, float eps, const uint16_t *x, const uint16_t *gate,
+H3DIT_API int h3dit_row_gate_adaln(int64_t n, int32_t d, float eps, const uint16_t *x, const uint16_t *gate,
                          const uint16_t *y, uint16_t *x_out, const uint16_t *shift,
                          const uint16_t *scale, uint16_t *h, int8_t *q, float *s, void *stream);
 
@@ -50,7 +50,7 @@ int h3dit_row_gate_adaln(int64_t n, int32_t d, float eps, const uint16_t *x, con
  * [rows][cols], or, when headmajor_hd > 0, the head-major attention output [cols/hd][rows][hd]
  * read as token-major.  q: int8 [rows][cols]; s: fp32 [rows][cols/group].
  * cols % group == 0, group % 8 == 0; head-major input needs group <= 8192. */
-int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v,
+H3DIT_API int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v,
                         int32_t headmajor_hd, int8_t *q, float *s, void *stream);
 
 /* Projection out = A W^T on MFMA ([DD] "h3.c 的核心设计", "int8 量化").
@@ -99,17 +99,17 @@ typedef struct {
   void *workspace;
   uint64_t workspace_bytes;
 } h3dit_linear_args;
-int h3dit_linear(const h3dit_linear_args *args, void *stream);
+H3DIT_API int h3dit_linear(const h3dit_linear_args *args, void *stream);
 /* Workspace bytes h3dit_linear needs for these arguments, written to *bytes. */
-int h3dit_linear_workspace(const h3dit_linear_args *args, uint64_t *bytes);
+H3DIT_API int h3dit_linear_workspace(const h3dit_linear_args *args, uint64_t *bytes);
 
 /* Rotary + head split of a token-major projection t bf16 [n][3*heads*head_dim] into q, k
  * head-major and v as V^T; the same arithmetic as H3DIT_OUT_QKV. */
-int h3dit_rope_split(int64_t n, int32_t heads, int32_t head_dim, const uint16_t *t, const float *cos_t,
+H3DIT_API int h3dit_rope_split(int64_t n, int32_t heads, int32_t head_dim, const uint16_t *t, const float *cos_t,
                      const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *vt, void *stream);
 
 /* gl = bf16(GELU_tanh(u)) elementwise over count bf16 values (count % 8 == 0). */
-int h3dit_gelu(int64_t count, const uint16_t *u, uint16_t *gl, void *stream);
+H3DIT_API int h3dit_gelu(int64_t count, const uint16_t *u, uint16_t *gl, void *stream);
 
 /* Full non-causal attention ([RV] README: full attention), per head h and query n:
  *   o[h][n] = bf16( sum_m softmax_m(q[h][n] . k[h][m] / sqrt(hd)) v[h][m] ),
@@ -119,20 +119,20 @@ int h3dit_gelu(int64_t count, const uint16_t *u, uint16_t *gl, void *stream);
  * anything.  row_max / row_sum (fp32
  * [H][n], optional) receive max_m(score) and sum_m exp(score - max) in natural-log units.
  * head_dim 64 or 128. */
-int h3dit_attention(int32_t heads, int64_t n, int32_t head_dim, const uint16_t *q, const uint16_t *k,
+H3DIT_API int h3dit_attention(int32_t heads, int64_t n, int32_t head_dim, const uint16_t *q, const uint16_t *k,
                     const uint16_t *vt, uint16_t *o, float *row_max, float *row_sum, void *stream);
 
 /* Token pair step ([DD] "Token 缩减"): r = bf16((a + b) * 0.5) for each horizontal pair
  * (t,h,2k),(t,h,2k+1) of x (bf16 [n_full][d]), the odd last column, text and audio copied;
  * reduced order per (t,h) row: pairs, then the unpaired column; then text, audio.
  * r and r_in (bf16 [n_reduced][d]) both receive the result (r_in may be NULL). */
-int h3dit_token_pair(const h3dit_layout *layout, int32_t d, const uint16_t *x, uint16_t *r,
+H3DIT_API int h3dit_token_pair(const h3dit_layout *layout, int32_t d, const uint16_t *x, uint16_t *r,
                      uint16_t *r_in, void *stream);
 
 /* Token restore step ([DD] "Token 缩减"): for paired token i of pair p,
  * x[i] = bf16(x[i] + (y[p] - r_in[p])); every other token x[i] = y[p].  x (bf16 [n_full][d])
  * holds the bypass on entry and the restored residual on return. */
-int h3dit_token_restore(const h3dit_layout *layout, int32_t d, uint16_t *x, const uint16_t *y,
+H3DIT_API int h3dit_token_restore(const h3dit_layout *layout, int32_t d, uint16_t *x, const uint16_t *y,
                         const uint16_t *r_in, void *stream);
 
 #ifdef __cplusplus

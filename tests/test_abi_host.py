@@ -4,6 +4,7 @@ launch (a call that reached the device here would fail with EHIP, not the code a
 import ctypes as C
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -19,16 +20,20 @@ def declared_functions():
     names = set()
     for hdr in ("h3dit.h", "h3dit_stages.h"):
         with open(os.path.join(ROOT, "include", hdr)) as fh:
-            names.update(re.findall(r"^int\s+(h3dit_\w+)\s*\(", fh.read(), flags=re.M))
+            names.update(re.findall(r"^H3DIT_API\s+int\s+(h3dit_\w+)\s*\(", fh.read(), flags=re.M))
     return sorted(names)
 
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) >= 12
+    assert len(names) >= 13
     assert set(names) == set(h3.EXPORTS)
     for n in names:
         assert getattr(h3.lib(), n) is not None
+    # and nothing else of the C ABI: the library is built with hidden default visibility
+    out = subprocess.run(["nm", "-D", "--defined-only", h3.LIB_PATH], capture_output=True, text=True).stdout
+    c_funcs = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert c_funcs == set(names)
 
 
 def test_struct_sizes_match_header_layout():
