@@ -19,7 +19,7 @@ _lib = None
 class Dims(C.Structure):
     _fields_ = [("n_tokens", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
                 ("head_dim", C.c_int32), ("mlp", C.c_int32), ("fc2_group", C.c_int32),
-                ("ln_eps", C.c_float)]
+                ("ln_eps", C.c_float), ("n_video", C.c_int32), ("n_text", C.c_int32)]
 
 
 class Layout(C.Structure):
@@ -31,7 +31,7 @@ class Layout(C.Structure):
 class Block(C.Structure):
     _fields_ = [("int8", C.c_int32)] + \
         [(n, C.c_void_p) for n in ("wqkv", "wo", "w1", "w2", "qqkv", "qo", "q1", "q2",
-                                   "sqkv", "so", "s1", "s2", "mod")]
+                                   "sqkv", "so", "s1", "s2", "mod")] + [("mod_sets", C.c_int32)]
 
 
 class Taps(C.Structure):
@@ -71,8 +71,13 @@ def bf16(shape):
 
 
 def dims_of(w, n_tokens=None) -> Dims:
-    return Dims(int(n_tokens if n_tokens is not None else w.n_tokens), w.hidden, w.heads, w.head_dim,
-                w.mlp, w.fc2_group, w.ln_eps)
+    """Widths and the segments of an n_tokens sequence: the workload's own, or its paired
+    (reduced) sequence, whose video part is shorter by the number of pairs."""
+    N = int(n_tokens if n_tokens is not None else w.n_tokens)
+    n_video = N - w.n_text - w.n_audio
+    if n_video < 0:
+        raise ValueError("sequence shorter than the text and audio segments")
+    return Dims(N, w.hidden, w.heads, w.head_dim, w.mlp, w.fc2_group, w.ln_eps, n_video, w.n_text)
 
 
 def layout_of(w) -> Layout:
@@ -226,6 +231,7 @@ def _block_struct(p: dict, keep: list) -> Block:
     """p: bf16 weights {wqkv, wo, w1, w2, mod} and, for int8, {qqkv, sqkv, qo, so, q1, s1, q2, s2}."""
     b = Block()
     b.int8 = 1 if "qqkv" in p else 0
+    b.mod_sets = p["mod"].shape[0] // 6
     for name in ("wqkv", "wo", "w1", "w2", "qqkv", "qo", "q1", "q2", "sqkv", "so", "s1", "s2", "mod"):
         t = p.get(name)
         if t is not None:

@@ -24,6 +24,8 @@
 typedef struct {
   int32_t n_tokens, hidden, heads, head_dim, mlp, fc2_group;
   float ln_eps;
+  int32_t n_video, n_text;           /* segments of the current sequence: video rows, then text,
+                                        then audio (the rest); they select the modulation set */
 } orc_dims;
 
 typedef struct {
@@ -38,7 +40,8 @@ typedef struct {
   const uint16_t *wqkv, *wo, *w1, *w2;  /* bf16 [3d][d], [d][d], [f][d], [d][f] */
   const int8_t *qqkv, *qo, *q1, *q2;    /* int8, same shapes */
   const float *sqkv, *so, *s1, *s2;     /* fp32 per output row */
-  const uint16_t *mod;                  /* bf16 [6][d]: shift1 scale1 gate1 shift2 scale2 gate2 */
+  const uint16_t *mod;                  /* bf16 [mod_sets][6][d]: shift1 scale1 gate1 shift2 scale2 gate2 */
+  int32_t mod_sets;                     /* 1: one set for every token; 3: video, text, audio sets */
 } orc_block;
 
 typedef struct {                        /* optional stage outputs; any pointer may be NULL */

@@ -113,6 +113,7 @@ class Workload:
     reduce_after: int = -1
     restore_before: int = -1
     fc2_group: int = 1024
+    mod_sets: int = 1          # modulation sets: 1 for all tokens, or 3 (video, text, audio)
     ln_eps: float = 1e-6
     rope_theta: float = 10000.0
     rope_split: tuple = field(default=None)
@@ -163,12 +164,12 @@ def make_x(w: Workload, seed: int, device="cpu") -> torch.Tensor:
 
 def make_block(w: Workload, seed: int, block: int, device="cpu") -> dict:
     """bf16 weights of one block, [out][in] row-major, plus the 6 modulation rows
-    (shift1, scale1, gate1, shift2, scale2, gate2)."""
+    (shift1, scale1, gate1, shift2, scale2, gate2) per modulation set."""
     d, f = w.hidden, w.mlp
     return {
         "wqkv": normal_bf16(seed, block, T_WQKV, (3 * d, d), STD_W, device),
         "wo": normal_bf16(seed, block, T_WO, (d, d), STD_W, device),
         "w1": normal_bf16(seed, block, T_W1, (f, d), STD_W, device),
         "w2": normal_bf16(seed, block, T_W2, (d, f), STD_W, device),
-        "mod": normal_bf16(seed, block, T_MOD, (6, d), STD_MOD, device),
+        "mod": normal_bf16(seed, block, T_MOD, (6 * w.mod_sets, d), STD_MOD, device),
     }

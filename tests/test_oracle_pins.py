@@ -590,3 +590,69 @@ def test_stack_reduction_matches_stepwise():
     y = oracle.token_restore(w, y, z, r)
     y = oracle.block_fwd(w, blocks[3], y)
     assert torch.equal(out.view(torch.int16), y.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- modulation sets
+
+def _three_sets(p, sets=None):
+    """The block with modulation [3][6][d]: three copies of its one set, or the given sets."""
+    q = dict(p)
+    q["mod"] = p["mod"].repeat(3, 1).contiguous() if sets is None else sets
+    return q
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_three_equal_mod_sets_equal_one_set(int8):
+    x, p = _tiny_inputs()
+    q = _three_sets(p)
+    if int8:
+        p, q = oracle.quantize_block(p), oracle.quantize_block(q)
+    w3 = W0.replace(mod_sets=3)
+    for fused in (False, True):
+        a = oracle.block_fwd(W0, p, x, fused=fused)
+        b = oracle.block_fwd(w3, q, x, fused=fused)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_mod_sets_select_token_segments():
+    """Each segment takes its own set: gates of zero in the text set alone leave exactly the
+    text rows unchanged; AdaLN1 of the audio rows uses the audio set's shift and scale."""
+    w = W0.replace(mod_sets=3)
+    x = synth.make_x(w, 1000)
+    p = synth.make_block(w, 1000, 0)
+    assert p["mod"].shape == (18, w.hidden)
+    mod = p["mod"].clone()
+    mod[6 + 2] = 0   # text gate1
+    mod[6 + 5] = 0   # text gate2
+    p["mod"] = mod
+    out, taps = oracle.block_fwd(w, p, x, taps=True)
+    nv, nt = w.n_video, w.n_text
+    i16 = lambda t: t.view(torch.int16)
+    assert torch.equal(i16(out[nv:nv + nt]), i16(x[nv:nv + nt]))
+    assert not torch.equal(i16(out[:nv]), i16(x[:nv]))
+    assert not torch.equal(i16(out[nv + nt:]), i16(x[nv + nt:]))
+    ha = oracle.adaln(x[nv + nt:].contiguous(), mod[12], mod[13], w.ln_eps)
+    hv = oracle.adaln(x[:nv].contiguous(), mod[0], mod[1], w.ln_eps)
+    assert torch.equal(i16(taps["h1"][nv + nt:]), i16(ha))
+    assert torch.equal(i16(taps["h1"][:nv]), i16(hv))
+
+
+def test_mod_sets_in_a_reduced_stack():
+    """Through pair and restore: three equal sets equal one set, and zero text gates in every
+    block leave the text rows unchanged (the paired sequence keeps text and audio whole)."""
+    w1 = _small_tr(7)
+    w3 = w1.replace(mod_sets=3)
+    x, blocks = _stack_inputs(w1, 4)
+    b3 = [_three_sets(p) for p in blocks]
+    a = oracle.stack_fwd(w1, blocks, x, reduce_after=0, restore_before=3, fused=True)
+    b = oracle.stack_fwd(w3, b3, x, reduce_after=0, restore_before=3, fused=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for p in b3:
+        mod = p["mod"].clone()
+        mod[6 + 2] = 0
+        mod[6 + 5] = 0
+        p["mod"] = mod
+    c = oracle.stack_fwd(w3, b3, x, reduce_after=0, restore_before=3, fused=True)
+    nv, nt = w3.n_video, w3.n_text
+    assert torch.equal(c[nv:nv + nt].view(torch.int16), x[nv:nv + nt].view(torch.int16))
+    assert not torch.equal(c[:nv].view(torch.int16), x[:nv].view(torch.int16))
