@@ -48,7 +48,7 @@ class Dims(C.Structure):
 class Layout(C.Structure):
     _fields_ = [("video_t", C.c_int32), ("video_h", C.c_int32), ("video_w", C.c_int32), ("n_text", C.c_int32),
                 ("n_audio", C.c_int32), ("rope_t", C.c_int32), ("rope_h", C.c_int32), ("rope_w", C.c_int32),
-                ("rope_theta", C.c_float)]
+                ("rope_theta", C.c_float), ("mod_sets", C.c_int32)]
 
 
 class BlockW(C.Structure):
@@ -121,7 +121,8 @@ def dims_of(w, n_tokens=None) -> Dims:
 
 def layout_of(w) -> Layout:
     st, sh, sw = w.split
-    return Layout(w.video_t, w.video_h, w.video_w, w.n_text, w.n_audio, st, sh, sw, w.rope_theta)
+    return Layout(w.video_t, w.video_h, w.video_w, w.n_text, w.n_audio, st, sh, sw, w.rope_theta,
+                  getattr(w, "mod_sets", 1))
 
 
 def ldv(n: int) -> int:

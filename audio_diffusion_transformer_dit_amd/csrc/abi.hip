@@ -47,6 +47,7 @@ int check_dims(const h3dit_dims *D, const h3dit_layout *L, int precision) {
   if (L->rope_t < 0 || L->rope_h < 0 || L->rope_w < 0 || (L->rope_t | L->rope_h | L->rope_w) & 1 ||
       L->rope_t + L->rope_h + L->rope_w != D->head_dim || !(L->rope_theta > 0.0f))
     return H3DIT_EINVAL;
+  if (L->mod_sets != 0 && L->mod_sets != 1 && L->mod_sets != 3) return H3DIT_EINVAL;
   // 32-bit buffer offsets inside the kernels
   if ((int64_t)D->n_tokens * D->mlp * 2 >= ((int64_t)1 << 31)) return H3DIT_EINVAL;
   return H3DIT_OK;
@@ -171,12 +172,21 @@ Plan make_plan(const h3dit_dims &D, const h3dit_layout &L, int precision, uint32
 
 struct Ctx {
   const h3dit_dims *D;
+  const h3dit_layout *L;
   uint32_t flags;
   uint8_t *ws;
   Plan P;
   hipStream_t st;
   template <class T>
   T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
+  // row kernel on n rows (the full or the paired sequence), with the modulation set of each
+  // row's segment: video rows first, then text, then audio
+  hipError_t row(int64_t n, const uint16_t *x, const uint16_t *gate, const uint16_t *y, uint16_t *x_out,
+                 const uint16_t *shift, const uint16_t *scale, uint16_t *h, int8_t *q, float *s) const {
+    const int64_t seg1 = n - L->n_text - L->n_audio, seg2 = seg1 + L->n_text;
+    const int64_t stride = L->mod_sets == 3 ? 6 * (int64_t)D->hidden : 0;
+    return launch_row(n, D->hidden, D->ln_eps, x, gate, y, x_out, shift, scale, h, q, s, st, seg1, seg2, stride);
+  }
 };
 
 // AdaLN (with optional gate) producing the projection input of the next GEMM: bf16 into
@@ -185,12 +195,11 @@ int adaln_into(const Ctx &c, int64_t n, const uint16_t *x, const uint16_t *gate,
                const uint16_t *shift, const uint16_t *scale, bool i8, size_t dst) {
   const int d = c.D->hidden;
   if (!i8) {
-    TRY(launch_row(n, d, c.D->ln_eps, x, gate, y, x_out, shift, scale, c.at<uint16_t>(dst), nullptr, nullptr, c.st));
+    TRY(c.row(n, x, gate, y, x_out, shift, scale, c.at<uint16_t>(dst), nullptr, nullptr));
   } else if (!(c.flags & H3DIT_NOFUSE_QUANT)) {
-    TRY(launch_row(n, d, c.D->ln_eps, x, gate, y, x_out, shift, scale, nullptr, c.at<int8_t>(dst), c.at<float>(c.P.sa),
-                   c.st));
+    TRY(c.row(n, x, gate, y, x_out, shift, scale, nullptr, c.at<int8_t>(dst), c.at<float>(c.P.sa)));
   } else {
-    TRY(launch_row(n, d, c.D->ln_eps, x, gate, y, x_out, shift, scale, c.at<uint16_t>(c.P.hb), nullptr, nullptr, c.st));
+    TRY(c.row(n, x, gate, y, x_out, shift, scale, c.at<uint16_t>(c.P.hb), nullptr, nullptr));
     TRY(launch_quant_rows(n, d, d, c.at<uint16_t>(c.P.hb), 0, c.at<int8_t>(dst), c.at<float>(c.P.sa), c.st));
   }
   return H3DIT_OK;
@@ -257,7 +266,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
   if (!(F & H3DIT_NOFUSE_GATE_ADALN)) {
     if ((rc = adaln_into(c, n, x, g1, c.at<uint16_t>(P.y1), x, sh2, sc2, i8, P.h2)) != H3DIT_OK) return rc;
   } else {
-    TRY(launch_row(n, d, D.ln_eps, x, g1, c.at<uint16_t>(P.y1), x, nullptr, nullptr, nullptr, nullptr, nullptr, c.st));
+    TRY(c.row(n, x, g1, c.at<uint16_t>(P.y1), x, nullptr, nullptr, nullptr, nullptr, nullptr));
     if ((rc = adaln_into(c, n, x, nullptr, nullptr, nullptr, sh2, sc2, i8, P.h2)) != H3DIT_OK) return rc;
   }
 
@@ -294,7 +303,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
     if ((rc = adaln_into(c, n, x, g2, c.at<uint16_t>(P.y2), x, next->mod, next->mod + d, ni8, P.h1)) != H3DIT_OK)
       return rc;
   } else {
-    TRY(launch_row(n, d, D.ln_eps, x, g2, c.at<uint16_t>(P.y2), x, nullptr, nullptr, nullptr, nullptr, nullptr, c.st));
+    TRY(c.row(n, x, g2, c.at<uint16_t>(P.y2), x, nullptr, nullptr, nullptr, nullptr, nullptr));
   }
   return H3DIT_OK;
 }
@@ -341,7 +350,7 @@ int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3
   if (rc) return rc;
   if ((rc = check_block(blk, blk->precision))) return rc;
   if ((rc = check_device())) return rc;
-  Ctx c{dims, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
+  Ctx c{dims, layout, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
   float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
   TRY(launch_rope_tables(*layout, dims->head_dim, 0, cf, sf, c.st));
   return run_block(c, dims->n_tokens, cf, sf, *blk, x, false, nullptr);
@@ -361,7 +370,7 @@ int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t 
   for (int32_t b = 0; b < n_blocks; b++)
     if ((rc = check_block(&blocks[b], precision))) return rc;
   if ((rc = check_device())) return rc;
-  Ctx c{dims, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
+  Ctx c{dims, layout, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
   float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
   float *cr = nullptr, *sr = nullptr;
   TRY(launch_rope_tables(*layout, dims->head_dim, 0, cf, sf, c.st));

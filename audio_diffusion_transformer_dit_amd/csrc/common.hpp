@@ -107,9 +107,11 @@ namespace h3 {
 
 hipError_t launch_rope_tables(const h3dit_layout &L, int hd, int reduced, float *cos_t, float *sin_t,
                               hipStream_t st);
+// one modulation set (seg1 = seg2 = n, set_stride = 0), or three sets by row segment
 hipError_t launch_row(int64_t n, int d, float eps, const uint16_t *x, const uint16_t *gate,
                       const uint16_t *y, uint16_t *x_out, const uint16_t *shift, const uint16_t *scale,
-                      uint16_t *h, int8_t *q, float *s, hipStream_t st);
+                      uint16_t *h, int8_t *q, float *s, hipStream_t st, int64_t seg1 = 0, int64_t seg2 = 0,
+                      int64_t set_stride = 0);
 hipError_t launch_quant_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v, int hm_hd,
                              int8_t *q, float *s, hipStream_t st);
 hipError_t launch_gelu(int64_t count, const uint16_t *u, uint16_t *gl, hipStream_t st);

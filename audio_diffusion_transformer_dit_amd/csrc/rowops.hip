@@ -43,15 +43,22 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 // NORM: LN of the rounded row (two passes over registers), modulation, bf16 rounding, and
 // optionally the row's int8 code.  The LN part is the same code whether or not GATE ran in
 // this kernel, so the fused and the two-kernel sequences give the same bytes.
+// Modulation sets: rows [0, seg1) use gate/shift/scale as given, rows [seg1, seg2) the vectors
+// set_stride elements further, rows from seg2 on 2*set_stride further (set_stride 0: one set).
 template <bool GATE, bool NORM>
 __global__ __launch_bounds__(ROW_THREADS) void k_row(int d, float eps, const uint16_t *__restrict__ x,
                                                      const uint16_t *__restrict__ gate,
                                                      const uint16_t *__restrict__ y, uint16_t *x_out,
                                                      const uint16_t *__restrict__ shift,
                                                      const uint16_t *__restrict__ scale, uint16_t *__restrict__ h,
-                                                     int8_t *__restrict__ q, float *__restrict__ s) {
+                                                     int8_t *__restrict__ q, float *__restrict__ s, int64_t seg1,
+                                                     int64_t seg2, int64_t set_stride) {
   __shared__ float red[ROW_THREADS / 64];
   const int64_t row = blockIdx.x;
+  const int64_t mset = (int64_t)(row >= seg1) + (int64_t)(row >= seg2);
+  gate += mset * set_stride;
+  shift += mset * set_stride;
+  scale += mset * set_stride;
   const int nch = d >> 3;
   const int tid = threadIdx.x;
   const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + row * d);
@@ -138,15 +145,17 @@ __global__ __launch_bounds__(ROW_THREADS) void k_row(int d, float eps, const uin
 
 hipError_t launch_row(int64_t n, int d, float eps, const uint16_t *x, const uint16_t *gate, const uint16_t *y,
                       uint16_t *x_out, const uint16_t *shift, const uint16_t *scale, uint16_t *h, int8_t *q,
-                      float *s, hipStream_t st) {
+                      float *s, hipStream_t st, int64_t seg1, int64_t seg2, int64_t set_stride) {
   if (n == 0) return hipSuccess;
   dim3 grid((unsigned)n), block(ROW_THREADS);
   if (gate && shift)
-    k_row<true, true><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s);
+    k_row<true, true><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s, seg1, seg2, set_stride);
   else if (gate)
-    k_row<true, false><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s);
+    k_row<true, false><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s, seg1, seg2,
+                                               set_stride);
   else
-    k_row<false, true><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s);
+    k_row<false, true><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s, seg1, seg2,
+                                               set_stride);
   return hipGetLastError();
 }
 

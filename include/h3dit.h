@@ -87,6 +87,11 @@ typedef struct {
   int32_t video_t, video_h, video_w, n_text, n_audio;
   int32_t rope_t, rope_h, rope_w;
   float rope_theta;
+  /* modulation sets in each block's `mod`: 0 or 1 = one set for every token; 3 = one set
+   * each for the video, text and audio tokens (a reading of the per-segment conditioning of
+   * [DD] "引用系统：Ref2VA 的多模态条件控制"; in the paired span the video segment is the
+   * paired video tokens) */
+  int32_t mod_sets;
 } h3dit_layout;
 
 /* One block's parameters (device pointers).
@@ -94,8 +99,8 @@ typedef struct {
  *   [d][d], [mlp][d], [d][mlp]; s_* unused.
  * precision H3DIT_INT8: w_* are int8 codes of the same shapes and s_* fp32 per-output-row
  *   scales, as written by h3dit_quantize_weights.
- * mod: bf16 [6][d] modulation rows shift1, scale1, gate1, shift2, scale2, gate2, broadcast
- *   over tokens ([DD] AdaLN branches are precomputable per block). */
+ * mod: bf16 [mod_sets][6][d] modulation rows shift1, scale1, gate1, shift2, scale2, gate2 per
+ *   set, each set broadcast over its tokens ([DD] AdaLN branches are precomputable per block). */
 typedef struct {
   int32_t precision;
   const void *w_qkv, *w_o, *w_fc1, *w_fc2;

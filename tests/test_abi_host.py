@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported():
 
 def test_struct_sizes_match_header_layout():
     assert C.sizeof(h3.Dims) == 28
-    assert C.sizeof(h3.Layout) == 36
+    assert C.sizeof(h3.Layout) == 40
     assert C.sizeof(h3.BlockW) == 8 + 9 * 8
     assert C.sizeof(h3.TokenReduction) == 8
     assert C.sizeof(h3.LinearArgs) == 160   # 14 pointer-sized / int64 fields + 4 int32 pairs + 2 padded int32
@@ -204,3 +204,14 @@ def test_int8_row_level_fc2_group_accepted():
         rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(h3.layout_of(w)), C.byref(blk), None, 0, None,
                                       C.byref(size), None)
         assert (rc == 0) == ok, g
+
+
+def test_mod_sets_validated():
+    w = WORKLOADS[1]
+    size = C.c_size_t(0)
+    for m, ok in ((0, True), (1, True), (3, True), (2, False), (6, False)):
+        lay = h3.layout_of(w)
+        lay.mod_sets = m
+        rc = h3.lib().h3dit_block_fwd(C.byref(h3.dims_of(w)), C.byref(lay), C.byref(fake_block()), None, 0, None,
+                                      C.byref(size), None)
+        assert (rc == 0) == ok, m

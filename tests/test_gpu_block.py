@@ -203,3 +203,53 @@ def test_stack_reduction_restore_after_last_block():
     h3.stack_fwd(SMALL_TR, pg, xg, reduction=(0, 40))
     ref = oracle.stack_fwd(SMALL_TR, ps, x, reduce_after=0, restore_before=40, fused=True)
     check_residual(cpu(xg), ref, x)
+
+
+# ----------------------------------------------------------------------------- modulation sets
+
+def _text_gates_zero(p, d):
+    p = dict(p)
+    mod = p["mod"].clone()
+    mod[6 + 2] = 0
+    mod[6 + 5] = 0
+    p["mod"] = mod
+    return p
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_block_mod_sets_match_oracle(int8):
+    """Three modulation sets (video, text, audio): against the oracle; three equal sets give
+    the one-set bytes; zero gates in the text set leave exactly the text rows unchanged."""
+    w = RAGGED.replace(mod_sets=3)
+    x, ps = inputs(w)
+    pg = gpu_params(ps, int8)[0]
+    xg = x.to(DEV)
+    h3.block_fwd(w, pg, xg)
+    check_residual(cpu(xg), oracle.block_fwd(w, cpu_params(ps, int8)[0], x), x)
+    # equal sets == one set
+    one = dict(ps[0])
+    one["mod"] = ps[0]["mod"][:6].contiguous()
+    three = dict(ps[0])
+    three["mod"] = one["mod"].repeat(3, 1).contiguous()
+    a, b = x.to(DEV), x.to(DEV)
+    h3.block_fwd(RAGGED, gpu_params([one], int8)[0], a)
+    h3.block_fwd(w, gpu_params([three], int8)[0], b)
+    assert_bitexact(cpu(b), cpu(a), "three equal sets")
+    # text rows pass through with zero text gates
+    z = x.to(DEV)
+    h3.block_fwd(w, gpu_params([_text_gates_zero(ps[0], w.hidden)], int8)[0], z)
+    nv, nt = w.n_video, w.n_text
+    zc = cpu(z)
+    assert_bitexact(zc[nv:nv + nt], x[nv:nv + nt], "text rows")
+    assert not torch.equal(zc[:nv].view(torch.int16), x[:nv].view(torch.int16))
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_stack_mod_sets_token_reduction_matches_oracle(int8):
+    w = SMALL_TR.replace(mod_sets=3)
+    x, ps = inputs(w, blocks=6)
+    pg = gpu_params(ps, int8)
+    xg = x.to(DEV)
+    h3.stack_fwd(w, pg, xg, reduction=(1, 4))
+    ref = oracle.stack_fwd(w, cpu_params(ps, int8), x, reduce_after=1, restore_before=4, fused=True)
+    check_residual(cpu(xg), ref, x)
