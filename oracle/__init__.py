@@ -230,7 +230,7 @@ def token_restore(w, bypass, y, r_in):
 def _block_struct(p: dict, keep: list) -> Block:
     """p: bf16 weights {wqkv, wo, w1, w2, mod} and, for int8, {qqkv, sqkv, qo, so, q1, s1, q2, s2}."""
     b = Block()
-    b.int8 = 1 if "qqkv" in p else 0
+    b.int8 = 1 if "qqkv" in p else (2 if "q1" in p else 0)
     b.mod_sets = p["mod"].shape[0] // 6
     for name in ("wqkv", "wo", "w1", "w2", "qqkv", "qo", "q1", "q2", "sqkv", "so", "s1", "s2", "mod"):
         t = p.get(name)
@@ -241,10 +241,12 @@ def _block_struct(p: dict, keep: list) -> Block:
     return b
 
 
-def quantize_block(p: dict) -> dict:
-    """Adds the int8 codes and scales of the four weight matrices to a bf16 block dict."""
+def quantize_block(p: dict, mlp_only: bool = False) -> dict:
+    """Adds the int8 codes and scales of the four weight matrices (or of FC1 and FC2 only, the
+    "int8 MLP" row of the pages' table) to a bf16 block dict."""
     out = dict(p)
-    for w, q, s in (("wqkv", "qqkv", "sqkv"), ("wo", "qo", "so"), ("w1", "q1", "s1"), ("w2", "q2", "s2")):
+    pairs = (("wqkv", "qqkv", "sqkv"), ("wo", "qo", "so"), ("w1", "q1", "s1"), ("w2", "q2", "s2"))
+    for w, q, s in (pairs[2:] if mlp_only else pairs):
         out[q], out[s] = quantize_weights(p[w])
     return out
 

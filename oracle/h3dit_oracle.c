@@ -513,7 +513,9 @@ static int32_t block_body(const orc_dims *D, const orc_block *B, const float *co
                           uint16_t *h1_next, int32_t fused, orc_taps *T) {
   int64_t N = D->n_tokens;
   int32_t d = D->hidden, H = D->heads, hd = D->head_dim, f = D->mlp;
-  if (d != H * hd || N <= 0 || f <= 0 || (B->int8 && (D->fc2_group <= 0 || f % D->fc2_group)))
+  const int32_t i8_attn = B->int8 == 1, i8_mlp = B->int8 == 1 || B->int8 == 2;
+  if (d != H * hd || N <= 0 || f <= 0 || B->int8 < 0 || B->int8 > 2 ||
+      (i8_mlp && (D->fc2_group <= 0 || f % D->fc2_group)))
     return -1;
   if (D->n_video < 0 || D->n_text < 0 || (int64_t)D->n_video + D->n_text > N || (B->mod_sets != 1 && B->mod_sets != 3))
     return -1;
@@ -536,7 +538,7 @@ static int32_t block_body(const orc_dims *D, const orc_block *B, const float *co
     }
   }
   /* QKV projection, rotary, head split */
-  project(N, 3 * d, d, h1, B->int8, B->wqkv, B->qqkv, B->sqkv, t);
+  project(N, 3 * d, d, h1, i8_attn, B->wqkv, B->qqkv, B->sqkv, t);
   orc_rope_split(N, d, H, hd, t, cosv, sinv, q, k, v);
   /* attention, then the head-major output read as [N][d] (column h*hd + i) */
   orc_attention(H, N, N, hd, q, k, v, o, T ? T->att_max : NULL, T ? T->att_sum : NULL);
@@ -544,7 +546,7 @@ static int32_t block_body(const orc_dims *D, const orc_block *B, const float *co
     for (int32_t h = 0; h < H; h++)
       memcpy(ot + n * d + h * hd, o + ((int64_t)h * N + n) * hd, 2 * (size_t)hd);
   /* output projection */
-  project(N, d, d, ot, B->int8, B->wo, B->qo, B->so, y1);
+  project(N, d, d, ot, i8_attn, B->wo, B->qo, B->so, y1);
   /* gate1 (x1 = x + g1 y1) then AdaLN2 (shift2, scale2) of the rounded x1 */
   for (int32_t sg = 0; sg < 3; sg++) {
     int64_t r0, r1;
@@ -554,10 +556,10 @@ static int32_t block_body(const orc_dims *D, const orc_block *B, const float *co
                       mod_vec(B, d, sg, 3), mod_vec(B, d, sg, 4), h2 + r0 * d, fused);
   }
   /* FC1, GELU */
-  project(N, f, d, h2, B->int8, B->w1, B->q1, B->s1, u);
+  project(N, f, d, h2, i8_mlp, B->w1, B->q1, B->s1, u);
   orc_gelu_rows((int64_t)Nf, u, gl);
   /* FC2 */
-  if (!B->int8) {
+  if (!i8_mlp) {
     project(N, d, f, gl, 0, B->w2, NULL, NULL, y2);
   } else {
     int64_t ng = f / D->fc2_group;

@@ -36,7 +36,8 @@ typedef struct {
 } orc_layout;
 
 typedef struct {
-  int32_t int8;                         /* 0: bf16 weights; 1: int8 weights + per-row scales */
+  int32_t int8;                         /* int8 projections ([DD] "int8 量化" table rows): 0 none
+                                           (bf16); 1 all four; 2 FC1 and FC2 only ("int8 MLP") */
   const uint16_t *wqkv, *wo, *w1, *w2;  /* bf16 [3d][d], [d][d], [f][d], [d][f] */
   const int8_t *qqkv, *qo, *q1, *q2;    /* int8, same shapes */
   const float *sqkv, *so, *s1, *s2;     /* fp32 per output row */

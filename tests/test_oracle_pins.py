@@ -656,3 +656,24 @@ def test_mod_sets_in_a_reduced_stack():
     nv, nt = w3.n_video, w3.n_text
     assert torch.equal(c[nv:nv + nt].view(torch.int16), x[nv:nv + nt].view(torch.int16))
     assert not torch.equal(c[:nv].view(torch.int16), x[:nv].view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- int8 MLP only
+
+def test_int8_mlp_only_block():
+    """FC1 and FC2 in int8, QKV and the output projection in bf16: every stage up to the MLP
+    input is the bf16 block's, bytewise; FC1 is the int8 projection of that input."""
+    x, p = _tiny_inputs()
+    pm = oracle.quantize_block(p, mlp_only=True)
+    assert "q1" in pm and "qqkv" not in pm
+    _, ta = oracle.block_fwd(W0, p, x, taps=True)
+    out, tm = oracle.block_fwd(W0, pm, x, taps=True)
+    for name in ("h1", "t", "q", "k", "v", "o", "y1", "x1", "h2"):
+        assert torch.equal(tm[name].view(torch.int16), ta[name].view(torch.int16)), name
+    qa, sa = oracle.q8_rows(tm["h2"])
+    u = oracle.dequant_bf16(oracle.gemm_i32(qa, pm["q1"]), sa[:, 0].contiguous(), pm["s1"])
+    assert torch.equal(tm["u"].view(torch.int16), u.view(torch.int16))
+    assert not torch.equal(tm["u"].view(torch.int16), ta["u"].view(torch.int16))
+    # and the whole int8 block differs from it already in the attention branch
+    _, t8 = oracle.block_fwd(W0, oracle.quantize_block(p), x, taps=True)
+    assert not torch.equal(t8["t"].view(torch.int16), ta["t"].view(torch.int16))
