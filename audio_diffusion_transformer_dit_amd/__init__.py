@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
-BF16, INT8 = 0, 1
+BF16, INT8, INT8_MLP = 0, 1, 2
 NOFUSE_GATE_ADALN, NOFUSE_ROPE, NOFUSE_GELU, NOFUSE_QUANT, NOFUSE_CROSS_BLOCK, NO_ALIAS = 1, 2, 4, 8, 16, 32
 OUT_BF16, OUT_F32, OUT_I32, OUT_GELU, OUT_QKV = 0, 1, 2, 3, 4
 
@@ -161,18 +161,26 @@ def quantize_weights(w: torch.Tensor, stream=None):
 
 
 def block_struct(p: dict) -> BlockW:
-    """p: {wqkv, wo, w1, w2, mod} bf16 device tensors, or int8 codes {qqkv, qo, q1, q2} with
-    scales {sqkv, so, s1, s2} and mod."""
+    """p: {wqkv, wo, w1, w2, mod} bf16 device tensors; or int8 codes {qqkv, qo, q1, q2} with
+    scales {sqkv, so, s1, s2} and mod; or bf16 {wqkv, wo} with int8 {q1, q2, s1, s2} (int8 MLP)."""
     if "qqkv" in p:
         return BlockW(INT8, _ptr(p["qqkv"]), _ptr(p["qo"]), _ptr(p["q1"]), _ptr(p["q2"]), _ptr(p["sqkv"]),
                       _ptr(p["so"]), _ptr(p["s1"]), _ptr(p["s2"]), _ptr(p["mod"]))
+    if "q1" in p:
+        return BlockW(INT8_MLP, _ptr(p["wqkv"]), _ptr(p["wo"]), _ptr(p["q1"]), _ptr(p["q2"]), None, None,
+                      _ptr(p["s1"]), _ptr(p["s2"]), _ptr(p["mod"]))
     return BlockW(BF16, _ptr(p["wqkv"]), _ptr(p["wo"]), _ptr(p["w1"]), _ptr(p["w2"]), None, None, None, None,
                   _ptr(p["mod"]))
 
 
-def quantize_block(p: dict, stream=None) -> dict:
+def quantize_block(p: dict, stream=None, mlp_only: bool = False) -> dict:
+    """int8 codes of the four projections, or (mlp_only) of FC1 and FC2 with QKV and the
+    output projection kept in bf16."""
     out = {"mod": p["mod"]}
-    for w, q, s in (("wqkv", "qqkv", "sqkv"), ("wo", "qo", "so"), ("w1", "q1", "s1"), ("w2", "q2", "s2")):
+    pairs = (("wqkv", "qqkv", "sqkv"), ("wo", "qo", "so"), ("w1", "q1", "s1"), ("w2", "q2", "s2"))
+    if mlp_only:
+        out["wqkv"], out["wo"] = p["wqkv"], p["wo"]
+    for w, q, s in (pairs[2:] if mlp_only else pairs):
         out[q], out[s] = quantize_weights(p[w], stream)
     return out
 

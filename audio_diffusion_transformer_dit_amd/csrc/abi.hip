@@ -34,8 +34,8 @@ int check_dims(const h3dit_dims *D, const h3dit_layout *L, int precision) {
   if (D->head_dim != 64 && D->head_dim != 128) return H3DIT_EUNSUPPORTED;
   if (D->hidden % 256 || D->hidden > 8192 || D->mlp < 256 || D->mlp % 256) return H3DIT_EINVAL;
   if (!(D->ln_eps >= 0.0f)) return H3DIT_EINVAL;
-  if (precision != H3DIT_BF16 && precision != H3DIT_INT8) return H3DIT_EINVAL;
-  if (precision == H3DIT_INT8) {
+  if (precision != H3DIT_BF16 && precision != H3DIT_INT8 && precision != H3DIT_INT8_MLP) return H3DIT_EINVAL;
+  if (precision != H3DIT_BF16) {
     // 1024-channel groups as on the pages, or one code per token over the whole FC2 input
     // (fc2_group == mlp, the row-level variant)
     if (D->fc2_group < 128 || D->fc2_group % 128 || (D->fc2_group > 8192 && D->fc2_group != D->mlp) ||
@@ -61,6 +61,10 @@ int check_block(const h3dit_block_w *b, int precision) {
   if (!b->mod || !aligned(b->mod, 16)) return H3DIT_EINVAL;
   if (precision == H3DIT_INT8) {
     const float *s[4] = {b->s_qkv, b->s_o, b->s_fc1, b->s_fc2};
+    for (const float *p : s)
+      if (!p || !aligned(p, 4)) return H3DIT_EINVAL;
+  } else if (precision == H3DIT_INT8_MLP) {
+    const float *s[2] = {b->s_fc1, b->s_fc2};
     for (const float *p : s)
       if (!p || !aligned(p, 4)) return H3DIT_EINVAL;
   }
@@ -96,31 +100,35 @@ struct Plan {
   size_t sk = 0, sk_bytes = 0;                        // split-K partial tiles of the projections
 };
 
+// Precision of the attention projections (QKV, output) and of the MLP projections.
+int attn_prec(int precision) { return precision == H3DIT_INT8 ? H3DIT_INT8 : H3DIT_BF16; }
+int mlp_prec(int precision) { return precision == H3DIT_BF16 ? H3DIT_BF16 : H3DIT_INT8; }
+
 // Largest split-K workspace of the block's four projections at n tokens.
 size_t block_splitk_bytes(const h3dit_dims &D, int precision, int64_t n) {
-  const bool i8 = precision == H3DIT_INT8;
   h3dit_linear_args la{};
   la.M = n;
-  la.precision = precision;
   size_t m = 0;
-  auto take = [&](int64_t N, int64_t K, int out_kind, int group) {
+  auto take = [&](int prec, int64_t N, int64_t K, int out_kind, int group) {
+    la.precision = prec;
     la.N = N; la.K = K; la.out_kind = out_kind; la.a_group = group;
     la.heads = D.heads; la.head_dim = D.head_dim;
     const size_t b = linear_workspace(la);
     if (b > m) m = b;
   };
-  take(3 * (int64_t)D.hidden, D.hidden, H3DIT_OUT_QKV, 0);
-  take(3 * (int64_t)D.hidden, D.hidden, H3DIT_OUT_BF16, 0);
-  take(D.hidden, D.hidden, H3DIT_OUT_BF16, 0);
-  take(D.mlp, D.hidden, H3DIT_OUT_GELU, 0);
-  take(D.hidden, D.mlp, H3DIT_OUT_BF16, (i8 && D.fc2_group != D.mlp) ? D.fc2_group : 0);
+  const int pa = attn_prec(precision), pm = mlp_prec(precision);
+  take(pa, 3 * (int64_t)D.hidden, D.hidden, H3DIT_OUT_QKV, 0);
+  take(pa, 3 * (int64_t)D.hidden, D.hidden, H3DIT_OUT_BF16, 0);
+  take(pa, D.hidden, D.hidden, H3DIT_OUT_BF16, 0);
+  take(pm, D.mlp, D.hidden, H3DIT_OUT_GELU, 0);
+  take(pm, D.hidden, D.mlp, H3DIT_OUT_BF16, (pm == H3DIT_INT8 && D.fc2_group != D.mlp) ? D.fc2_group : 0);
   return m;
 }
 
 Plan make_plan(const h3dit_dims &D, const h3dit_layout &L, int precision, uint32_t flags, bool reduction) {
   const size_t N = (size_t)D.n_tokens, d = (size_t)D.hidden, f = (size_t)D.mlp, hd = (size_t)D.head_dim;
   const size_t ldv = (size_t)vt_pitch((int64_t)N);
-  const bool i8 = precision == H3DIT_INT8;
+  const bool i8 = precision != H3DIT_BF16;   // the int8 buffers (a superset for int8-MLP blocks)
   const size_t Nd2 = N * d * 2;
   Plan p;
   size_t off = 0;
@@ -211,7 +219,8 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
               bool h1_ready, const h3dit_block_w *next) {
   const h3dit_dims &D = *c.D;
   const int d = D.hidden, H = D.heads, hd = D.head_dim, f = D.mlp;
-  const bool i8 = b.precision == H3DIT_INT8;
+  const int pa = attn_prec(b.precision), pm = mlp_prec(b.precision);
+  const bool i8 = pa == H3DIT_INT8, i8m = pm == H3DIT_INT8;   // attention / MLP projections in int8
   const uint32_t F = c.flags;
   const uint16_t *mod = b.mod;
   const uint16_t *sh1 = mod, *sc1 = mod + d, *g1 = mod + 2 * d, *sh2 = mod + 3 * d, *sc2 = mod + 4 * d, *g2 = mod + 5 * d;
@@ -224,7 +233,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
   // QKV projection + rotary + head-major split
   h3dit_linear_args la{};
   la.M = n; la.N = 3 * d; la.K = d;
-  la.precision = b.precision;
+  la.precision = pa;
   la.a = c.at<void>(P.h1);
   la.a_scale = i8 ? c.at<float>(P.sa) : nullptr;
   la.w = b.w_qkv;
@@ -249,7 +258,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
 
   // output projection
   la = h3dit_linear_args{};
-  la.M = n; la.N = d; la.K = d; la.precision = b.precision; la.w = b.w_o; la.w_scale = b.s_o;
+  la.M = n; la.N = d; la.K = d; la.precision = pa; la.w = b.w_o; la.w_scale = b.s_o;
   la.out_kind = H3DIT_OUT_BF16; la.out = c.at<void>(P.y1);
   la.workspace = c.at<void>(P.sk); la.workspace_bytes = P.sk_bytes;
   if (!i8) {
@@ -264,16 +273,16 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
 
   // gate1 + AdaLN2
   if (!(F & H3DIT_NOFUSE_GATE_ADALN)) {
-    if ((rc = adaln_into(c, n, x, g1, c.at<uint16_t>(P.y1), x, sh2, sc2, i8, P.h2)) != H3DIT_OK) return rc;
+    if ((rc = adaln_into(c, n, x, g1, c.at<uint16_t>(P.y1), x, sh2, sc2, i8m, P.h2)) != H3DIT_OK) return rc;
   } else {
     TRY(c.row(n, x, g1, c.at<uint16_t>(P.y1), x, nullptr, nullptr, nullptr, nullptr, nullptr));
-    if ((rc = adaln_into(c, n, x, nullptr, nullptr, nullptr, sh2, sc2, i8, P.h2)) != H3DIT_OK) return rc;
+    if ((rc = adaln_into(c, n, x, nullptr, nullptr, nullptr, sh2, sc2, i8m, P.h2)) != H3DIT_OK) return rc;
   }
 
   // FC1 + GELU
   la = h3dit_linear_args{};
-  la.M = n; la.N = f; la.K = d; la.precision = b.precision; la.w = b.w_fc1; la.w_scale = b.s_fc1;
-  la.a = c.at<void>(P.h2); la.a_scale = i8 ? c.at<float>(P.sa) : nullptr;
+  la.M = n; la.N = f; la.K = d; la.precision = pm; la.w = b.w_fc1; la.w_scale = b.s_fc1;
+  la.a = c.at<void>(P.h2); la.a_scale = i8m ? c.at<float>(P.sa) : nullptr;
   la.out = c.at<void>(P.gl);
   la.out_kind = (F & H3DIT_NOFUSE_GELU) ? H3DIT_OUT_BF16 : H3DIT_OUT_GELU;
   la.workspace = c.at<void>(P.sk); la.workspace_bytes = P.sk_bytes;
@@ -282,10 +291,10 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
 
   // FC2
   la = h3dit_linear_args{};
-  la.M = n; la.N = d; la.K = f; la.precision = b.precision; la.w = b.w_fc2; la.w_scale = b.s_fc2;
+  la.M = n; la.N = d; la.K = f; la.precision = pm; la.w = b.w_fc2; la.w_scale = b.s_fc2;
   la.out_kind = H3DIT_OUT_BF16; la.out = c.at<void>(P.y2);
   la.workspace = c.at<void>(P.sk); la.workspace_bytes = P.sk_bytes;
-  if (!i8) {
+  if (!i8m) {
     la.a = c.at<void>(P.gl);
   } else {
     TRY(launch_quant_rows(n, f, D.fc2_group, c.at<uint16_t>(P.gl), 0, c.at<int8_t>(P.qg), c.at<float>(P.sg), c.st));
@@ -299,7 +308,7 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
 
   // gate2, optionally with the next block's AdaLN1
   if (next) {
-    const bool ni8 = next->precision == H3DIT_INT8;
+    const bool ni8 = attn_prec(next->precision) == H3DIT_INT8;
     if ((rc = adaln_into(c, n, x, g2, c.at<uint16_t>(P.y2), x, next->mod, next->mod + d, ni8, P.h1)) != H3DIT_OK)
       return rc;
   } else {

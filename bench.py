@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=3, help="workload index in synth.WORKLOADS (3 or 4)")
     ap.add_argument("--blocks", type=int, default=None, help="override the block count")
-    ap.add_argument("--no-int8", action="store_true", help="skip the int8 leg")
+    ap.add_argument("--no-int8", action="store_true", help="skip the int8 legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--only-kernels", action="store_true", help="per-kernel timing only (profiling runs)")
@@ -50,14 +50,14 @@ def parse():
     return ap.parse_args()
 
 
-def make_blocks(w, n_blocks, seed, device, int8):
+def make_blocks(w, n_blocks, seed, device, int8, mlp_only=False):
     import synth
     import audio_diffusion_transformer_dit_amd as h3
     blocks = []
     for b in range(n_blocks):
         p = synth.make_block(w, seed, b, device)
         if int8:
-            q = h3.quantize_block(p)
+            q = h3.quantize_block(p, mlp_only=mlp_only)
             del p
             p = q
         blocks.append(p)
@@ -291,6 +291,13 @@ def main():
                          "tops": round(step_flop / (ms8 / 1e3) / 1e12, 1),
                          "kernels": kernel_breakdown(w, blocks8[0], x, args.kernel_iters, True)}
         del blocks8
+        torch.cuda.empty_cache()
+        # the middle row of the pages' int8 table: FC1 and FC2 in int8, attention projections bf16
+        blocks8m = make_blocks(w, w.blocks, seed, dev, True, mlp_only=True)
+        ms8m, _, _ = time_stack(w, blocks8m, x, args.steps, args.warmup, red)
+        extra["int8_mlp_only"] = {"ms_per_step": round(ms8m, 3), "ms_per_block": round(ms8m / w.blocks, 3),
+                                  "tflops_equiv": round(step_flop / (ms8m / 1e3) / 1e12, 1)}
+        del blocks8m
         torch.cuda.empty_cache()
 
     line = {

@@ -53,6 +53,7 @@ extern "C" {
 
 #define H3DIT_BF16 0
 #define H3DIT_INT8 1
+#define H3DIT_INT8_MLP 2   /* FC1 and FC2 in int8, QKV and output projection in bf16 */
 
 /* Fusion switches ([DD] "DiT 融合内核": every fusion can be turned back into its step-wise
  * form for a byte-identical A/B).  Each flag selects the unfused sequence; the results are
@@ -99,6 +100,9 @@ typedef struct {
  *   [d][d], [mlp][d], [d][mlp]; s_* unused.
  * precision H3DIT_INT8: w_* are int8 codes of the same shapes and s_* fp32 per-output-row
  *   scales, as written by h3dit_quantize_weights.
+ * precision H3DIT_INT8_MLP ([DD] "int8 量化", the table's int8-MLP row): w_qkv, w_o bf16 as
+ *   in H3DIT_BF16; w_fc1, w_fc2 int8 codes with s_fc1, s_fc2.  Every block of a stack has the
+ *   same precision.
  * mod: bf16 [mod_sets][6][d] modulation rows shift1, scale1, gate1, shift2, scale2, gate2 per
  *   set, each set broadcast over its tokens ([DD] AdaLN branches are precomputable per block). */
 typedef struct {

@@ -253,3 +253,33 @@ def test_stack_mod_sets_token_reduction_matches_oracle(int8):
     h3.stack_fwd(w, pg, xg, reduction=(1, 4))
     ref = oracle.stack_fwd(w, cpu_params(ps, int8), x, reduce_after=1, restore_before=4, fused=True)
     check_residual(cpu(xg), ref, x)
+
+
+# ----------------------------------------------------------------------------- int8 MLP only
+
+def test_block_int8_mlp_only_matches_oracle():
+    """FC1 and FC2 in int8, QKV and output projection in bf16 (the pages' int8-MLP row)."""
+    x, ps = inputs(RAGGED)
+    pg = h3.quantize_block(dev_block(ps[0]), mlp_only=True)
+    pc = oracle.quantize_block(ps[0], mlp_only=True)
+    for k in ("q1", "s1", "q2", "s2"):
+        assert_bitexact(cpu(pg[k]), pc[k], k)
+    xg = x.to(DEV)
+    h3.block_fwd(RAGGED, pg, xg)
+    check_residual(cpu(xg), oracle.block_fwd(RAGGED, pc, x), x)
+    # the fusion switches stay byte-identical on this path too
+    for f in (h3.NOFUSE_GATE_ADALN, h3.NOFUSE_QUANT, h3.NO_ALIAS):
+        y = x.to(DEV)
+        h3.block_fwd(RAGGED, pg, y, flags=f)
+        assert_bitexact(cpu(y), cpu(xg), f"flags {f}")
+
+
+def test_stack_int8_mlp_only_token_reduction():
+    w = SMALL_TR
+    x, ps = inputs(w, blocks=5)
+    pg = [h3.quantize_block(dev_block(p), mlp_only=True) for p in ps]
+    pc = [oracle.quantize_block(p, mlp_only=True) for p in ps]
+    xg = x.to(DEV)
+    h3.stack_fwd(w, pg, xg, reduction=(1, 3))
+    ref = oracle.stack_fwd(w, pc, x, reduce_after=1, restore_before=3, fused=True)
+    check_residual(cpu(xg), ref, x)
