@@ -153,6 +153,20 @@ def kernel_breakdown(w, p, x, iters, int8):
                             2.0 * N * f * d, 0),
             "gate": (lambda: h3.row_gate_adaln(x1, gate=mod[5], y=y2, x_out=x2), 0, 6.0 * N * d),
         }
+    if w.reduce_after >= 0:
+        # token pair / restore ([DD] "Token 缩减"): unique bytes moved
+        rows, W = w.video_t * w.video_h, w.video_w
+        rest = w.n_text + w.n_audio
+        n_full = rows * W + rest
+        n_red = rows * (W // 2 + W % 2) + rest
+        paired = rows * (W // 2) * 2
+        xr = x[:n_full].clone()
+        red = torch.empty((n_red, d), **bf)
+        r_in = torch.zeros((n_red, d), **bf)
+        yred = torch.zeros((n_red, d), **bf)
+        ops["token_pair"] = (lambda: h3.token_pair(w, xr, red, r_in), 0, 2.0 * d * (n_full + 2 * n_red))
+        ops["token_restore"] = (lambda: h3.token_restore(w, xr, yred, r_in), 0,
+                                2.0 * d * (paired + n_full + n_red + paired // 2))
     # one pass in order so that every kernel reads realistic data
     for fn, _, _ in ops.values():
         fn()
