@@ -433,8 +433,10 @@ int h3dit_rope_tables(const h3dit_layout *L, int32_t head_dim, int32_t reduced, 
 int h3dit_row_gate_adaln(int64_t n, int32_t d, float eps, const uint16_t *x, const uint16_t *gate, const uint16_t *y,
                          uint16_t *x_out, const uint16_t *shift, const uint16_t *scale, uint16_t *h, int8_t *q,
                          float *s, void *stream) {
-  if (n < 0 || d < 8 || d % 8 || d > 8192 || !x || !aligned(x, 16)) return H3DIT_EINVAL;
+  if (n < 0 || d < 8 || d % 8 || d > 8192) return H3DIT_EINVAL;
   if (!gate && !shift) return H3DIT_EINVAL;
+  if (n == 0) return H3DIT_OK;   // nothing to do: pointers are not examined
+  if (!x || !aligned(x, 16)) return H3DIT_EINVAL;
   if (gate && (!y || !x_out || !aligned(gate, 16) || !aligned(y, 16) || !aligned(x_out, 16))) return H3DIT_EINVAL;
   if (shift && (!scale || !aligned(shift, 16) || !aligned(scale, 16))) return H3DIT_EINVAL;
   if (shift && !h && !q) return H3DIT_EINVAL;
@@ -451,6 +453,7 @@ int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, const uint16_
   if (rows < 0 || cols < 8 || group < 8 || group % 8 || cols % group || rows > INT32_MAX) return H3DIT_EINVAL;
   if (headmajor_hd < 0 || (headmajor_hd > 0 && (headmajor_hd % 8 || cols % headmajor_hd || group > 8192)))
     return H3DIT_EINVAL;
+  if (rows == 0) return H3DIT_OK;
   if (!v || !q || !s || !aligned(v, 16) || !aligned(q, 8) || !aligned(s, 4)) return H3DIT_EINVAL;
   int rc = check_device();
   if (rc) return rc;
@@ -460,6 +463,7 @@ int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, const uint16_
 
 static int check_linear(const h3dit_linear_args *a) {
   if (!a || a->M < 0 || a->N < 128 || a->N % 128 || a->K < 128 || a->K % 128) return H3DIT_EINVAL;
+  if (a->M == 0) return H3DIT_OK;   // nothing to do: pointers are not examined
   if (!a->a || !a->w || !aligned(a->a, 16) || !aligned(a->w, 16)) return H3DIT_EINVAL;
   const bool i8 = a->precision == H3DIT_INT8;
   if (!i8 && a->precision != H3DIT_BF16) return H3DIT_EINVAL;
@@ -500,6 +504,7 @@ int h3dit_linear_workspace(const h3dit_linear_args *a, uint64_t *bytes) {
 int h3dit_linear(const h3dit_linear_args *a, void *stream) {
   int rc = check_linear(a);
   if (rc) return rc;
+  if (a->M == 0) return H3DIT_OK;
   const size_t need = linear_workspace(*a);
   if (need && (!a->workspace || a->workspace_bytes < need)) return H3DIT_EWORKSPACE;
   if ((rc = check_device())) return rc;
@@ -510,6 +515,7 @@ int h3dit_linear(const h3dit_linear_args *a, void *stream) {
 int h3dit_rope_split(int64_t n, int32_t heads, int32_t head_dim, const uint16_t *t, const float *cos_t,
                      const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *vt, void *stream) {
   if (n < 0 || heads < 1 || (head_dim != 64 && head_dim != 128)) return H3DIT_EINVAL;
+  if (n == 0) return H3DIT_OK;
   if (!t || !cos_t || !sin_t || !q || !k || !vt || !aligned(t, 16) || !aligned(q, 16) || !aligned(k, 16))
     return H3DIT_EINVAL;
   int rc = check_device();
@@ -519,7 +525,9 @@ int h3dit_rope_split(int64_t n, int32_t heads, int32_t head_dim, const uint16_t 
 }
 
 int h3dit_gelu(int64_t count, const uint16_t *u, uint16_t *gl, void *stream) {
-  if (count < 0 || count % 8 || !u || !gl || !aligned(u, 16) || !aligned(gl, 16)) return H3DIT_EINVAL;
+  if (count < 0 || count % 8) return H3DIT_EINVAL;
+  if (count == 0) return H3DIT_OK;
+  if (!u || !gl || !aligned(u, 16) || !aligned(gl, 16)) return H3DIT_EINVAL;
   int rc = check_device();
   if (rc) return rc;
   TRY(launch_gelu(count, u, gl, (hipStream_t)stream));
@@ -529,6 +537,7 @@ int h3dit_gelu(int64_t count, const uint16_t *u, uint16_t *gl, void *stream) {
 int h3dit_attention(int32_t heads, int64_t n, int32_t head_dim, const uint16_t *q, const uint16_t *k,
                     const uint16_t *vt, uint16_t *o, float *row_max, float *row_sum, void *stream) {
   if (heads < 1 || n < 0 || (head_dim != 64 && head_dim != 128)) return H3DIT_EINVAL;
+  if (n == 0) return H3DIT_OK;
   if (!q || !k || !vt || !o || !aligned(q, 16) || !aligned(k, 16) || !aligned(vt, 16) || !aligned(o, 16))
     return H3DIT_EINVAL;
   if ((row_max == nullptr) != (row_sum == nullptr)) return H3DIT_EINVAL;

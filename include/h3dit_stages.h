@@ -4,7 +4,9 @@
  * These expose each kernel the block and stack calls are built from, so that every stage
  * can be checked on its own and timed on its own.  The rules of h3dit.h apply (device
  * pointers, 16-byte alignment, caller-owned memory, asynchronous on `stream`, validation
- * before launch, negative status on error).  Source abbreviations [RV], [DD] as in h3dit.h.
+ * before launch, negative status on error).  A call with nothing to do (zero rows, tokens or
+ * elements) checks its sizes, returns H3DIT_OK and does not examine its pointers.  Source
+ * abbreviations [RV], [DD], [NS] as in h3dit.h.
  *
  * Layouts used below:
  *   token-major  [n][d]       row n holds the d features of token n

@@ -215,3 +215,18 @@ def test_mod_sets_validated():
         rc = h3.lib().h3dit_block_fwd(C.byref(h3.dims_of(w)), C.byref(lay), C.byref(fake_block()), None, 0, None,
                                       C.byref(size), None)
         assert (rc == 0) == ok, m
+
+
+def test_zero_sized_stage_calls_return_ok_without_pointers():
+    lib = h3.lib()
+    assert lib.h3dit_row_gate_adaln(0, 256, 1e-6, None, None, None, None, 1 << 20, 1 << 20, None, None, None,
+                                    None) == 0
+    assert lib.h3dit_quantize_rows(0, 256, 256, None, 0, None, None, None) == 0
+    assert lib.h3dit_attention(2, 0, 128, None, None, None, None, None, None, None) == 0
+    assert lib.h3dit_gelu(0, None, None, None) == 0
+    assert lib.h3dit_rope_split(0, 2, 64, None, None, None, None, None, None, None) == 0
+    args = h3.LinearArgs(M=0, N=128, K=128, precision=h3.BF16, out_kind=h3.OUT_BF16)
+    assert lib.h3dit_linear(C.byref(args), None) == 0
+    # sizes are still checked
+    assert lib.h3dit_row_gate_adaln(0, 100, 1e-6, None, None, None, None, 1 << 20, 1 << 20, None, None, None,
+                                    None) == h3.EINVAL

@@ -283,3 +283,33 @@ def test_stack_int8_mlp_only_token_reduction():
     h3.stack_fwd(w, pg, xg, reduction=(1, 3))
     ref = oracle.stack_fwd(w, pc, x, reduce_after=1, restore_before=3, fused=True)
     check_residual(cpu(xg), ref, x)
+
+
+# ----------------------------------------------------------------------------- limits
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_block_maximum_hidden_width(int8):
+    """hidden 8192 (64 heads x 128), the widest row the row kernels hold, against the oracle."""
+    w = W0.replace(hidden=8192, heads=64, head_dim=128, mlp=8192, fc2_group=1024,
+                   video_t=1, video_h=4, video_w=20, n_text=12, n_audio=4)
+    assert w.n_tokens == 96
+    x, ps = inputs(w)
+    pg = gpu_params(ps, int8)[0]
+    xg = x.to(DEV)
+    h3.block_fwd(w, pg, xg)
+    check_residual(cpu(xg), oracle.block_fwd(w, cpu_params(ps, int8)[0], x), x)
+
+
+def test_zero_sized_stage_calls_touch_nothing():
+    """n = 0 / M = 0 stage calls return OK and leave their outputs alone."""
+    d = 256
+    x = torch.randn((4, d), device=DEV).to(torch.bfloat16)
+    sentinel = torch.full((4, d), 7.0, device=DEV, dtype=torch.bfloat16)
+    mod = torch.zeros((6, d), device=DEV, dtype=torch.bfloat16)
+    h3.row_gate_adaln(x[:0], gate=mod[2], y=x[:0], x_out=sentinel[:0], shift=mod[3], scale=mod[4], h=sentinel[:0])
+    w = torch.randn((256, d), device=DEV).to(torch.bfloat16)
+    h3.linear(0, 256, d, x, w, h3.OUT_BF16, sentinel)
+    q = torch.zeros((2, 1, 128), device=DEV, dtype=torch.bfloat16)
+    h3.attention(2, 0, 128, q, q, torch.zeros((2, 128, 16), device=DEV, dtype=torch.bfloat16), sentinel)
+    torch.cuda.synchronize()
+    assert bool((sentinel.float() == 7.0).all())
