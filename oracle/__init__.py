@@ -225,6 +225,26 @@ def token_restore(w, bypass, y, r_in):
     return x
 
 
+def final_head(w, x, video=None, audio=None):
+    """The final head on the video rows [0, n_video) and the audio rows (the last n_audio) of
+    the residual x: each part is (mod bf16 [2][d] = shift, scale; W bf16 [c][d]); returns
+    (out_video [n_video][c_v] or None, out_audio [n_audio][c_a] or None)."""
+    n_video = x.shape[0] - w.n_text - w.n_audio
+    outs = []
+    for part, r0, n in ((video, 0, n_video), (audio, x.shape[0] - w.n_audio, w.n_audio)):
+        if part is None:
+            outs.append(None)
+            continue
+        mod, wt = part
+        c = wt.shape[0]
+        out = bf16((n, c))
+        xs = x[r0:r0 + n].contiguous()
+        lib().orc_final_head(_i64(n), C.c_int32(w.hidden), C.c_int32(c), C.c_float(w.ln_eps), _p(xs),
+                             _p(mod[0].contiguous()), _p(mod[1].contiguous()), _p(wt.contiguous()), _p(out))
+        outs.append(out)
+    return tuple(outs)
+
+
 # ------------------------------------------------------------------ block and stack
 
 def _block_struct(p: dict, keep: list) -> Block:

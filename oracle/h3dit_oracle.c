@@ -161,6 +161,21 @@ void orc_adaln(int64_t n, int32_t d, float eps, const uint16_t *x, const uint16_
   }
 }
 
+/* Final head of one modality ([DD] "DiT 融合内核", 最终片层直接绑定: the audio and video AdaLN
+ * read their rows of the residual stream in place, and the bf16 head applies AdaLN on the way
+ * into its projection): for n residual rows x, out = bf16(h W^T) with h = AdaLN(x; shift,
+ * scale) rounded to bf16 (the rounding point of every other AdaLN), W bf16 [c][d], no bias. */
+void orc_final_head(int64_t n, int32_t d, int32_t c, float eps, const uint16_t *x, const uint16_t *shift,
+                    const uint16_t *scale, const uint16_t *w, uint16_t *out) {
+  uint16_t *h = xmalloc(2 * (size_t)n * d);
+  float *acc = xmalloc(sizeof(float) * (size_t)n * c);
+  orc_adaln(n, d, eps, x, shift, scale, h, NULL, NULL);
+  orc_gemm_f32(n, c, d, h, w, acc);
+  orc_f32_to_bf16(acc, out, n * c);
+  free(h);
+  free(acc);
+}
+
 /* ---------------------------------------------------------------- int8 */
 
 /* Symmetric int8 code of a span of bf16 values ([DD] "int8 量化"): scale = absmax / 127 by

@@ -79,6 +79,8 @@ void orc_fc2_int8(int64_t M, int64_t N, int64_t K, int64_t group, const int8_t *
                   const float *sa, const int8_t *qw, const float *sw, uint16_t *y);
 void orc_dequant_bf16(int64_t M, int64_t N, const int32_t *acc, const float *sa, const float *sw,
                       uint16_t *out);
+void orc_final_head(int64_t n, int32_t d, int32_t c, float eps, const uint16_t *x, const uint16_t *shift,
+                    const uint16_t *scale, const uint16_t *w, uint16_t *out);
 int32_t orc_token_pair(const orc_layout *L, int32_t d, const uint16_t *x, uint16_t *r);
 int32_t orc_token_restore(const orc_layout *L, int32_t d, const uint16_t *bypass,
                           const uint16_t *y, const uint16_t *r_in, uint16_t *x);

@@ -677,3 +677,48 @@ def test_int8_mlp_only_block():
     # and the whole int8 block differs from it already in the attention branch
     _, t8 = oracle.block_fwd(W0, oracle.quantize_block(p), x, taps=True)
     assert not torch.equal(t8["t"].view(torch.int16), ta["t"].view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- final head
+
+def test_final_head_identity_projection_is_layernorm():
+    """shift = scale = 0 and W = I: the head returns the rows' LayerNorm (<= 1 bf16 step),
+    the video rows from the front of the residual and the audio rows from its end."""
+    w = W0
+    d = w.hidden
+    x = synth.make_x(w, 1000)
+    zero = torch.zeros((2, d), dtype=torch.bfloat16)
+    eye = torch.eye(d, dtype=torch.bfloat16)
+    ov, oa = oracle.final_head(w, x, video=(zero, eye), audio=(zero, eye))
+    nv = w.n_tokens - w.n_text - w.n_audio
+    ref_v = bf(F.layer_norm(x[:nv].to(torch.float64), (d,), eps=w.ln_eps))
+    ref_a = bf(F.layer_norm(x[-w.n_audio:].to(torch.float64), (d,), eps=w.ln_eps))
+    assert int(ulp_diff(ov, ref_v).max()) <= 1
+    assert int(ulp_diff(oa, ref_a).max()) <= 1
+
+
+def test_final_head_orientation_and_modulation():
+    """A one-hot W row picks one feature (W is [c][d]); a scale of -1 leaves only the shift;
+    and the general case against a float64 composition of library routines."""
+    w = W0
+    d, c = w.hidden, 128
+    x = synth.make_x(w, 1001)
+    g = torch.Generator().manual_seed(7)
+    mod = bf(torch.randn(2, d, generator=g, dtype=torch.float64) * 0.1)
+    wt = torch.zeros((c, d), dtype=torch.bfloat16)
+    wt[5, 17] = 1.0
+    ov, _ = oracle.final_head(w, x, video=(mod, wt))
+    nv = w.n_tokens - w.n_text - w.n_audio
+    h = oracle.adaln(x[:nv].contiguous(), mod[0], mod[1], w.ln_eps)
+    assert torch.equal(ov[:, 5].view(torch.int16), h[:, 17].view(torch.int16))
+    assert float(ov[:, :5].abs().max()) == 0.0
+    m2 = mod.clone()
+    m2[1] = -1.0
+    ov2, _ = oracle.final_head(w, x, video=(m2, wt))
+    assert bool((ov2[:, 5] == m2[0, 17]).all())
+    wt = bf(torch.randn(c, d, generator=g, dtype=torch.float64) * 0.02)
+    _, oa = oracle.final_head(w, x, audio=(mod, wt))
+    xa = x[-w.n_audio:].to(torch.float64)
+    hh = bf(F.layer_norm(xa, (d,), eps=w.ln_eps) * (1 + mod[1].to(torch.float64)) + mod[0].to(torch.float64))
+    ref = bf(hh.to(torch.float64) @ wt.to(torch.float64).T)
+    assert relerr(oa, ref) < 2e-2
