@@ -30,7 +30,8 @@ OUT_BF16, OUT_F32, OUT_I32, OUT_GELU, OUT_QKV = 0, 1, 2, 3, 4
 
 EXPORTS = ("h3dit_quantize_weights", "h3dit_block_fwd", "h3dit_stack_fwd", "h3dit_rope_tables",
            "h3dit_row_gate_adaln", "h3dit_quantize_rows", "h3dit_linear", "h3dit_rope_split", "h3dit_gelu",
-           "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore", "h3dit_linear_workspace")
+           "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore", "h3dit_linear_workspace",
+           "h3dit_final_head")
 
 
 class H3Error(RuntimeError):
@@ -79,6 +80,7 @@ _lib.h3dit_row_gate_adaln.argtypes = [C.c_int64, C.c_int32, C.c_float, _P, _P, _
 _lib.h3dit_quantize_rows.argtypes = [C.c_int64, C.c_int64, C.c_int64, _P, C.c_int32, _P, _P, _P]
 _lib.h3dit_linear.argtypes = [_P, _P]
 _lib.h3dit_linear_workspace.argtypes = [_P, _P]
+_lib.h3dit_final_head.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_rope_split.argtypes = [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_gelu.argtypes = [C.c_int64, _P, _P, _P]
 _lib.h3dit_attention.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
@@ -301,6 +303,36 @@ def linear_workspace(M, N, K, precision=BF16, a_group=0, out_kind=OUT_BF16, head
     need = C.c_uint64(0)
     _check("h3dit_linear_workspace", _lib.h3dit_linear_workspace(C.byref(args), C.byref(need)))
     return need.value
+
+
+class HeadPart(C.Structure):
+    _fields_ = [("mod", C.c_void_p), ("w", C.c_void_p), ("channels", C.c_int32)]
+
+
+def final_head(w, x, video=None, audio=None, stream=None):
+    """Final AdaLN head: video / audio are (mod bf16 [2][d], W bf16 [c][d]) device tensors or None.
+    Returns (out_video [n_video][c] or None, out_audio [n_audio][c] or None)."""
+    import torch
+    n_video = w.n_tokens - w.n_text - w.n_audio
+    parts, outs = [], []
+    for part, n in ((video, n_video), (audio, w.n_audio)):
+        if part is None:
+            parts.append(None)
+            outs.append(None)
+            continue
+        mod, wt = part
+        parts.append(HeadPart(_ptr(mod), _ptr(wt), wt.shape[0]))
+        outs.append(torch.empty((n, wt.shape[0]), dtype=torch.bfloat16, device=x.device))
+    refs = [C.byref(p) if p is not None else None for p in parts]
+    d, l = C.byref(dims_of(w)), C.byref(layout_of(w))
+    size = C.c_size_t(0)
+    _check("h3dit_final_head", _lib.h3dit_final_head(d, l, refs[0], refs[1], None, None, None, None, C.byref(size),
+                                                     None))
+    ws = torch.empty(max(size.value, 256), dtype=torch.uint8, device=x.device)
+    size = C.c_size_t(ws.numel())
+    _check("h3dit_final_head", _lib.h3dit_final_head(d, l, refs[0], refs[1], _ptr(x), _ptr(outs[0]), _ptr(outs[1]),
+                                                     _ptr(ws), C.byref(size), _stream(stream)))
+    return tuple(outs)
 
 
 def rope_split(n, heads, head_dim, t, cos, sin, q, k, vt, stream=None):

@@ -415,6 +415,60 @@ int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t 
   return H3DIT_OK;
 }
 
+int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,
+                     const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video, uint16_t *out_audio,
+                     void *workspace, size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes) return H3DIT_EINVAL;
+  int rc = check_dims(dims, layout, H3DIT_BF16);
+  if (rc) return rc;
+  const int64_t N = dims->n_tokens, d = dims->hidden;
+  const int64_t n_video = N - layout->n_text - layout->n_audio, n_audio = layout->n_audio;
+  struct Part {
+    const h3dit_head_part *p;
+    int64_t r0, n;
+    uint16_t *out;
+  } parts[2] = {{video, 0, n_video, out_video}, {audio, N - n_audio, n_audio, out_audio}};
+  size_t h_bytes = 0, sk_bytes = 0;
+  for (const Part &q : parts) {
+    if (!q.p) continue;
+    if (!q.p->mod || !q.p->w || !aligned(q.p->mod, 16) || !aligned(q.p->w, 16)) return H3DIT_EINVAL;
+    if (q.p->channels < 128 || q.p->channels % 128) return H3DIT_EINVAL;
+    h3dit_linear_args la{};
+    la.M = q.n; la.N = q.p->channels; la.K = d; la.precision = H3DIT_BF16; la.out_kind = H3DIT_OUT_BF16;
+    const size_t sk = linear_workspace(la);
+    if (sk > sk_bytes) sk_bytes = sk;
+    if ((size_t)(q.n * d * 2) > h_bytes) h_bytes = (size_t)(q.n * d * 2);
+  }
+  const size_t h_off = 0, sk_off = up(h_bytes), total = sk_off + up(sk_bytes);
+  if (!workspace) {
+    *workspace_bytes = total;
+    return H3DIT_OK;
+  }
+  if (!x || !aligned(x, 16) || !aligned(workspace, ALIGN)) return H3DIT_EINVAL;
+  for (const Part &q : parts)
+    if (q.p && q.n > 0 && (!q.out || !aligned(q.out, 16))) return H3DIT_EINVAL;
+  if (*workspace_bytes < total) {
+    *workspace_bytes = total;
+    return H3DIT_EWORKSPACE;
+  }
+  if ((rc = check_device())) return rc;
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  uint16_t *h = reinterpret_cast<uint16_t *>(ws + h_off);
+  const hipStream_t st = (hipStream_t)stream;
+  for (const Part &q : parts) {
+    if (!q.p || q.n == 0) continue;
+    // AdaLN of the modality's rows, read in place at their offset in the residual
+    TRY(launch_row(q.n, (int)d, dims->ln_eps, x + q.r0 * d, nullptr, nullptr, nullptr, q.p->mod, q.p->mod + d, h,
+                   nullptr, nullptr, st));
+    h3dit_linear_args la{};
+    la.M = q.n; la.N = q.p->channels; la.K = d; la.precision = H3DIT_BF16; la.out_kind = H3DIT_OUT_BF16;
+    la.a = h; la.w = q.p->w; la.out = q.out;
+    la.workspace = ws + sk_off; la.workspace_bytes = sk_bytes;
+    TRY(launch_linear(la, st));
+  }
+  return H3DIT_OK;
+}
+
 // ---------------------------------------------------------------- stage entry points
 
 int h3dit_rope_tables(const h3dit_layout *L, int32_t head_dim, int32_t reduced, float *cos_t, float *sin_t,

@@ -230,3 +230,20 @@ def test_zero_sized_stage_calls_return_ok_without_pointers():
     # sizes are still checked
     assert lib.h3dit_row_gate_adaln(0, 100, 1e-6, None, None, None, None, 1 << 20, 1 << 20, None, None, None,
                                     None) == h3.EINVAL
+
+
+def test_final_head_validation_and_workspace():
+    w = WORKLOADS[3]
+    lib = h3.lib()
+    a = 1 << 20
+    good = h3.HeadPart(a, a, 128)
+    bad = h3.HeadPart(a, a, 100)
+    size = C.c_size_t(0)
+    d, l = C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w))
+    assert lib.h3dit_final_head(d, l, C.byref(good), None, None, None, None, None, C.byref(size), None) == 0
+    n_video = w.n_tokens - w.n_text - w.n_audio
+    assert size.value >= n_video * w.hidden * 2
+    assert lib.h3dit_final_head(d, l, C.byref(bad), None, None, None, None, None, C.byref(size), None) == h3.EINVAL
+    assert lib.h3dit_final_head(d, l, None, None, None, None, None, None, C.byref(size), None) == 0
+    small = C.c_size_t(16)
+    assert lib.h3dit_final_head(d, l, C.byref(good), None, a, a, None, a, C.byref(small), None) == h3.EWORKSPACE

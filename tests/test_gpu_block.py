@@ -313,3 +313,26 @@ def test_zero_sized_stage_calls_touch_nothing():
     h3.attention(2, 0, 128, q, q, torch.zeros((2, 128, 16), device=DEV, dtype=torch.bfloat16), sentinel)
     torch.cuda.synchronize()
     assert bool((sentinel.float() == 7.0).all())
+
+
+# ----------------------------------------------------------------------------- final head
+
+@pytest.mark.parametrize("w", [W0, WORKLOADS[3].replace(blocks=1)], ids=["tiny", "4096tok"])
+def test_final_head_matches_oracle(w):
+    d = w.hidden
+    x = synth.make_x(w, 1005)
+    g = torch.Generator().manual_seed(3)
+    mv = (torch.randn(2, d, generator=g) * 0.1).to(torch.bfloat16)
+    ma = (torch.randn(2, d, generator=g) * 0.1).to(torch.bfloat16)
+    wv = (torch.randn(128, d, generator=g) * 0.02).to(torch.bfloat16)
+    wa = (torch.randn(256, d, generator=g) * 0.02).to(torch.bfloat16)
+    xg = x.to(DEV)
+    ov, oa = h3.final_head(w, xg, video=(mv.to(DEV), wv.to(DEV)), audio=(ma.to(DEV), wa.to(DEV)))
+    rv, ra = oracle.final_head(w, x, video=(mv, wv), audio=(ma, wa))
+    assert relerr(cpu(ov), rv) <= BF16_TOL
+    assert relerr(cpu(oa), ra) <= BF16_TOL
+    assert_bitexact(cpu(xg), x, "residual untouched")
+    # one part alone gives the same bytes
+    ov2, none = h3.final_head(w, xg, video=(mv.to(DEV), wv.to(DEV)))
+    assert none is None
+    assert_bitexact(cpu(ov2), cpu(ov), "video part alone")
