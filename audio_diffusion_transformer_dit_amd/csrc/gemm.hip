@@ -4,16 +4,21 @@
 //
 // Tiling: a workgroup owns a BM x BN output tile split over a WGM x WGN grid of waves, each
 // wave a grid of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16 or v_mfma_i32_32x32x32_i8; both
-// read 16 bytes of K per lane, so one LDS layout serves both).  The main shape is 256 x 256
-// with 8 waves (two per SIMD, 128 x 64 each): operand streaming from L2 is the bound on
-// gfx950, so the tile is as large as the register file allows, and a second wave per SIMD
-// keeps the matrix pipe busy while the other wave's memory instructions wait for issue.
-// K advances in 128-byte slices (full cache lines per row).  Slices travel global -> VGPR ->
-// LDS: while slice k is multiplied from LDS, slice k+1 waits in the other LDS stage and the
-// loads of slice k+2 are spread between the MFMAs, so each load has a whole iteration to
-// arrive.  Chunk c of row r sits at LDS slot c ^ ((r >> 1) & 7): the 16 lanes of one LDS
-// read phase (16 rows, one chunk) cover all 64 banks.  Fragment reads of the next 16-byte K
-// step overlap the MFMAs of the current one.
+// read 16 bytes of K per lane, so one LDS layout serves both).  K advances in 128-byte slices
+// (full cache lines per row) that travel global -> VGPR -> LDS.  Chunk c of row r sits at LDS
+// slot c ^ ((r >> 1) & 7): the 16 lanes of one LDS read phase (16 rows, one chunk) cover all
+// 64 banks.  Fragment reads of the next 16-byte K step overlap the MFMAs of the current one.
+// The main shape is 256 x 256, in one of two forms:
+//  * bf16: 4 waves (one per SIMD) of 128 x 128, accumulators in AGPRs.  Measured on gfx950 the
+//    fragment reads out of LDS are what holds the matrix pipe back, and a 128 x 128 wave tile
+//    reads a third fewer LDS bytes per MFMA than 128 x 64.  With no second wave to cover
+//    stalls the schedule is explicit: slice k+1's LDS stores and slice k+2's loads are spread
+//    between the MFMAs of slice k, and the per-slice barrier sits before the last K step so
+//    that the next slice's first fragments are read under that step's MFMAs.
+//  * int8 (and the 256 x 128 shape): 8 waves (two per SIMD) of 128 x 64; while slice k is
+//    multiplied, slice k+1 is stored to the other LDS stage at the top of the iteration and
+//    the loads of slice k+3 are spread between the MFMAs, so each load has more than a whole
+//    iteration to arrive.
 // Rows past M read as zeros (buffer range check).  The epilogue stages the bf16 tile in LDS
 // and writes 16-byte row chunks (or, for V, 16-byte token chunks of V^T).  Workgroups are
 // dealt round-robin to the 8 XCDs; the tile order is remapped so that each XCD sweeps a
@@ -218,21 +223,99 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
           acc[i][j] = sg == 0 ? val : acc[i][j] + val;
         }
   } else {
+  if constexpr (NW == 4) {
+    static_assert(!GROUPED, "grouped int8 keeps the 8-wave tiles");
+    // One wave per SIMD, 128 x 128 each (accumulators in AGPRs): a third fewer LDS bytes per
+    // MFMA than 8 waves of 128 x 64.  Iteration kt: MFMA steps 0..3 of slice kt from stage
+    // kt&1 with fragments read one step ahead; the registers of slice kt+1 go to stage
+    // (kt+1)&1 during steps 0..2 and the loads of slice kt+2 are spread over the iteration.
+    // The barrier sits before step 3, whose fragments are already in registers; the step-0
+    // fragments of slice kt+1 are read right after it, under step 3's MFMAs.
+    // LDS store li follows MFMA 2 li of the iteration (steps 0 and 1), global load li follows
+    // MFMA 4 li + 1 (spread over all four steps)
+    constexpr int NSTEP = FM * FN;
+    static_assert(2 * (NL - 1) < 3 * NSTEP && 4 * (NL - 1) + 1 < 4 * NSTEP, "store / load placement");
+    u32x4 fa[2][FM], fb[2][FN];
+    auto store_one = [&](const u32x4 *src, int kt, int li) {
+      uint8_t *st = smem + (kt & 1) * C::STAGE + lds0;
+      *reinterpret_cast<u32x4 *>(st + (li < LA ? li * NW * 1024 : BM * GKB + (li - LA) * NW * 1024)) = src[li];
+    };
+#pragma unroll
+    for (int li = 0; li < NL; li++) load_one(stage_reg[0], kt0, li);
+    store_slice(stage_reg[0], kt0);
+#pragma unroll
+    for (int li = 0; li < NL; li++) load_one(stage_reg[1], kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1, li);
+    __syncthreads();
+    read_step(smem + (kt0 & 1) * C::STAGE, 0, fa[0], fb[0]);
+    auto iter1 = [&](int kt, const u32x4 *cur, u32x4 *nxt, auto steady) {
+      constexpr bool STEADY = decltype(steady)::value;
+      const bool more = STEADY || kt + 1 < kt1;
+      const int ktl = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
+      const uint8_t *sa = smem + (kt & 1) * C::STAGE;
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) {
+        if (ks < 3) {
+          read_step(sa, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        } else {
+          __syncthreads();
+          if (more) read_step(smem + ((kt + 1) & 1) * C::STAGE, 0, fa[0], fb[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+          for (int j = 0; j < FN; j++) {
+            const int g = ks * NSTEP + i * FN + j;
+            if constexpr (INT8)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa[ks & 1][i]),
+                                                                __builtin_bit_cast(i32x4, fb[ks & 1][j]), acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[ks & 1][i]),
+                                                                  __builtin_bit_cast(bf16x8, fb[ks & 1][j]), acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int li = 0; li < NL; li++) {
+              if (g == 2 * li && more) {
+                __builtin_amdgcn_sched_barrier(0);
+                store_one(cur, kt + 1, li);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              if (STEADY && g == 4 * li + 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_one(nxt, ktl, li);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+          }
+      }
+    };
+    using Steady = std::integral_constant<bool, true>;
+    using Tail = std::integral_constant<bool, false>;
+    int kt = kt0;
+    for (; kt + 2 < kt1; kt += 2) {
+      iter1(kt, stage_reg[1], stage_reg[0], Steady{});
+      iter1(kt + 1, stage_reg[0], stage_reg[1], Steady{});
+    }
+    if (kt < kt1) iter1(kt, stage_reg[1], stage_reg[0], Tail{});
+    if (kt + 1 < kt1) iter1(kt + 1, stage_reg[0], stage_reg[1], Tail{});
+  } else {
   // prologue: slice kt0 into its LDS stage, slice kt0+1 in registers
 #pragma unroll
   for (int li = 0; li < NL; li++) load_one(stage_reg[0], kt0, li);
-#pragma unroll
-  for (int li = 0; li < NL; li++) load_one(stage_reg[1], kt0 + 1 < kt1 ? kt0 + 1 : kt0, li);
   store_slice(stage_reg[0], kt0);
+#pragma unroll
+  for (int li = 0; li < NL; li++) load_one(stage_reg[1], kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1, li);
+#pragma unroll
+  for (int li = 0; li < NL; li++) load_one(stage_reg[0], kt0 + 2 < kt1 ? kt0 + 2 : kt1 - 1, li);
   __syncthreads();
 
   // Iteration kt: registers of slice kt+1 -> LDS stage (kt+1)&1 (last read in iteration kt-1),
   // loads of slice kt+2 spread between the MFMAs of slice kt, barrier.  Past the end the loads
   // repeat the last slice (in range, never stored).  sched_barrier fixes the issue order.
   constexpr int NMMA = 4 * FM * FN;                 // MFMAs per slice; load li follows MFMA li*NMMA/NL
-  auto iteration = [&](int kt, const u32x4 *cur, u32x4 *nxt) {
-    if (kt + 1 < kt1) store_slice(cur, kt + 1);
-    const int ktl = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
+  auto iteration = [&](int kt, const u32x4 *cur, u32x4 *nxt, auto steady) {
+    constexpr bool STEADY = decltype(steady)::value;
+    if (STEADY || kt + 1 < kt1) store_slice(cur, kt + 1);
+    const int ktl = kt + 3 < kt1 ? kt + 3 : kt1 - 1;
     const uint8_t *sa = smem + (kt & 1) * C::STAGE;
     u32x4 fa[2][FM], fb[2][FN];
     read_step(sa, 0, fa[0], fb[0]);
@@ -253,7 +336,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
                                                                 __builtin_bit_cast(bf16x8, fb[ks & 1][j]), acc[i][j], 0, 0, 0);
 #pragma unroll
           for (int li = 0; li < NL; li++)
-            if (li * NMMA / NL == m) {
+            if (STEADY && li * NMMA / NL == m) {
               __builtin_amdgcn_sched_barrier(0);
               load_one(nxt, ktl, li);
               __builtin_amdgcn_sched_barrier(0);
@@ -288,9 +371,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
     __syncthreads();
   };
   // two iterations per trip so that each register set is addressed statically
-  for (int kt = kt0; kt < kt1; kt += 2) {
-    iteration(kt, stage_reg[1], stage_reg[0]);
-    if (kt + 1 < kt1) iteration(kt + 1, stage_reg[0], stage_reg[1]);
+  using Steady = std::integral_constant<bool, true>;
+  using Tail = std::integral_constant<bool, false>;
+  int kt = kt0;
+  for (; kt + 2 < kt1; kt += 2) {
+    iteration(kt, stage_reg[1], stage_reg[1], Steady{});
+    iteration(kt + 1, stage_reg[0], stage_reg[0], Steady{});
+  }
+  if (kt < kt1) iteration(kt, stage_reg[1], stage_reg[1], Tail{});
+  if (kt + 1 < kt1) iteration(kt + 1, stage_reg[0], stage_reg[0], Tail{});
   }
   wait_vmem();   // the register loads past the end
   if (!GROUPED && seg >= 0) {
@@ -522,7 +611,11 @@ static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st)
     // 8 waves of 64 x 64
     return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, false>(p, pl, st);
   } else {
-    if (pl.bn == 256) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, pl, st);
+    // bf16: four waves of 128 x 128; int8: eight waves of 128 x 64 (measured faster for int8)
+    if (pl.bn == 256) {
+      if constexpr (INT8) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, pl, st);
+      else return run_gemm<256, 256, 2, 2, INT8, OUT, GROUPED, HM>(p, pl, st);
+    }
     return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, HM>(p, pl, st);
   }
 }
