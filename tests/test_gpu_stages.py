@@ -163,6 +163,35 @@ def test_linear_bf16(M, N, K):
     assert_close_bf16(glc, ref, "GELU epilogue")
 
 
+@pytest.mark.parametrize("M,K,int8", [(4096, 128, False), (4000, 256, False), (4096, 384, False),
+                                      (4096, 384, True), (3900, 640, True)])
+def test_linear_full_round_short_k(M, K, int8):
+    # 16 x 16 tiles of 256 x 256 fill one round of the chip, so the plan takes whole 256 x 256
+    # tiles (bf16: the 4-wave loop; int8: the 8-wave loop) with only a few K slices: the paths
+    # where the steady loop runs zero or few times and the peeled tail does the work (int8 with
+    # 3 and 5 slices: odd counts); M = 4000 / 3900 leaves a ragged last tile row
+    N = 4096
+    assert h3.linear_workspace(M, N, K, precision=h3.INT8 if int8 else h3.BF16) == 0
+    a = bf_randn((M, K), 40 + K)
+    wt = bf_randn((N, K), 41 + K, 0.02)
+    if int8:
+        qa, sa = oracle.q8_rows(a)
+        qw, sw = oracle.quantize_weights(wt)
+        sa = sa[:, 0].contiguous()
+        acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+        h3.linear(M, N, K, to_dev(qa), to_dev(qw), h3.OUT_I32, acc, precision=h3.INT8, a_scale=to_dev(sa),
+                  w_scale=to_dev(sw))
+        assert_bitexact(cpu(acc), oracle.gemm_i32(qa, qw), "int32 accumulators")
+        return
+    ag, wg = to_dev(a), to_dev(wt)
+    acc = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    h3.linear(M, N, K, ag, wg, h3.OUT_F32, acc)
+    assert relerr(cpu(acc), oracle.gemm_f32(a, wt)) <= F32_TOL
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    h3.linear(M, N, K, ag, wg, h3.OUT_BF16, out)
+    assert_bitexact(cpu(out), cpu(acc).to(torch.bfloat16), "bf16 output = rounded fp32 accumulator")
+
+
 def test_linear_bf16_headmajor_input():
     H, M, hd, N = 4, 300, 64, 512
     K = H * hd
