@@ -31,7 +31,7 @@ OUT_BF16, OUT_F32, OUT_I32, OUT_GELU, OUT_QKV = 0, 1, 2, 3, 4
 EXPORTS = ("h3dit_quantize_weights", "h3dit_block_fwd", "h3dit_stack_fwd", "h3dit_rope_tables",
            "h3dit_row_gate_adaln", "h3dit_quantize_rows", "h3dit_linear", "h3dit_rope_split", "h3dit_gelu",
            "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore", "h3dit_linear_workspace",
-           "h3dit_final_head")
+           "h3dit_final_head", "h3dit_stack_fwd_streamed")
 
 
 class H3Error(RuntimeError):
@@ -75,6 +75,7 @@ _P = C.c_void_p
 _lib.h3dit_quantize_weights.argtypes = [_P, C.c_int64, C.c_int64, _P, _P, _P]
 _lib.h3dit_block_fwd.argtypes = [_P, _P, _P, _P, C.c_uint32, _P, _P, _P]
 _lib.h3dit_stack_fwd.argtypes = [_P, _P, C.c_int32, _P, _P, _P, C.c_uint32, _P, _P, _P]
+_lib.h3dit_stack_fwd_streamed.argtypes = [_P, _P, C.c_int32, _P, _P, _P, C.c_uint32, _P, _P, _P, _P]
 _lib.h3dit_rope_tables.argtypes = [_P, C.c_int32, C.c_int32, _P, _P, _P]
 _lib.h3dit_row_gate_adaln.argtypes = [C.c_int64, C.c_int32, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_quantize_rows.argtypes = [C.c_int64, C.c_int64, C.c_int64, _P, C.c_int32, _P, _P, _P]
@@ -246,6 +247,45 @@ def stack_fwd(w, blocks: list, x: torch.Tensor, flags: int = 0, reduction=None, 
     if workspace is None:
         workspace = alloc_workspace(s.workspace_bytes, x.device)
     return s(x, workspace, stream)
+
+
+def host_block(p: dict) -> dict:
+    """Copies of a block's tensors in newly allocated pinned host memory (the weights of a
+    streamed stack)."""
+    return {k: torch.empty(v.shape, dtype=v.dtype, pin_memory=True).copy_(v) for k, v in p.items()}
+
+
+def stack_streamed_workspace(w, blocks: list, flags: int = 0, reduction=None) -> int:
+    size = C.c_size_t(0)
+    arr = (BlockW * len(blocks))(*[block_struct(p) for p in blocks])
+    tr = TokenReduction(*reduction) if reduction else None
+    _check("h3dit_stack_fwd_streamed",
+           _lib.h3dit_stack_fwd_streamed(C.byref(dims_of(w)), C.byref(layout_of(w)), len(blocks), arr,
+                                         C.byref(tr) if tr else None, None, flags, None, C.byref(size), None, None))
+    return size.value
+
+
+class StreamedStack:
+    """A stack whose block weights stay in host memory (pinned host tensors, see host_block):
+    each block's matrices are copied into one of two device slots on `copy_stream` while the
+    previous block computes."""
+
+    def __init__(self, w, host_blocks: list, flags: int = 0, reduction=None):
+        self.blocks = host_blocks
+        self.flags = flags
+        self.arr = (BlockW * len(host_blocks))(*[block_struct(p) for p in host_blocks])
+        self.tr = TokenReduction(*reduction) if reduction else None
+        self.dims = dims_of(w)
+        self.layout = layout_of(w)
+        self.workspace_bytes = stack_streamed_workspace(w, host_blocks, flags, reduction)
+
+    def __call__(self, x: torch.Tensor, workspace: torch.Tensor, stream=None, copy_stream=None):
+        size = C.c_size_t(workspace.numel())
+        _check("h3dit_stack_fwd_streamed",
+               _lib.h3dit_stack_fwd_streamed(C.byref(self.dims), C.byref(self.layout), len(self.blocks), self.arr,
+                                             C.byref(self.tr) if self.tr else None, _ptr(x), self.flags,
+                                             _ptr(workspace), C.byref(size), _stream(stream), copy_stream))
+        return x
 
 
 # ------------------------------------------------------------------ h3dit_stages.h

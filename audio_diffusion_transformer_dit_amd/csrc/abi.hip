@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <vector>
 
 #include "common.hpp"
 
@@ -317,23 +318,105 @@ int run_block(const Ctx &c, int64_t n, const float *cos_t, const float *sin_t, c
   return H3DIT_OK;
 }
 
+// Validates the call, plans the workspace (plan.total bytes of activations, then `extra` bytes
+// for the caller) and answers a size query (returns 1).
 int prepare(const h3dit_dims *dims, const h3dit_layout *layout, int precision, uint32_t flags, bool reduction,
-            uint16_t *x, void *workspace, size_t *workspace_bytes, Plan &plan) {
+            uint16_t *x, void *workspace, size_t *workspace_bytes, Plan &plan, size_t extra = 0) {
   if (!workspace_bytes) return H3DIT_EINVAL;
   if (flags & ~(uint32_t)63) return H3DIT_EINVAL;
   int rc = check_dims(dims, layout, precision);
   if (rc) return rc;
   plan = make_plan(*dims, *layout, precision, flags, reduction);
+  const size_t need = plan.total + extra;
   if (!workspace) {
-    *workspace_bytes = plan.total;
+    *workspace_bytes = need;
     return 1;  // size query answered
   }
   if (!x || !aligned(x, 16) || !aligned(workspace, ALIGN)) return H3DIT_EINVAL;
-  if (*workspace_bytes < plan.total) {
-    *workspace_bytes = plan.total;
+  if (*workspace_bytes < need) {
+    *workspace_bytes = need;
     return H3DIT_EWORKSPACE;
   }
   return H3DIT_OK;
+}
+
+// The stack loop: rotary tables, token pair / restore, cross-block fusion.  blocks[b] must
+// hold device pointers by the time block b's kernels are enqueued; before(b) runs first and
+// after(b) once they are enqueued (both may enqueue work).  The next block's AdaLN1, fused into
+// block b's final gate, reads only blocks[b + 1].mod.
+template <class Before, class After>
+int run_stack(const Ctx &c, int32_t n_blocks, const h3dit_block_w *blocks, const h3dit_token_reduction *tr,
+              uint16_t *x, Before before, After after) {
+  const h3dit_dims *dims = c.D;
+  const h3dit_layout *layout = c.L;
+  const Plan &plan = c.P;
+  float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
+  float *cr = nullptr, *sr = nullptr;
+  TRY(launch_rope_tables(*layout, dims->head_dim, 0, cf, sf, c.st));
+  if (tr) {
+    cr = c.at<float>(plan.cos_r);
+    sr = c.at<float>(plan.sin_r);
+    TRY(launch_rope_tables(*layout, dims->head_dim, 1, cr, sr, c.st));
+  }
+  const int64_t Nf = dims->n_tokens, Nr = layout_tokens(*layout, true);
+  const int d = dims->hidden;
+  uint16_t *red = tr ? c.at<uint16_t>(plan.red) : nullptr, *r_in = tr ? c.at<uint16_t>(plan.r_in) : nullptr;
+  const bool cross = !(c.flags & (H3DIT_NOFUSE_CROSS_BLOCK | H3DIT_NOFUSE_GATE_ADALN));
+  bool reduced = false, h1_ready = false;
+  int rc;
+  for (int32_t b = 0; b < n_blocks; b++) {
+    if (reduced && b == tr->restore_before) {
+      TRY(launch_token_restore(*layout, d, x, red, r_in, c.st));
+      reduced = false;
+      h1_ready = false;
+    }
+    if ((rc = before(b))) return rc;
+    const bool boundary = (tr && (b == tr->reduce_after || b + 1 == tr->restore_before)) || b + 1 == n_blocks;
+    const h3dit_block_w *next = (cross && !boundary) ? &blocks[b + 1] : nullptr;
+    rc = run_block(c, reduced ? Nr : Nf, reduced ? cr : cf, reduced ? sr : sf, blocks[b], reduced ? red : x, h1_ready,
+                   next);
+    if (rc) return rc;
+    if ((rc = after(b))) return rc;
+    h1_ready = next != nullptr;
+    if (tr && b == tr->reduce_after) {
+      TRY(launch_token_pair(*layout, d, x, red, r_in, c.st));
+      reduced = true;
+      h1_ready = false;
+    }
+  }
+  if (reduced) TRY(launch_token_restore(*layout, d, x, red, r_in, c.st));
+  return H3DIT_OK;
+}
+
+// Device copy of one block's matrices and scales (a slot of the streamed stack): offsets of
+// w_qkv, w_o, w_fc1, w_fc2, s_qkv, s_o, s_fc1, s_fc2 (0 bytes where a precision has no scale).
+struct SlotLayout {
+  size_t off[8] = {}, bytes[8] = {};
+  size_t total = 0;
+};
+
+SlotLayout slot_layout(const h3dit_dims &D, int precision) {
+  const size_t d = (size_t)D.hidden, f = (size_t)D.mlp;
+  const size_t ea = attn_prec(precision) == H3DIT_INT8 ? 1 : 2, em = mlp_prec(precision) == H3DIT_INT8 ? 1 : 2;
+  const size_t rows[4] = {3 * d, d, f, d};
+  SlotLayout s;
+  s.bytes[0] = 3 * d * d * ea;
+  s.bytes[1] = d * d * ea;
+  s.bytes[2] = f * d * em;
+  s.bytes[3] = d * f * em;
+  for (int i = 0; i < 4; i++) {
+    const bool scaled = (i < 2 ? ea : em) == 1;
+    s.bytes[4 + i] = scaled ? rows[i] * 4 : 0;
+  }
+  for (int i = 0; i < 8; i++) {
+    s.off[i] = s.total;
+    s.total += up(s.bytes[i]);
+  }
+  return s;
+}
+
+size_t mod_bytes(const h3dit_dims &D, const h3dit_layout &L) {
+  return (size_t)(L.mod_sets == 3 ? 3 : 1) * 6 * (size_t)D.hidden * 2;
 }
 
 }  // namespace
@@ -380,39 +463,81 @@ int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t 
     if ((rc = check_block(&blocks[b], precision))) return rc;
   if ((rc = check_device())) return rc;
   Ctx c{dims, layout, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
-  float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
-  float *cr = nullptr, *sr = nullptr;
-  TRY(launch_rope_tables(*layout, dims->head_dim, 0, cf, sf, c.st));
-  if (tr) {
-    cr = c.at<float>(plan.cos_r);
-    sr = c.at<float>(plan.sin_r);
-    TRY(launch_rope_tables(*layout, dims->head_dim, 1, cr, sr, c.st));
-  }
-  const int64_t Nf = dims->n_tokens, Nr = layout_tokens(*layout, true);
-  const int d = dims->hidden;
-  uint16_t *red = tr ? c.at<uint16_t>(plan.red) : nullptr, *r_in = tr ? c.at<uint16_t>(plan.r_in) : nullptr;
-  const bool cross = !(flags & (H3DIT_NOFUSE_CROSS_BLOCK | H3DIT_NOFUSE_GATE_ADALN));
-  bool reduced = false, h1_ready = false;
+  auto none = [](int32_t) { return H3DIT_OK; };
+  return run_stack(c, n_blocks, blocks, tr, x, none, none);
+}
+
+int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
+                             const h3dit_block_w *blocks, const h3dit_token_reduction *tr, uint16_t *x, uint32_t flags,
+                             void *workspace, size_t *workspace_bytes, void *stream, void *copy_stream) {
+  if (!blocks || n_blocks < 1 || !dims || !layout) return H3DIT_EINVAL;
+  const int precision = blocks[0].precision;
+  if (tr && (tr->reduce_after < 0 || tr->restore_before <= tr->reduce_after || tr->reduce_after >= n_blocks))
+    return H3DIT_EINVAL;
+  int rc = check_dims(dims, layout, precision);   // the slot sizes below need valid widths
+  if (rc) return rc;
+  const SlotLayout sl = slot_layout(*dims, precision);
+  const size_t mb = mod_bytes(*dims, *layout);
+  const size_t mods_region = up(mb * (size_t)n_blocks);
+  Plan plan;
+  rc = prepare(dims, layout, precision, flags, tr != nullptr, x, workspace, workspace_bytes, plan,
+               mods_region + 2 * sl.total);
+  if (rc == 1) return H3DIT_OK;
+  if (rc) return rc;
+  for (int32_t b = 0; b < n_blocks; b++)
+    if ((rc = check_block(&blocks[b], precision))) return rc;
+  if ((rc = check_device())) return rc;
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  uint8_t *mods = ws + plan.total, *slot[2] = {mods + mods_region, mods + mods_region + sl.total};
+  const hipStream_t st = (hipStream_t)stream;
+  const hipStream_t cs = copy_stream ? (hipStream_t)copy_stream : st;
+
+  // device view of every block: matrices in slot b % 2, mod rows resident
+  std::vector<h3dit_block_w> dev((size_t)n_blocks);
   for (int32_t b = 0; b < n_blocks; b++) {
-    if (reduced && b == tr->restore_before) {
-      TRY(launch_token_restore(*layout, d, x, red, r_in, c.st));
-      reduced = false;
-      h1_ready = false;
-    }
-    const bool boundary = (tr && (b == tr->reduce_after || b + 1 == tr->restore_before)) || b + 1 == n_blocks;
-    const h3dit_block_w *next = (cross && !boundary) ? &blocks[b + 1] : nullptr;
-    rc = run_block(c, reduced ? Nr : Nf, reduced ? cr : cf, reduced ? sr : sf, blocks[b], reduced ? red : x, h1_ready,
-                   next);
-    if (rc) return rc;
-    h1_ready = next != nullptr;
-    if (tr && b == tr->reduce_after) {
-      TRY(launch_token_pair(*layout, d, x, red, r_in, c.st));
-      reduced = true;
-      h1_ready = false;
-    }
+    uint8_t *s = slot[b & 1];
+    h3dit_block_w &v = dev[(size_t)b];
+    v.precision = precision;
+    v.w_qkv = s + sl.off[0]; v.w_o = s + sl.off[1]; v.w_fc1 = s + sl.off[2]; v.w_fc2 = s + sl.off[3];
+    v.s_qkv = sl.bytes[4] ? reinterpret_cast<const float *>(s + sl.off[4]) : nullptr;
+    v.s_o = sl.bytes[5] ? reinterpret_cast<const float *>(s + sl.off[5]) : nullptr;
+    v.s_fc1 = sl.bytes[6] ? reinterpret_cast<const float *>(s + sl.off[6]) : nullptr;
+    v.s_fc2 = sl.bytes[7] ? reinterpret_cast<const float *>(s + sl.off[7]) : nullptr;
+    v.mod = reinterpret_cast<const uint16_t *>(mods + (size_t)b * mb);
+    TRY(hipMemcpyAsync(mods + (size_t)b * mb, blocks[b].mod, mb, hipMemcpyHostToDevice, st));
   }
-  if (reduced) TRY(launch_token_restore(*layout, d, x, red, r_in, c.st));
-  return H3DIT_OK;
+  // copied[s]: block weights in slot s are complete; freed[s]: the block that used slot s is done
+  struct Events {
+    hipEvent_t e[4] = {};
+    ~Events() {
+      for (hipEvent_t x : e)
+        if (x) (void)hipEventDestroy(x);
+    }
+  } ev;
+  for (hipEvent_t &e : ev.e) TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  hipEvent_t *copied = ev.e, *freed = ev.e + 2;
+  auto copy_block = [&](int32_t b) -> int {
+    const int s = b & 1;
+    if (b >= 2) TRY(hipStreamWaitEvent(cs, freed[s], 0));
+    const void *src[8] = {blocks[b].w_qkv, blocks[b].w_o, blocks[b].w_fc1, blocks[b].w_fc2,
+                          blocks[b].s_qkv, blocks[b].s_o, blocks[b].s_fc1, blocks[b].s_fc2};
+    for (int i = 0; i < 8; i++)
+      if (sl.bytes[i]) TRY(hipMemcpyAsync(slot[s] + sl.off[i], src[i], sl.bytes[i], hipMemcpyHostToDevice, cs));
+    TRY(hipEventRecord(copied[s], cs));
+    return H3DIT_OK;
+  };
+  Ctx c{dims, layout, flags, ws, plan, st};
+  if ((rc = copy_block(0))) return rc;
+  auto before = [&](int32_t b) -> int {
+    if (b + 1 < n_blocks && (rc = copy_block(b + 1))) return rc;
+    TRY(hipStreamWaitEvent(st, copied[b & 1], 0));
+    return H3DIT_OK;
+  };
+  auto after = [&](int32_t b) -> int {
+    TRY(hipEventRecord(freed[b & 1], st));
+    return H3DIT_OK;
+  };
+  return run_stack(c, n_blocks, dev.data(), tr, x, before, after);
 }
 
 int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,

@@ -152,6 +152,24 @@ H3DIT_API int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout
                     const h3dit_block_w *blocks, const h3dit_token_reduction *tr, uint16_t *x,
                     uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream);
 
+/* h3dit_stack_fwd with the block matrices left in host memory ([RV] section "h3-metal 的 SSD
+ * 串流：用速度換常駐記憶體": the small per-block weights stay resident while two full matrix
+ * slots alternate, the next block's matrices being fetched while the current block computes).
+ * blocks: host array as in h3dit_stack_fwd, but w_qkv, w_o, w_fc1, w_fc2, s_* and mod are HOST
+ * pointers (16-byte aligned; allocate them pinned, e.g. hipHostMalloc, or the copies run
+ * synchronously and nothing overlaps).  Every block's mod rows are copied once into the
+ * workspace; block b's matrices and scales are copied into slot b % 2 of the workspace on
+ * copy_stream, after the block that last used that slot has finished on `stream`, and block b
+ * waits for its copy.  Results are byte-identical to h3dit_stack_fwd with the same weights
+ * resident.  copy_stream: a second stream for the copies (NULL or equal to `stream`: copies
+ * on `stream`, no overlap).  workspace: as h3dit_stack_fwd plus the mod rows and two slots
+ * (NULL queries the size).  The host weights must stay valid until `stream` has completed
+ * the call's work.  Errors as h3dit_stack_fwd. */
+H3DIT_API int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
+                                       const h3dit_block_w *blocks, const h3dit_token_reduction *tr, uint16_t *x,
+                                       uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream,
+                                       void *copy_stream);
+
 /* One modality of the final head: mod bf16 [2][d] (shift, scale), w bf16 [channels][d],
  * channels % 128 == 0 (device pointers). */
 typedef struct {

@@ -192,6 +192,46 @@ def test_linear_workspace_plan():
     assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EINVAL       # misaligned
 
 
+def test_stack_streamed_workspace_and_validation():
+    """The streamed stack's workspace is the resident stack's plus every block's mod rows and
+    two slots of one block's matrices (each region 256-byte aligned); bad arguments are
+    rejected before anything runs."""
+    up = lambda v: (v + 255) // 256 * 256
+    w = WORKLOADS[1]
+    d, f = w.hidden, w.mlp
+    n = 3
+    for prec, ea, em in ((h3.BF16, 2, 2), (h3.INT8, 1, 1), (h3.INT8_MLP, 2, 1)):
+        arr = (h3.BlockW * n)(*[fake_block(prec) for _ in range(n)])
+        dims, lay = h3.dims_of(w), h3.layout_of(w)
+        res, stm = C.c_size_t(0), C.c_size_t(0)
+        assert h3.lib().h3dit_stack_fwd(C.byref(dims), C.byref(lay), n, arr, None, None, 0, None, C.byref(res),
+                                        None) == 0
+        assert h3.lib().h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), n, arr, None, None, 0, None,
+                                                 C.byref(stm), None, None) == 0
+        mats = [3 * d * d * ea, d * d * ea, f * d * em, d * f * em]
+        scales = [3 * d * 4 if ea == 1 else 0, d * 4 if ea == 1 else 0, f * 4 if em == 1 else 0,
+                  d * 4 if em == 1 else 0]
+        slot = sum(up(b) for b in mats + scales)
+        assert stm.value == res.value + up(n * 6 * d * 2) + 2 * slot, prec
+    arr = (h3.BlockW * 1)(fake_block(h3.BF16))
+    size = C.c_size_t(0)
+    dims, lay = h3.dims_of(w), h3.layout_of(w)
+    lib = h3.lib()
+    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 0, arr, None, None, 0, None, C.byref(size),
+                                        None, None) == h3.EINVAL                        # no blocks
+    bad = h3.TokenReduction(1, 1)
+    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, arr, C.byref(bad), None, 0, None,
+                                        C.byref(size), None, None) == h3.EINVAL         # empty reduced span
+    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, None, None, None, 0, None, C.byref(size),
+                                        None, None) == h3.EINVAL                        # NULL block array
+    arr2 = (h3.BlockW * 1)(fake_block(h3.BF16))
+    arr2[0].w_o = (1 << 20) + 8
+    x = 1 << 20
+    size = C.c_size_t(1 << 40)
+    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, arr2, None, x, 0, x, C.byref(size), None,
+                                        None) == h3.EINVAL                              # misaligned host matrix
+
+
 def test_int8_row_level_fc2_group_accepted():
     """fc2_group == mlp (one code per token over the FC2 input) is accepted above 8192;
     other groups above 8192 are not."""

@@ -285,6 +285,50 @@ def test_stack_int8_mlp_only_token_reduction():
     check_residual(cpu(xg), ref, x)
 
 
+# ----------------------------------------------------------------------------- streamed weights
+
+def _streamed(w, pg, x, reduction=None, separate_copy_stream=True, pinned=True):
+    """h3dit_stack_fwd_streamed with every block's tensors in host memory."""
+    hb = [h3.host_block(p) if pinned else {k: v.to("cpu") for k, v in p.items()} for p in pg]
+    s = h3.StreamedStack(w, hb, reduction=reduction)
+    ws = h3.alloc_workspace(s.workspace_bytes, DEV)
+    xg = x.to(DEV)
+    cs = torch.cuda.Stream() if separate_copy_stream else None
+    s(xg, ws, copy_stream=cs.cuda_stream if cs is not None else None)
+    out = cpu(xg)
+    del hb   # host weights stay alive until the stream is done (cpu() synchronised)
+    return out
+
+
+@pytest.mark.parametrize("prec", ["bf16", "int8", "int8_mlp"])
+def test_stack_streamed_equals_resident(prec):
+    # matrices copied per block into two alternating device slots on a second stream: byte
+    # for byte the resident stack, with token reduction, cross-block fusion and the slot reuse
+    # of six blocks
+    w = SMALL_TR
+    x, ps = inputs(w, blocks=6)
+    if prec == "int8_mlp":
+        pg = [h3.quantize_block(dev_block(p), mlp_only=True) for p in ps]
+    else:
+        pg = gpu_params(ps, prec == "int8")
+    xr = x.to(DEV)
+    h3.stack_fwd(w, pg, xr, reduction=(1, 4))
+    assert_bitexact(_streamed(w, pg, x, reduction=(1, 4)), cpu(xr), "streamed vs resident stack")
+
+
+def test_stack_streamed_single_stream_pageable_and_mod_sets():
+    # copies on the compute stream, weights in ordinary (pageable) host memory, three
+    # modulation sets: still the resident result
+    w = SMALL_TR.replace(mod_sets=3)
+    x, ps = inputs(w, blocks=3)
+    pg = gpu_params(ps, False)
+    xr = x.to(DEV)
+    h3.stack_fwd(w, pg, xr)
+    ref = cpu(xr)
+    assert_bitexact(_streamed(w, pg, x, separate_copy_stream=False), ref, "single stream")
+    assert_bitexact(_streamed(w, pg, x, pinned=False), ref, "pageable host weights")
+
+
 # ----------------------------------------------------------------------------- limits
 
 @pytest.mark.parametrize("int8", [False, True])
