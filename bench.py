@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--fc2-group", type=int, default=None,
                     help="int8 FC2-input group (1024 as on the pages; the MLP width gives one code per token, "
                          "the row-level variant)")
+    ap.add_argument("--streamed", action="store_true",
+                    help="also time the stack with every block's weights in pinned host memory "
+                         "(h3dit_stack_fwd_streamed: two device slots filled over the host link)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only-kernels: also run one plain device copy of this many bytes, the reference "
                          "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -82,6 +85,47 @@ def time_stack(w, blocks, x, steps, warmup, reduction=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return s.elapsed_time(e) / steps, wall, stack.workspace_bytes
+
+
+def time_streamed(w, blocks, x, steps, warmup, reduction=None):
+    """The stack with the block matrices streamed from pinned host memory; also the
+    host-to-device rate of one block's matrices copied alone."""
+    import torch
+    import audio_diffusion_transformer_dit_amd as h3
+    hb = [h3.host_block(p) for p in blocks]
+    torch.cuda.synchronize()
+    stack = h3.StreamedStack(w, hb, 0, reduction)
+    ws = h3.alloc_workspace(stack.workspace_bytes, x.device)
+    cs = torch.cuda.Stream()
+    for _ in range(warmup):
+        stack(x, ws, copy_stream=cs.cuda_stream)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        stack(x, ws, copy_stream=cs.cuda_stream)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    mats = {k: t for k, t in hb[0].items() if k != "mod"}
+    dst = {k: torch.empty_like(t, device=x.device) for k, t in mats.items()}
+    nbytes = sum(t.numel() * t.element_size() for t in mats.values())
+    for _ in range(2):
+        for k, t in mats.items():
+            dst[k].copy_(t, non_blocking=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(5):
+        for k, t in mats.items():
+            dst[k].copy_(t, non_blocking=True)
+    e.record()
+    torch.cuda.synchronize()
+    copy_ms = s.elapsed_time(e) / 5
+    del hb, dst
+    return {"ms_per_step": round(ms, 3), "ms_per_block": round(ms / w.blocks, 3), "block_bytes": nbytes,
+            "h2d_gbps": round(nbytes / (copy_ms / 1e3) / 1e9, 1),
+            "copy_bound_ms_per_step": round(copy_ms * w.blocks, 3),
+            "workspace_bytes": stack.workspace_bytes}
 
 
 def kernel_breakdown(w, p, x, iters, int8):
@@ -294,6 +338,9 @@ def main():
             "traffic": traffic_for(dom)}
     extra = {"ms_per_block": round(ms / w.blocks, 3), "tflop_per_step": round(step_flop / 1e12, 2),
              "workspace_bytes": ws_bytes, "kernels": kern, "wall_s_timed": round(wall, 3)}
+    if args.streamed:
+        print("[bench] timing the stack with weights streamed from host memory", file=sys.stderr, flush=True)
+        extra["streamed"] = time_streamed(w, blocks, x, args.steps, args.warmup, red)
 
     if not args.no_int8 and not int8_main:
         del blocks
@@ -304,6 +351,8 @@ def main():
                          "fc2_group": w.fc2_group,
                          "tops": round(step_flop / (ms8 / 1e3) / 1e12, 1),
                          "kernels": kernel_breakdown(w, blocks8[0], x, args.kernel_iters, True)}
+        if args.streamed:
+            extra["int8"]["streamed"] = time_streamed(w, blocks8, x, args.steps, args.warmup, red)
         del blocks8
         torch.cuda.empty_cache()
         # the middle row of the pages' int8 table: FC1 and FC2 in int8, attention projections bf16
