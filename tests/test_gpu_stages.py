@@ -330,8 +330,9 @@ def test_gelu_kernel():
 # ----------------------------------------------------------------------------- attention
 
 @pytest.mark.parametrize("H,N,hd", [(2, 1, 64), (3, 7, 64), (2, 64, 128), (4, 300, 64), (2, 257, 128),
-                                    (1, 1000, 128)])
+                                    (1, 1000, 128), (64, 300, 64), (128, 257, 128)])
 def test_attention(H, N, hd):
+    # the last two: many heads, so query tiles of several heads share each XCD (head grouping)
     q = bf_randn((H, N, hd), 23, 2.0)
     k = bf_randn((H, N, hd), 24, 2.0)
     v = bf_randn((H, N, hd), 25)
