@@ -146,8 +146,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   const uint32_t hm_shift = hm ? (p.hm_hd == 128 ? 7u : 6u) : 31u;
   const uint32_t hm_mask = hm ? (uint32_t)(p.hm_hd - 1) : 0xFFFFFFFFu;
 
-  // Slices travel global -> registers -> LDS: registers hold slice kt+2 while LDS holds slices
-  // kt (multiplied) and kt+1 (ready), so each load has a whole iteration to arrive.
+  // Slices travel global -> registers -> LDS through two register sets (the loop forms below
+  // say which slices they hold when).
   constexpr int NL = LA + LW;                       // 16-byte loads per lane per slice
   u32x4 stage_reg[2][NL];
   auto load_one = [&](u32x4 *dst, int kt, int li) {
@@ -227,8 +227,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
     static_assert(!GROUPED, "grouped int8 keeps the 8-wave tiles");
     // One wave per SIMD, 128 x 128 each (accumulators in AGPRs): a third fewer LDS bytes per
     // MFMA than 8 waves of 128 x 64.  Iteration kt: MFMA steps 0..3 of slice kt from stage
-    // kt&1 with fragments read one step ahead; the registers of slice kt+1 go to stage
-    // (kt+1)&1 during steps 0..2 and the loads of slice kt+2 are spread over the iteration.
+    // kt&1 with fragments read one step ahead; the register set holding slice kt+1 goes to
+    // stage (kt+1)&1 during steps 0 and 1, and the loads of slice kt+2 into the other set are
+    // spread over the iteration.
     // The barrier sits before step 3, whose fragments are already in registers; the step-0
     // fragments of slice kt+1 are read right after it, under step 3's MFMAs.
     // LDS store li follows MFMA 2 li of the iteration (steps 0 and 1), global load li follows
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
     if (kt < kt1) iter1(kt, stage_reg[1], stage_reg[0], Tail{});
     if (kt + 1 < kt1) iter1(kt + 1, stage_reg[0], stage_reg[1], Tail{});
   } else {
-  // prologue: slice kt0 into its LDS stage, slice kt0+1 in registers
+  // prologue: slice kt0 into its LDS stage, slices kt0+1 and kt0+2 in the two register sets
 #pragma unroll
   for (int li = 0; li < NL; li++) load_one(stage_reg[0], kt0, li);
   store_slice(stage_reg[0], kt0);
@@ -308,9 +309,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   for (int li = 0; li < NL; li++) load_one(stage_reg[0], kt0 + 2 < kt1 ? kt0 + 2 : kt1 - 1, li);
   __syncthreads();
 
-  // Iteration kt: registers of slice kt+1 -> LDS stage (kt+1)&1 (last read in iteration kt-1),
-  // loads of slice kt+2 spread between the MFMAs of slice kt, barrier.  Past the end the loads
-  // repeat the last slice (in range, never stored).  sched_barrier fixes the issue order.
+  // Iteration kt: the register set holding slice kt+1 -> LDS stage (kt+1)&1 (last read in
+  // iteration kt-1), then the same set receives slice kt+3, its loads spread between the MFMAs
+  // of slice kt; the other set (slice kt+2) stays in flight for the whole iteration; barrier.
+  // Past the end the loads repeat the last slice (in range, never stored).  sched_barrier
+  // fixes the issue order.
   constexpr int NMMA = 4 * FM * FN;                 // MFMAs per slice; load li follows MFMA li*NMMA/NL
   auto iteration = [&](int kt, const u32x4 *cur, u32x4 *nxt, auto steady) {
     constexpr bool STEADY = decltype(steady)::value;
