@@ -492,8 +492,14 @@ int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout,
   const hipStream_t st = (hipStream_t)stream;
   const hipStream_t cs = copy_stream ? (hipStream_t)copy_stream : st;
 
-  // device view of every block: matrices in slot b % 2, mod rows resident
-  std::vector<h3dit_block_w> dev((size_t)n_blocks);
+  // device view of every block: matrices in slot b % 2, mod rows resident (host-side array; no
+  // exception leaves the C ABI)
+  std::vector<h3dit_block_w> dev;
+  try {
+    dev.resize((size_t)n_blocks);
+  } catch (...) {
+    return H3DIT_EINVAL;
+  }
   for (int32_t b = 0; b < n_blocks; b++) {
     uint8_t *s = slot[b & 1];
     h3dit_block_w &v = dev[(size_t)b];
