@@ -236,3 +236,20 @@ def test_int8_token_reduction_identity_middle_full_size():
     xp = x.clone()
     h3.stack_fwd(w, [ps[0], ps[1], ps[4]], xp)
     assert_bitexact(cpu(xr), cpu(xp))
+
+
+def test_stack_streamed_equals_resident_full_size():
+    # production widths: three blocks' matrices (629 MB each) through the two device slots
+    w = WORKLOADS[3]
+    seed = synth.seed_for(3)
+    x = synth.make_x(w, seed, DEV)
+    ps = [synth.make_block(w, seed, b, DEV) for b in range(3)]
+    xr = x.clone()
+    h3.stack_fwd(w, ps, xr)
+    hb = [h3.host_block(p) for p in ps]
+    s = h3.StreamedStack(w, hb)
+    ws = h3.alloc_workspace(s.workspace_bytes, DEV)
+    xs = x.clone()
+    cs = torch.cuda.Stream()
+    s(xs, ws, copy_stream=cs.cuda_stream)
+    assert_bitexact(cpu(xs), cpu(xr), "streamed vs resident, 4096 tokens")
