@@ -2,12 +2,14 @@
  * h3dit.h — C ABI of the MI355X (gfx950) library for the MiniMax-H3 single-stream Omni DiT
  * block: the forward pass of one block, and of a stack of blocks for one denoising
  * evaluation, over a joint video + text + audio token sequence, in a bf16 path and an int8
- * path.  Every step runs in hand-written HIP kernels; the library never allocates.
+ * path.  Every step runs in hand-written HIP kernels; the library never allocates device
+ * memory.
  *
  * Sources (web pages about antirez's h3.c / h3-metal engine for MiniMax-H3):
  *   [RV] alphalab.site, "h3-metal 把 MiniMax-H3 搬上 Apple Silicon：突破與代價（2026）",
- *        section "h3.c README" (components: 50-layer single-stream Omni Transformer, full
- *        attention in the first public release).
+ *        sections "h3.c README" (components: 50-layer single-stream Omni Transformer, full
+ *        attention in the first public release) and "h3-metal 的 SSD 串流：用速度換常駐記憶體"
+ *        (two alternating weight slots, next block prefetched while the current one runs).
  *   [DD] linlog.top article 1265 (h3.c deep dive), sections "MiniMax H3：原生音频视频一体化
  *        生成" (dense Omni Transformer, precomputable AdaLN branches), "h3.c 的核心设计"
  *        (QKV and attention-output projections, Q/K/V routed head-major), "int8 量化：从 36
@@ -23,9 +25,12 @@
  *
  * Common rules for every entry point:
  *  - Pointers marked "device" must be device memory of the current HIP device; "host"
- *    pointers (the argument structs, the block array) are read during the call only.
+ *    pointers (the argument structs, the block array) are read during the call only, except
+ *    the host weights of h3dit_stack_fwd_streamed, which its copies read later.
  *  - The caller owns every buffer.  Calls are asynchronous on `stream` (a hipStream_t;
- *    NULL means the default stream); nothing is allocated and the host never waits.
+ *    NULL means the default stream); no memory is allocated and the host never waits
+ *    (h3dit_stack_fwd_streamed creates four HIP events per call, and its copies from
+ *    pageable host memory may run synchronously).
  *  - bf16 is passed as uint16_t bit patterns.  Matrices are row-major; weights are
  *    [out][in].  Device pointers must be 16-byte aligned.
  *  - Return: H3DIT_OK, or a negative status.  Arguments are validated before any launch;
