@@ -31,7 +31,8 @@ OUT_BF16, OUT_F32, OUT_I32, OUT_GELU, OUT_QKV = 0, 1, 2, 3, 4
 EXPORTS = ("h3dit_quantize_weights", "h3dit_block_fwd", "h3dit_stack_fwd", "h3dit_rope_tables",
            "h3dit_row_gate_adaln", "h3dit_quantize_rows", "h3dit_linear", "h3dit_rope_split", "h3dit_gelu",
            "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore", "h3dit_linear_workspace",
-           "h3dit_final_head", "h3dit_stack_fwd_streamed")
+           "h3dit_final_head", "h3dit_stack_fwd_streamed", "h3dit_denoise_plan", "h3dit_velocity_step",
+           "h3dit_denoise_fwd")
 
 
 class H3Error(RuntimeError):
@@ -62,6 +63,21 @@ class TokenReduction(C.Structure):
     _fields_ = [("reduce_after", C.c_int32), ("restore_before", C.c_int32)]
 
 
+class HeadPart(C.Structure):
+    _fields_ = [("mod", C.c_void_p), ("w", C.c_void_p), ("channels", C.c_int32)]
+
+
+class DenoiseOpts(C.Structure):
+    _fields_ = [("steps", C.c_int32), ("reuse", C.c_int32), ("core_reuse", C.c_int32), ("layers", C.c_int32),
+                ("reduce_after", C.c_int32), ("restore_early", C.c_int32), ("restore_late", C.c_int32),
+                ("early_evals", C.c_int32)]
+
+
+class DenoiseStep(C.Structure):
+    _fields_ = [("fresh", C.c_int32), ("core", C.c_int32), ("eval", C.c_int32), ("n_blocks", C.c_int32),
+                ("restore_before", C.c_int32)]
+
+
 class LinearArgs(C.Structure):
     _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64), ("precision", C.c_int32),
                 ("a", C.c_void_p), ("a_headmajor_hd", C.c_int32), ("a_scale", C.c_void_p), ("a_group", C.c_int32),
@@ -82,6 +98,9 @@ _lib.h3dit_quantize_rows.argtypes = [C.c_int64, C.c_int64, C.c_int64, _P, C.c_in
 _lib.h3dit_linear.argtypes = [_P, _P]
 _lib.h3dit_linear_workspace.argtypes = [_P, _P]
 _lib.h3dit_final_head.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.h3dit_denoise_plan.argtypes = [_P, C.c_int32, _P]
+_lib.h3dit_velocity_step.argtypes = [C.c_int64, C.c_float, _P, _P, _P]
+_lib.h3dit_denoise_fwd.argtypes = [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, C.c_uint32, _P, _P, _P]
 _lib.h3dit_rope_split.argtypes = [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_gelu.argtypes = [C.c_int64, _P, _P, _P]
 _lib.h3dit_attention.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
@@ -288,6 +307,56 @@ class StreamedStack:
         return x
 
 
+def denoise_opts(steps, reuse=1, core_reuse=1, layers=50, reduce_after=-1, restore_early=40, restore_late=30,
+                 early_evals=10) -> DenoiseOpts:
+    return DenoiseOpts(steps, reuse, core_reuse, layers, reduce_after, restore_early, restore_late, early_evals)
+
+
+def denoise_plan(opts: DenoiseOpts, n_blocks: int):
+    """(number of stack runs, list of per-step dicts {fresh, core, eval, n_blocks, restore_before})."""
+    arr = (DenoiseStep * max(int(opts.steps), 1))()
+    runs = _check("h3dit_denoise_plan", _lib.h3dit_denoise_plan(C.byref(opts), n_blocks, arr))
+    return runs, [{k: getattr(arr[i], k) for k, _ in DenoiseStep._fields_} for i in range(opts.steps)]
+
+
+def velocity_step(z, v, dt: float, stream=None):
+    """z = bf16(z + dt * v) in place (bf16 device tensors of one size, a multiple of 8)."""
+    _check("h3dit_velocity_step", _lib.h3dit_velocity_step(z.numel(), dt, _ptr(v), _ptr(z), _stream(stream)))
+    return z
+
+
+class Denoise:
+    """The denoising loop of h3dit_denoise_fwd with its host-side arguments marshalled once:
+    blocks (device weights), the plan options, per-step dt, and the head parts (video / audio:
+    (mod bf16 [2][d], W bf16 [c][d]) device tensors or None)."""
+
+    def __init__(self, w, blocks: list, opts: DenoiseOpts, dt, video=None, audio=None, flags: int = 0):
+        self.blocks = blocks
+        self.arr = (BlockW * len(blocks))(*[block_struct(p) for p in blocks])
+        self.opts = opts
+        self.dt = (C.c_float * int(opts.steps))(*[float(t) for t in dt])
+        self.parts = [None if p is None else HeadPart(_ptr(p[0]), _ptr(p[1]), p[1].shape[0]) for p in (video, audio)]
+        self.flags = flags
+        self.dims = dims_of(w)
+        self.layout = layout_of(w)
+        size = C.c_size_t(0)
+        _check("h3dit_denoise_fwd", _lib.h3dit_denoise_fwd(C.byref(self.dims), C.byref(self.layout), len(blocks),
+                                                           self.arr, C.byref(opts), self.dt, None, *self._refs(),
+                                                           None, None, flags, None, C.byref(size), None))
+        self.workspace_bytes = size.value
+
+    def _refs(self):
+        return [C.byref(p) if p is not None else None for p in self.parts]
+
+    def __call__(self, x_in, z_video, z_audio, workspace, stream=None):
+        size = C.c_size_t(workspace.numel())
+        _check("h3dit_denoise_fwd", _lib.h3dit_denoise_fwd(C.byref(self.dims), C.byref(self.layout), len(self.blocks),
+                                                           self.arr, C.byref(self.opts), self.dt, _ptr(x_in),
+                                                           *self._refs(), _ptr(z_video), _ptr(z_audio), self.flags,
+                                                           _ptr(workspace), C.byref(size), _stream(stream)))
+        return z_video, z_audio
+
+
 # ------------------------------------------------------------------ h3dit_stages.h
 
 def rope_tables(w, reduced=False, device="cuda", stream=None):
@@ -343,10 +412,6 @@ def linear_workspace(M, N, K, precision=BF16, a_group=0, out_kind=OUT_BF16, head
     need = C.c_uint64(0)
     _check("h3dit_linear_workspace", _lib.h3dit_linear_workspace(C.byref(args), C.byref(need)))
     return need.value
-
-
-class HeadPart(C.Structure):
-    _fields_ = [("mod", C.c_void_p), ("w", C.c_void_p), ("channels", C.c_int32)]
 
 
 def final_head(w, x, video=None, audio=None, stream=None):

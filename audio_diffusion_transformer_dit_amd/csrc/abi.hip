@@ -600,6 +600,114 @@ int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h
   return H3DIT_OK;
 }
 
+// ---------------------------------------------------------------- denoising loop
+
+int h3dit_denoise_plan(const h3dit_denoise_opts *o, int32_t n_blocks, h3dit_denoise_step *plan) {
+  if (!o || !plan) return H3DIT_EINVAL;
+  if (o->steps < 1 || o->reuse < 1 || o->core_reuse < 1 || (o->reuse > 1 && o->core_reuse > 1)) return H3DIT_EINVAL;
+  if (n_blocks < 1 || o->layers < 1 || o->layers > n_blocks) return H3DIT_EINVAL;
+  const bool red = o->reduce_after >= 0;
+  if (red && (o->reduce_after >= o->layers || o->restore_early <= o->reduce_after ||
+              o->restore_late <= o->reduce_after || o->early_evals < 0))
+    return H3DIT_EINVAL;
+  int32_t evals = 0;
+  for (int32_t i = 0; i < o->steps; i++) {
+    const bool last = i + 1 == o->steps;
+    const bool fresh = i % o->reuse == 0 || last;
+    const bool core = fresh && (i % o->core_reuse == 0 || last);
+    if (core) evals++;
+    h3dit_denoise_step &st = plan[i];
+    st.fresh = fresh;
+    st.core = core;
+    st.eval = evals - 1;
+    st.n_blocks = o->layers;
+    st.restore_before = red ? (st.eval < o->early_evals ? o->restore_early : o->restore_late) : -1;
+  }
+  return evals;
+}
+
+int h3dit_velocity_step(int64_t count, float dt, const uint16_t *v, uint16_t *z, void *stream) {
+  if (count < 0 || count % 8 || !v || !z || !aligned(v, 16) || !aligned(z, 16)) return H3DIT_EINVAL;
+  if (count == 0) return H3DIT_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  TRY(launch_velocity_step(count, dt, v, z, (hipStream_t)stream));
+  return H3DIT_OK;
+}
+
+int h3dit_denoise_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
+                      const h3dit_block_w *blocks, const h3dit_denoise_opts *opts, const float *dt,
+                      const uint16_t *x_in, const h3dit_head_part *video, const h3dit_head_part *audio,
+                      uint16_t *z_video, uint16_t *z_audio, uint32_t flags, void *workspace,
+                      size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes || !dims || !layout || !blocks || !opts || n_blocks < 1 || (!video && !audio))
+    return H3DIT_EINVAL;
+  if (opts->steps < 1) return H3DIT_EINVAL;
+  std::vector<h3dit_denoise_step> plan;
+  try {
+    plan.resize((size_t)opts->steps);
+  } catch (...) {
+    return H3DIT_EINVAL;
+  }
+  int rc = h3dit_denoise_plan(opts, n_blocks, plan.data());
+  if (rc < 0) return rc;
+  const bool red = opts->reduce_after >= 0;
+  // sizes: the working residual, the two velocity buffers, then the stack's or the head's
+  // workspace (they run one after the other on the stream, so they share it)
+  h3dit_token_reduction tr_q{opts->reduce_after, opts->restore_early > opts->restore_late ? opts->restore_early
+                                                                                          : opts->restore_late};
+  size_t stack_bytes = 0, head_bytes = 0;
+  if ((rc = h3dit_stack_fwd(dims, layout, opts->layers, blocks, red ? &tr_q : nullptr, nullptr, flags, nullptr,
+                            &stack_bytes, nullptr)))
+    return rc;
+  if ((rc = h3dit_final_head(dims, layout, video, audio, nullptr, nullptr, nullptr, nullptr, &head_bytes, nullptr)))
+    return rc;
+  const int64_t N = dims->n_tokens, d = dims->hidden;
+  const int64_t n_audio = layout->n_audio, n_video = N - layout->n_text - n_audio;
+  const int64_t cv = video ? (int64_t)video->channels * n_video : 0, ca = audio ? (int64_t)audio->channels * n_audio : 0;
+  const size_t x_off = 0, vv_off = up((size_t)(N * d * 2)), va_off = vv_off + up((size_t)cv * 2),
+               rest_off = va_off + up((size_t)ca * 2);
+  const size_t rest = stack_bytes > head_bytes ? stack_bytes : head_bytes, total = rest_off + rest;
+  if (!workspace) {
+    *workspace_bytes = total;
+    return H3DIT_OK;
+  }
+  if (!dt || !x_in || !aligned(x_in, 16) || !aligned(workspace, ALIGN)) return H3DIT_EINVAL;
+  if ((video && cv > 0 && (!z_video || !aligned(z_video, 16))) || (audio && ca > 0 && (!z_audio || !aligned(z_audio, 16))))
+    return H3DIT_EINVAL;
+  if (*workspace_bytes < total) {
+    *workspace_bytes = total;
+    return H3DIT_EWORKSPACE;
+  }
+  for (int32_t b = 0; b < opts->layers; b++)
+    if ((rc = check_block(&blocks[b], blocks[0].precision))) return rc;
+  if ((rc = check_device())) return rc;
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  uint16_t *x = reinterpret_cast<uint16_t *>(ws + x_off);
+  uint16_t *vv = reinterpret_cast<uint16_t *>(ws + vv_off), *va = reinterpret_cast<uint16_t *>(ws + va_off);
+  const hipStream_t st = (hipStream_t)stream;
+  for (const h3dit_denoise_step &s : plan) {
+    if (s.core) {
+      TRY(hipMemcpyAsync(x, x_in, (size_t)(N * d * 2), hipMemcpyDeviceToDevice, st));
+      h3dit_token_reduction tr{opts->reduce_after, s.restore_before};
+      size_t sb = rest;
+      if ((rc = h3dit_stack_fwd(dims, layout, s.n_blocks, blocks, red ? &tr : nullptr, x, flags, ws + rest_off, &sb,
+                                stream)))
+        return rc;
+    }
+    if (s.fresh) {
+      size_t hb = rest;
+      if ((rc = h3dit_final_head(dims, layout, video, audio, x, video ? vv : nullptr, audio ? va : nullptr,
+                                 ws + rest_off, &hb, stream)))
+        return rc;
+    }
+    const float step_dt = dt[&s - plan.data()];
+    if (cv > 0) TRY(launch_velocity_step(cv, step_dt, vv, z_video, st));
+    if (ca > 0) TRY(launch_velocity_step(ca, step_dt, va, z_audio, st));
+  }
+  return H3DIT_OK;
+}
+
 // ---------------------------------------------------------------- stage entry points
 
 int h3dit_rope_tables(const h3dit_layout *L, int32_t head_dim, int32_t reduced, float *cos_t, float *sin_t,

@@ -115,6 +115,7 @@ hipError_t launch_row(int64_t n, int d, float eps, const uint16_t *x, const uint
 hipError_t launch_quant_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v, int hm_hd,
                              int8_t *q, float *s, hipStream_t st);
 hipError_t launch_gelu(int64_t count, const uint16_t *u, uint16_t *gl, hipStream_t st);
+hipError_t launch_velocity_step(int64_t count, float dt, const uint16_t *v, uint16_t *z, hipStream_t st);
 hipError_t launch_rope_split(int64_t n, int heads, int hd, const uint16_t *t, const float *cos_t,
                              const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *vt, hipStream_t st);
 hipError_t launch_token_pair(const h3dit_layout &L, int d, const uint16_t *x, uint16_t *r, uint16_t *r_in,

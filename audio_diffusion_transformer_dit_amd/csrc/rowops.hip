@@ -353,6 +353,27 @@ hipError_t launch_gelu(int64_t count, const uint16_t *u, uint16_t *gl, hipStream
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- velocity step
+
+// z = bf16(z + dt * v): one Euler transition, product and sum each rounded in fp32.
+__global__ void k_velocity_step(int64_t nch, float dt, const uint16_t *__restrict__ v, uint16_t *__restrict__ z) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nch) return;
+  float fz[8], fv[8];
+  unpack8(reinterpret_cast<const u32x4 *>(z)[c], fz);
+  unpack8(reinterpret_cast<const u32x4 *>(v)[c], fv);
+#pragma unroll
+  for (int e = 0; e < 8; e++) fz[e] = __fadd_rn(fz[e], __fmul_rn(dt, fv[e]));
+  reinterpret_cast<u32x4 *>(z)[c] = pack8(fz);
+}
+
+hipError_t launch_velocity_step(int64_t count, float dt, const uint16_t *v, uint16_t *z, hipStream_t st) {
+  const int64_t nch = count / 8;
+  if (nch == 0) return hipSuccess;
+  k_velocity_step<<<(unsigned)((nch + 255) / 256), 256, 0, st>>>(nch, dt, v, z);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- rotary tables
 
 // Position of token n along each axis.  Video token (t, h, w) rotates the first rope_t/2

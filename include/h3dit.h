@@ -193,6 +193,60 @@ H3DIT_API int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layou
                                const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video,
                                uint16_t *out_audio, void *workspace, size_t *workspace_bytes, void *stream);
 
+/* Denoising schedule ([DD] "速度/质量预设矩阵": denoising steps, whole-denoiser velocity reuse,
+ * active blocks and core-residual reuse, with reuse and core reuse mutually exclusive;
+ * [DD] "Token 缩减": the bypass comes back before block 40 in the first ten noise evaluations
+ * and before block 30 in the later ones).  The pages give the controls and, for 20 steps,
+ * 20 / 11 / 8 fresh evaluations at reuse 1 / 2 / 3; the rules below are readings:
+ *  - reuse r: step i evaluates the denoiser when i % r == 0 or i is the last step; any other
+ *    step repeats the most recent fresh velocity for its transition (this yields 20 / 11 / 8).
+ *  - core_reuse c: the head is refreshed every step; the block stack runs when i % c == 0 or
+ *    i is the last step, and in between its most recent output residual is reused.
+ *  - layers L: the first L of the n_blocks blocks run.
+ *  - token reduction (reduce_after >= 0): core evaluation e (counted from 0) restores before
+ *    block restore_early when e < early_evals, else before block restore_late (40, 30, 10). */
+typedef struct {
+  int32_t steps, reuse, core_reuse, layers;
+  int32_t reduce_after;                              /* -1: no token reduction */
+  int32_t restore_early, restore_late, early_evals;
+} h3dit_denoise_opts;
+
+/* One step of a plan.  fresh: the velocity is evaluated (the head runs) at this step; core: the
+ * block stack runs first; eval: index of the core evaluation whose residual the velocity
+ * comes from; n_blocks: blocks that evaluation runs; restore_before: its token restore index
+ * (-1 without token reduction). */
+typedef struct {
+  int32_t fresh, core, eval, n_blocks, restore_before;
+} h3dit_denoise_step;
+
+/* Fills plan[0 .. opts->steps-1] (host memory).  Returns the number of core evaluations
+ * (>= 1), or H3DIT_EINVAL for: NULL pointers, steps < 1, reuse < 1, core_reuse < 1, reuse > 1
+ * together with core_reuse > 1, layers outside [1, n_blocks], or, with token reduction,
+ * reduce_after >= layers, a restore index <= reduce_after, or early_evals < 0.  Host only. */
+H3DIT_API int h3dit_denoise_plan(const h3dit_denoise_opts *opts, int32_t n_blocks, h3dit_denoise_step *plan);
+
+/* One transition of a velocity step: z[i] = bf16(z[i] + dt * v[i]) in fp32, product and sum
+ * each rounded (an Euler step of the velocity the head predicts; the pages name velocities and
+ * extrapolated transitions but no sampler, so this plain step is a reading).  z, v: bf16
+ * [count] (device), count % 8 == 0. */
+H3DIT_API int h3dit_velocity_step(int64_t count, float dt, const uint16_t *v, uint16_t *z, void *stream);
+
+/* A denoising loop over the plan of `opts`: for each step, a core step copies x_in into the
+ * workspace residual and runs h3dit_stack_fwd over the first plan.n_blocks blocks (with the
+ * step's token reduction), a fresh step runs h3dit_final_head on that residual into velocity
+ * buffers, and every step applies h3dit_velocity_step with dt[step] to z_video and z_audio.
+ * x_in (bf16 [n_tokens][hidden], device) is the residual every core evaluation starts from: it
+ * stands in for the patch embedding of the current latents, which the pages do not describe,
+ * so the latents do not feed back into the stack.  dt: host fp32 [steps].  video / audio and
+ * z_video / z_audio as in h3dit_final_head (bf16 [n_video][channels], [n_audio][channels],
+ * updated in place; at least one part).  workspace: NULL queries the size.  Errors as
+ * h3dit_denoise_plan, h3dit_stack_fwd and h3dit_final_head. */
+H3DIT_API int h3dit_denoise_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
+                                const h3dit_block_w *blocks, const h3dit_denoise_opts *opts, const float *dt,
+                                const uint16_t *x_in, const h3dit_head_part *video, const h3dit_head_part *audio,
+                                uint16_t *z_video, uint16_t *z_audio, uint32_t flags, void *workspace,
+                                size_t *workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,7 +50,7 @@ def lib():
         _lib.orc_gelu_tanh_f32.argtypes = [C.c_float]
         _lib.orc_num_threads.restype = C.c_int32
         for name in ("orc_layout_tokens", "orc_rope_tables", "orc_token_pair", "orc_token_restore",
-                     "orc_block_fwd", "orc_stack_fwd"):
+                     "orc_block_fwd", "orc_stack_fwd", "orc_denoise_plan"):
             getattr(_lib, name).restype = C.c_int32
     return _lib
 
@@ -310,3 +310,48 @@ def stack_fwd(w, blocks: list, x, reduce_after=-1, restore_before=-1, fused=Fals
     if rc != 0:
         raise ValueError(f"orc_stack_fwd failed: {rc}")
     return xo
+
+
+# ------------------------------------------------------------------ denoising loop
+
+def velocity_step(z, v, dt: float):
+    """bf(z + dt*v) elementwise (bf16 tensors of one shape); returns a new tensor."""
+    zo = z.contiguous().clone()
+    vc = v.contiguous()
+    assert zo.numel() == vc.numel()
+    lib().orc_velocity_step(_i64(zo.numel()), C.c_float(dt), _p(vc), _p(zo))
+    return zo
+
+
+def denoise_plan(steps, reuse=1, core_reuse=1, reduce_after=-1, restore_early=40, restore_late=30, early=10):
+    """Per-step schedule: a list of dicts {fresh, core, eval, restore}."""
+    arrs = [(C.c_int32 * int(steps))() for _ in range(4)]
+    rc = lib().orc_denoise_plan(C.c_int32(steps), C.c_int32(reuse), C.c_int32(core_reuse), C.c_int32(reduce_after),
+                                C.c_int32(restore_early), C.c_int32(restore_late), C.c_int32(early), *arrs)
+    if rc < 0:
+        raise ValueError(f"orc_denoise_plan failed: {rc}")
+    return [dict(fresh=arrs[0][i], core=arrs[1][i], eval=arrs[2][i], restore=arrs[3][i]) for i in range(steps)]
+
+
+def denoise(w, blocks: list, x_in, opts: dict, dt, video=None, audio=None, z_video=None, z_audio=None):
+    """The denoising loop of the plan: a core step runs the first `layers` blocks from x_in
+    (with the step's token restore), a fresh step runs the final head on that residual, and
+    every step moves the latents by dt[i] times the current velocity.  Returns (z_video, z_audio)."""
+    plan = denoise_plan(opts["steps"], opts.get("reuse", 1), opts.get("core_reuse", 1), opts.get("reduce_after", -1),
+                        opts.get("restore_early", 40), opts.get("restore_late", 30), opts.get("early_evals", 10))
+    layers = opts.get("layers", len(blocks))
+    zv = None if z_video is None else z_video.clone()
+    za = None if z_audio is None else z_audio.clone()
+    x = vv = va = None
+    for i, s in enumerate(plan):
+        if s["core"]:
+            red = opts.get("reduce_after", -1)
+            x = stack_fwd(w, blocks[:layers], x_in, reduce_after=red, restore_before=s["restore"] if red >= 0 else -1,
+                          fused=True)
+        if s["fresh"]:
+            vv, va = final_head(w, x, video, audio)
+        if zv is not None:
+            zv = velocity_step(zv, vv, float(dt[i]))
+        if za is not None:
+            za = velocity_step(za, va, float(dt[i]))
+    return zv, za

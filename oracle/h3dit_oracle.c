@@ -176,6 +176,49 @@ void orc_final_head(int64_t n, int32_t d, int32_t c, float eps, const uint16_t *
   free(acc);
 }
 
+/* ---------------------------------------------------------------- denoising loop */
+
+/* One Euler transition of the latents with the velocity the head predicts: each element becomes
+ * bf(z + dt*v), the product and the sum each rounded in fp32.  The pages ([DD] "速度/质量预设
+ * 矩阵") speak of denoiser velocities and extrapolated transitions but give no sampler; this
+ * plain step is the reading. */
+void orc_velocity_step(int64_t n, float dt, const uint16_t *v, uint16_t *z) {
+  for (int64_t i = 0; i < n; i++) {
+    float prod = dt * bf2f(v[i]);
+    z[i] = f2bf(bf2f(z[i]) + prod);
+  }
+}
+
+/* Schedule of a denoising run ([DD] "速度/质量预设矩阵" and "Token 缩减").  For each step i of
+ * `steps` it writes fresh[i] (the denoiser is evaluated), core[i] (the block stack runs),
+ * eval[i] (which stack run the velocity comes from) and restore[i] (that run's token restore
+ * block, -1 without reduction).  Readings: with whole-denoiser reuse r, the evaluated steps are
+ * the multiples of r and the last step (20 steps give 20, 11 and 8 evaluations for r = 1, 2,
+ * 3, the counts the pages print); skipped steps keep the last velocity.  With core reuse c the
+ * head runs every step and the stack on the multiples of c and the last step.  The first
+ * `early` stack runs restore before block `restore_early`, the rest before `restore_late`
+ * (40, 30 and ten on the pages).  Returns the number of stack runs, or -1 for an invalid
+ * request (reuse and core reuse together, counts below one, a restore not after the
+ * reduction block). */
+int32_t orc_denoise_plan(int32_t steps, int32_t reuse, int32_t core_reuse, int32_t reduce_after,
+                         int32_t restore_early, int32_t restore_late, int32_t early, int32_t *fresh,
+                         int32_t *core, int32_t *eval, int32_t *restore) {
+  if (steps < 1 || reuse < 1 || core_reuse < 1) return -1;
+  if (reuse > 1 && core_reuse > 1) return -1;
+  if (reduce_after >= 0 && (restore_early <= reduce_after || restore_late <= reduce_after || early < 0)) return -1;
+  int32_t runs = 0;
+  for (int32_t i = 0; i < steps; i++) {
+    int32_t is_last = (i == steps - 1);
+    fresh[i] = (i % reuse == 0) || is_last;
+    core[i] = fresh[i] && ((i % core_reuse == 0) || is_last);
+    if (core[i]) runs += 1;
+    eval[i] = runs - 1;
+    if (reduce_after < 0) restore[i] = -1;
+    else restore[i] = (eval[i] < early) ? restore_early : restore_late;
+  }
+  return runs;
+}
+
 /* ---------------------------------------------------------------- int8 */
 
 /* Symmetric int8 code of a span of bf16 values ([DD] "int8 量化"): scale = absmax / 127 by

@@ -81,6 +81,10 @@ void orc_dequant_bf16(int64_t M, int64_t N, const int32_t *acc, const float *sa,
                       uint16_t *out);
 void orc_final_head(int64_t n, int32_t d, int32_t c, float eps, const uint16_t *x, const uint16_t *shift,
                     const uint16_t *scale, const uint16_t *w, uint16_t *out);
+void orc_velocity_step(int64_t n, float dt, const uint16_t *v, uint16_t *z);
+int32_t orc_denoise_plan(int32_t steps, int32_t reuse, int32_t core_reuse, int32_t reduce_after,
+                         int32_t restore_early, int32_t restore_late, int32_t early, int32_t *fresh,
+                         int32_t *core, int32_t *eval, int32_t *restore);
 int32_t orc_token_pair(const orc_layout *L, int32_t d, const uint16_t *x, uint16_t *r);
 int32_t orc_token_restore(const orc_layout *L, int32_t d, const uint16_t *bypass,
                           const uint16_t *y, const uint16_t *r_in, uint16_t *x);

@@ -287,3 +287,64 @@ def test_final_head_validation_and_workspace():
     assert lib.h3dit_final_head(d, l, None, None, None, None, None, None, C.byref(size), None) == 0
     small = C.c_size_t(16)
     assert lib.h3dit_final_head(d, l, C.byref(good), None, a, a, None, a, C.byref(small), None) == h3.EWORKSPACE
+
+
+def test_denoise_plan_equals_oracle_and_validates():
+    """h3dit_denoise_plan is host logic: bit for bit the oracle's schedule over a grid of
+    options, with the pages' 20 / 11 / 8 fresh evaluations, and EINVAL for bad requests."""
+    import oracle
+    for steps in (1, 4, 5, 20, 33):
+        for reuse, core in ((1, 1), (2, 1), (3, 1), (1, 4), (1, 6)):
+            for red in ((-1, 40, 30, 10), (3, 40, 30, 10), (0, 2, 1, 1)):
+                opts = h3.denoise_opts(steps, reuse, core, 45, *red)
+                runs, plan = h3.denoise_plan(opts, 50)
+                ref = oracle.denoise_plan(steps, reuse, core, *red)
+                assert runs == sum(s["core"] for s in ref)
+                for s, r in zip(plan, ref):
+                    assert (s["fresh"], s["core"], s["eval"], s["restore_before"]) == \
+                        (r["fresh"], r["core"], r["eval"], r["restore"])
+                    assert s["n_blocks"] == 45
+    assert [h3.denoise_plan(h3.denoise_opts(20, r), 50)[0] for r in (1, 2, 3)] == [20, 11, 8]
+    lib = h3.lib()
+    arr = (h3.DenoiseStep * 20)()
+    for bad in (dict(reuse=2, core_reuse=4), dict(reuse=0), dict(core_reuse=0), dict(layers=0), dict(layers=51),
+                dict(reduce_after=45), dict(reduce_after=3, restore_early=3), dict(reduce_after=3, early_evals=-1)):
+        assert lib.h3dit_denoise_plan(C.byref(h3.denoise_opts(20, **bad)), 50, arr) == h3.EINVAL
+    assert lib.h3dit_denoise_plan(C.byref(h3.denoise_opts(0)), 50, arr) == h3.EINVAL
+    assert lib.h3dit_denoise_plan(None, 50, arr) == h3.EINVAL
+
+
+def test_velocity_step_and_denoise_validation():
+    lib = h3.lib()
+    a = 1 << 20
+    assert lib.h3dit_velocity_step(12, 0.5, a, a, None) == h3.EINVAL      # count % 8
+    assert lib.h3dit_velocity_step(16, 0.5, None, a, None) == h3.EINVAL
+    assert lib.h3dit_velocity_step(16, 0.5, a + 8, a, None) == h3.EINVAL  # alignment
+    assert lib.h3dit_velocity_step(0, 0.5, None, None, None) == h3.EINVAL
+    w = WORKLOADS[3]
+    d, l = C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w))
+    blocks = (h3.BlockW * 50)(*[h3.BlockW(h3.BF16, a, a, a, a, None, None, None, None, a)] * 50)
+    head = h3.HeadPart(a, a, 128)
+    dt = (C.c_float * 20)(*([-0.05] * 20))
+    size = C.c_size_t(0)
+    opts = h3.denoise_opts(20, reuse=2, layers=45)
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(opts), dt, None, C.byref(head), None, None, None, 0, None,
+                                 C.byref(size), None) == 0
+    stack = h3.stack_workspace(w, [dict(wqkv=a, wo=a, w1=a, w2=a, mod=a)] * 45)
+    n_video = w.n_tokens - w.n_text - w.n_audio
+    assert size.value >= w.n_tokens * w.hidden * 2 + n_video * 128 * 2 + stack
+    red = h3.denoise_opts(20, reuse=2, layers=45, reduce_after=3)
+    rsize = C.c_size_t(0)
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(red), dt, None, C.byref(head), None, None, None, 0, None,
+                                 C.byref(rsize), None) == 0
+    assert rsize.value > size.value
+    # no head part, a bad plan, a short workspace: rejected before any launch
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(opts), dt, None, None, None, None, None, 0, None,
+                                 C.byref(size), None) == h3.EINVAL
+    bad = h3.denoise_opts(20, reuse=2, core_reuse=2, layers=45)
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(bad), dt, None, C.byref(head), None, None, None, 0, None,
+                                 C.byref(size), None) == h3.EINVAL
+    small = C.c_size_t(256)
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(opts), dt, a, C.byref(head), None, a, None, 0, a,
+                                 C.byref(small), None) == h3.EWORKSPACE
+    assert small.value == size.value

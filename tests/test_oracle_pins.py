@@ -722,3 +722,104 @@ def test_final_head_orientation_and_modulation():
     hh = bf(F.layer_norm(xa, (d,), eps=w.ln_eps) * (1 + mod[1].to(torch.float64)) + mod[0].to(torch.float64))
     ref = bf(hh.to(torch.float64) @ wt.to(torch.float64).T)
     assert relerr(oa, ref) < 2e-2
+
+
+# ----------------------------------------------------------------------------- denoising loop
+
+def test_denoise_plan_fresh_counts_are_the_pages():
+    """20 steps at reuse 1 / 2 / 3 give 20 / 11 / 8 fresh denoiser evaluations, the counts the
+    h3.c deep dive prints ("速度/质量预设矩阵"); the last step is always evaluated."""
+    for r, n in ((1, 20), (2, 11), (3, 8)):
+        plan = oracle.denoise_plan(20, reuse=r)
+        assert sum(s["fresh"] for s in plan) == n
+        assert sum(s["core"] for s in plan) == n
+        assert plan[-1]["fresh"] == 1 and plan[0]["fresh"] == 1
+
+
+def test_denoise_plan_token_restore_schedule():
+    """Token reduction restores before block 40 in the first ten noise evaluations and before
+    block 30 in the later ones ("Token 缩减"): at 20 fresh steps, ten of each."""
+    plan = oracle.denoise_plan(20, reduce_after=3)
+    assert [s["restore"] for s in plan] == [40] * 10 + [30] * 10
+    # skipped steps use the latest evaluation; the schedule counts evaluations, not steps
+    plan = oracle.denoise_plan(20, reuse=2, reduce_after=3)
+    evals = [s["eval"] for s in plan]
+    assert evals == [i // 2 for i in range(19)] + [10]
+    assert [s["restore"] for s in plan] == [40] * 19 + [30]
+    assert all(s["restore"] == -1 for s in oracle.denoise_plan(7))
+
+
+def test_denoise_plan_rules_brute_force():
+    """Against a direct enumeration: a step is evaluated iff it is a multiple of reuse or the
+    last; with core reuse every step refreshes the head and the stack runs on multiples of
+    core_reuse and the last step; reuse and core reuse together are rejected, as the pages
+    state they are mutually exclusive; the 4-step budget at reuse 1 runs the model every step."""
+    for steps in (1, 2, 3, 4, 7, 20, 50):
+        for r in (1, 2, 3, 5):
+            plan = oracle.denoise_plan(steps, reuse=r)
+            fresh = [s["fresh"] for s in plan]
+            assert fresh == [int(i % r == 0 or i == steps - 1) for i in range(steps)]
+            last = -1
+            for i, s in enumerate(plan):
+                last += fresh[i]
+                assert s["eval"] == last
+        for c in (2, 4, 6):
+            plan = oracle.denoise_plan(steps, core_reuse=c)
+            assert all(s["fresh"] for s in plan)
+            assert [s["core"] for s in plan] == [int(i % c == 0 or i == steps - 1) for i in range(steps)]
+    assert all(s["core"] for s in oracle.denoise_plan(4, reuse=1))
+    for bad in (dict(reuse=2, core_reuse=4), dict(reuse=0), dict(core_reuse=0), dict(reduce_after=3, restore_late=3)):
+        with pytest.raises(ValueError):
+            oracle.denoise_plan(20, **bad)
+
+
+def test_velocity_step_rounding():
+    """Hand-derived bf16 cases of z + dt*v: dt = 0 and v = 0 leave z; 1 + 2 * 0.5 = 2 exactly;
+    1 + 2^-8 is a tie between 1 and 1 + 2^-7 and goes to the even 1; (1 + 2^-7) + 2^-8 is a
+    tie that goes to the even 1 + 2^-6; and the general case against torch's float32
+    arithmetic with its round-to-nearest-even bf16 conversion."""
+    z = torch.tensor([1.0, 1.0, 1.0 + 2 ** -7, -3.0], dtype=torch.bfloat16)
+    v = torch.tensor([2.0, 2 ** -8, 2 ** -8, 0.0], dtype=torch.bfloat16)
+    out = oracle.velocity_step(z, v, 0.5)
+    assert out.tolist() == [2.0, 1.0, 1.0 + 2 ** -7, -3.0]
+    out = oracle.velocity_step(z, v, 1.0)
+    assert out.tolist() == [3.0, 1.0, 1.0 + 2 ** -6, -3.0]
+    g = torch.Generator().manual_seed(11)
+    z = torch.randn(4096, generator=g).to(torch.bfloat16)
+    v = torch.randn(4096, generator=g).to(torch.bfloat16)
+    assert torch.equal(oracle.velocity_step(z, v, 0.0).view(torch.int16), z.view(torch.int16))
+    for dt in (-0.05, 0.125, 1.0 / 3.0):
+        prod = torch.tensor(dt, dtype=torch.float32) * v.to(torch.float32)
+        ref = (z.to(torch.float32) + prod).to(torch.bfloat16)
+        assert torch.equal(oracle.velocity_step(z, v, dt).view(torch.int16), ref.view(torch.int16))
+
+
+def test_denoise_loop_is_euler_over_the_plan():
+    """The oracle loop against its parts: with one fresh evaluation per step and a residual
+    input that does not change, every evaluation gives the same velocity v, so the latents
+    after the loop are the Euler steps of v; with reuse 3 over 4 steps the same holds (skipped
+    steps repeat v); and with token reduction the early and late restore indices give
+    velocities that differ."""
+    w = W0
+    d = w.hidden
+    x = synth.make_x(w, 1007)
+    blocks = [synth.make_block(w, 1007, b) for b in range(3)]
+    g = torch.Generator().manual_seed(5)
+    mv = bf(torch.randn(2, d, generator=g) * 0.1)
+    wv = bf(torch.randn(128, d, generator=g) * 0.02)
+    nv = w.n_tokens - w.n_text - w.n_audio
+    z0 = bf(torch.randn(nv, 128, generator=g) * 0.01)
+    dt = [-0.25] * 4
+    zv, za = oracle.denoise(w, blocks, x, dict(steps=4, layers=2), dt, video=(mv, wv), z_video=z0)
+    assert za is None
+    v, _ = oracle.final_head(w, oracle.stack_fwd(w, blocks[:2], x, fused=True), video=(mv, wv))
+    ref = z0
+    for t in dt:
+        ref = oracle.velocity_step(ref, v, t)
+    assert torch.equal(zv.view(torch.int16), ref.view(torch.int16))
+    zr, _ = oracle.denoise(w, blocks, x, dict(steps=4, reuse=3, layers=2), dt, video=(mv, wv), z_video=z0)
+    assert torch.equal(zr.view(torch.int16), ref.view(torch.int16))
+    opts = dict(steps=3, layers=3, reduce_after=0, restore_early=2, restore_late=1, early_evals=1)
+    a, _ = oracle.denoise(w, blocks, x, opts, [-1.0, 0.0, 0.0], video=(mv, wv), z_video=z0)
+    b, _ = oracle.denoise(w, blocks, x, opts, [0.0, 0.0, -1.0], video=(mv, wv), z_video=z0)
+    assert not torch.equal(a.view(torch.int16), b.view(torch.int16))
