@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--streamed", action="store_true",
                     help="also time the stack with every block's weights in pinned host memory "
                          "(h3dit_stack_fwd_streamed: two device slots filled over the host link)")
+    ap.add_argument("--denoise", action="store_true",
+                    help="also time 20-step denoising runs (h3dit_denoise_fwd) at the pages' slow, default and "
+                         "token-reduction presets")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only-kernels: also run one plain device copy of this many bytes, the reference "
                          "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -275,6 +278,52 @@ def cpu_baseline(w):
                       f"{50 * block_flops(4096, 5120, 20480) / (fl / dt) :.0f} s"}
 
 
+DENOISE_PRESETS = {
+    # the pages' control matrix: slow reference, the verified --layers 45 --reuse 2 setting, and
+    # that setting with token reduction (bypass restored before block 40, then 30)
+    "slow_reference": dict(steps=20, reuse=1, layers=50),
+    "layers45_reuse2": dict(steps=20, reuse=2, layers=45),
+    "layers45_reuse2_token_reduction": dict(steps=20, reuse=2, layers=45, reduce_after=3),
+}
+
+
+def time_denoise(w, blocks, x, seed, channels=128):
+    """Each preset once after one untimed run: the stack runs of its plan plus the head and
+    the velocity steps (synthetic head weights; latents of `channels` per video / audio row)."""
+    import torch
+    import audio_diffusion_transformer_dit_amd as h3
+    g = torch.Generator(device=x.device).manual_seed(seed + 77)
+    d = w.hidden
+    nv = w.n_tokens - w.n_text - w.n_audio
+
+    def rnd(*shape, std):
+        return (torch.randn(*shape, generator=g, device=x.device) * std).to(torch.bfloat16)
+
+    video = (rnd(2, d, std=0.1), rnd(channels, d, std=0.02))
+    audio = (rnd(2, d, std=0.1), rnd(channels, d, std=0.02))
+    out = {}
+    for name, o in DENOISE_PRESETS.items():
+        layers = min(o["layers"], len(blocks))
+        opts = h3.denoise_opts(o["steps"], o.get("reuse", 1), 1, layers, o.get("reduce_after", -1), 40, 30, 10)
+        runs, plan = h3.denoise_plan(opts, len(blocks))
+        run = h3.Denoise(w, blocks, opts, [-1.0 / o["steps"]] * o["steps"], video=video, audio=audio)
+        ws = h3.alloc_workspace(run.workspace_bytes, x.device)
+        zv, za = rnd(nv, channels, std=1.0), rnd(w.n_audio, channels, std=1.0)
+        run(x, zv, za, ws)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        run(x, zv, za, ws)
+        e.record()
+        torch.cuda.synchronize()
+        out[name] = {"ms": round(s.elapsed_time(e), 2), "stack_runs": runs, "blocks_per_run": layers,
+                     "steps": o["steps"], "reuse": o.get("reuse", 1),
+                     "token_reduction": [o["reduce_after"], 40, 30] if "reduce_after" in o else None}
+        print(f"[bench] denoise {name}: {out[name]['ms']:.1f} ms ({runs} stack runs)", file=sys.stderr, flush=True)
+        del ws
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -342,6 +391,9 @@ def main():
         print("[bench] timing the stack with weights streamed from host memory", file=sys.stderr, flush=True)
         extra["streamed"] = time_streamed(w, blocks, x, args.steps, args.warmup, red)
 
+    if args.denoise:
+        extra["denoise"] = time_denoise(w, blocks, x, seed)
+
     if not args.no_int8 and not int8_main:
         del blocks
         torch.cuda.empty_cache()
@@ -353,6 +405,8 @@ def main():
                          "kernels": kernel_breakdown(w, blocks8[0], x, args.kernel_iters, True)}
         if args.streamed:
             extra["int8"]["streamed"] = time_streamed(w, blocks8, x, args.steps, args.warmup, red)
+        if args.denoise:
+            extra["int8"]["denoise"] = time_denoise(w, blocks8, x, seed)
         del blocks8
         torch.cuda.empty_cache()
         # the middle row of the pages' int8 table: FC1 and FC2 in int8, attention projections bf16
