@@ -49,7 +49,8 @@ def parse():
                          "(h3dit_stack_fwd_streamed: two device slots filled over the host link)")
     ap.add_argument("--denoise", action="store_true",
                     help="also time 20-step denoising runs (h3dit_denoise_fwd) at the pages' slow, default and "
-                         "token-reduction presets")
+                         "token-reduction presets (kept out of the default run: its reduced-sequence launches share "
+                         "kernel names with the full-size ones and would mix into the profiled per-kernel averages)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only-kernels: also run one plain device copy of this many bytes, the reference "
                          "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
