@@ -72,7 +72,9 @@ def make_blocks(w, n_blocks, seed, device, int8, mlp_only=False):
     return blocks
 
 
-def time_stack(w, blocks, x, steps, warmup, reduction=None):
+def time_stack(w, blocks, x, steps, warmup, reduction=None, per_step=None):
+    """Mean ms per step over `steps` stack calls between two events on the launch stream (and,
+    from events recorded between the calls, the median and minimum single step into per_step)."""
     import torch
     import audio_diffusion_transformer_dit_amd as h3
     stack = h3.Stack(w, blocks, 0, reduction)
@@ -80,15 +82,19 @@ def time_stack(w, blocks, x, steps, warmup, reduction=None):
     for _ in range(warmup):
         stack(x, ws)
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    s.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         stack(x, ws)
-    e.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return s.elapsed_time(e) / steps, wall, stack.workspace_bytes
+    if per_step is not None and steps > 0:
+        one = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        per_step["step_ms_median"] = round(one[steps // 2] if steps % 2 else 0.5 * (one[steps // 2 - 1] + one[steps // 2]), 3)
+        per_step["step_ms_min"] = round(one[0], 3)
+    return ev[0].elapsed_time(ev[steps]) / steps, wall, stack.workspace_bytes
 
 
 def time_streamed(w, blocks, x, steps, warmup, reduction=None):
@@ -367,7 +373,8 @@ def main():
     blocks = make_blocks(w, w.blocks, seed, dev, int8_main)
     torch.cuda.synchronize()
     print("[bench] weights resident; timing the stack", file=sys.stderr, flush=True)
-    ms, wall, ws_bytes = time_stack(w, blocks, x, args.steps, args.warmup, red)
+    step_stats = {}
+    ms, wall, ws_bytes = time_stack(w, blocks, x, args.steps, args.warmup, red, step_stats)
     if red:
         nr = w.video_t * w.video_h * (w.video_w // 2 + w.video_w % 2) + w.n_text + w.n_audio
         full = red[0] + 1 + max(0, w.blocks - red[1])
@@ -386,7 +393,7 @@ def main():
     roof = {"bound": "mfma", "kernel": dom, "achieved": mm[dom]["tflops"], "peak": PEAK[kprec],
             "unit": "TFLOP/s" if kprec == "bf16" else "TOP/s", "frac": round(mm[dom]["tflops"] / PEAK[kprec], 4),
             "traffic": traffic_for(dom)}
-    extra = {"ms_per_block": round(ms / w.blocks, 3), "tflop_per_step": round(step_flop / 1e12, 2),
+    extra = {"ms_per_block": round(ms / w.blocks, 3), **step_stats, "tflop_per_step": round(step_flop / 1e12, 2),
              "workspace_bytes": ws_bytes, "kernels": kern, "wall_s_timed": round(wall, 3)}
     if args.streamed:
         print("[bench] timing the stack with weights streamed from host memory", file=sys.stderr, flush=True)
@@ -399,8 +406,9 @@ def main():
         del blocks
         torch.cuda.empty_cache()
         blocks8 = make_blocks(w, w.blocks, seed, dev, True)
-        ms8, _, _ = time_stack(w, blocks8, x, args.steps, args.warmup, red)
-        extra["int8"] = {"ms_per_step": round(ms8, 3), "ms_per_block": round(ms8 / w.blocks, 3),
+        step8 = {}
+        ms8, _, _ = time_stack(w, blocks8, x, args.steps, args.warmup, red, step8)
+        extra["int8"] = {"ms_per_step": round(ms8, 3), **step8, "ms_per_block": round(ms8 / w.blocks, 3),
                          "fc2_group": w.fc2_group,
                          "tops": round(step_flop / (ms8 / 1e3) / 1e12, 1),
                          "kernels": kernel_breakdown(w, blocks8[0], x, args.kernel_iters, True)}

@@ -16,7 +16,8 @@
  *        秒到 19 秒" (int8 scheme and its table), "DiT 融合内核：减少全局内存往返" (gate +
  *        AdaLN fusion, cross-block AdaLN, activation aliasing, byte-identical fallbacks),
  *        "Token 缩减：28% 的去噪时间消减" (horizontal pairing after block 3, bypass,
- *        restore before block 40).
+ *        restore before block 40, before block 30 after the first ten noise evaluations),
+ *        "速度/质量预设矩阵" (denoising steps, velocity reuse, active blocks, core reuse).
  *   [NS] daily.steinslab.io, "零 Python 依赖：Redis 作者的 3.5 秒端侧实验", sections "算力拆解：如何在
  *        M5 Max 上把 16.69 秒压到 12.60 秒" (row-level int8 FC2 option) and "极简主控逻辑"
  *        (spatial rotary positions).

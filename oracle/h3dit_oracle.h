@@ -8,7 +8,7 @@
  *   [RV]  alphalab.site, "h3-metal 把 MiniMax-H3 搬上 Apple Silicon：突破與代價（2026）"
  *   [DD]  linlog.top article 1265 (h3.c deep dive), sections
  *         "MiniMax H3：原生音频视频一体化生成", "h3.c 的核心设计", "int8 量化：从 36 秒到 19 秒",
- *         "DiT 融合内核：减少全局内存往返", "Token 缩减：28% 的去噪时间消减"
+ *         "DiT 融合内核：减少全局内存往返", "Token 缩减：28% 的去噪时间消减", "速度/质量预设矩阵"
  *   [NS]  daily.steinslab.io, "零 Python 依赖：Redis 作者的 3.5 秒端侧实验"
  * The pages describe the block in words only; widths, the activation, eps, the
  * rotary split and every rounding point are readings, each stated where it is used.
