@@ -334,8 +334,9 @@ def time_denoise(w, blocks, x, seed, channels=128):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single "
-              "MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this path runs on a single "
+              "MI355X (sharding tokens by video rows with a K/V all-gather per block is the multi-GPU design, "
+              "not built here).", file=sys.stderr)
         sys.exit(2)
     import torch
     import synth
