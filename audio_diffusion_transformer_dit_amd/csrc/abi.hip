@@ -49,8 +49,11 @@ int check_dims(const h3dit_dims *D, const h3dit_layout *L, int precision) {
       L->rope_t + L->rope_h + L->rope_w != D->head_dim || !(L->rope_theta > 0.0f))
     return H3DIT_EINVAL;
   if (L->mod_sets != 0 && L->mod_sets != 1 && L->mod_sets != 3) return H3DIT_EINVAL;
-  // 32-bit buffer offsets inside the kernels
-  if ((int64_t)D->n_tokens * D->mlp * 2 >= ((int64_t)1 << 31)) return H3DIT_EINVAL;
+  // 32-bit buffer offsets inside the kernels: the widest activation ([N][mlp] or the
+  // token-major [N][3d] projection) and the largest weight ([mlp][d], [3d][d]) in bf16
+  const int64_t widest = D->mlp > 3 * (int64_t)D->hidden ? D->mlp : 3 * (int64_t)D->hidden;
+  if ((int64_t)D->n_tokens * widest * 2 >= ((int64_t)1 << 31)) return H3DIT_EINVAL;
+  if (widest * D->hidden * 2 >= ((int64_t)1 << 31)) return H3DIT_EINVAL;
   return H3DIT_OK;
 }
 

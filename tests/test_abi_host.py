@@ -348,3 +348,28 @@ def test_velocity_step_and_denoise_validation():
     assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(opts), dt, a, C.byref(head), None, a, None, 0, a,
                                  C.byref(small), None) == h3.EWORKSPACE
     assert small.value == size.value
+
+
+def test_sizes_beyond_32bit_offsets_rejected():
+    """The kernels address buffers with 32-bit offsets: widths or token counts whose largest
+    activation or weight reaches 2 GiB are refused before any launch; the largest accepted
+    shapes still answer the size query."""
+    lib = h3.lib()
+    blk = fake_block()
+    size = C.c_size_t(0)
+
+    def query(n_video_w, mlp, hidden=5120, heads=40):
+        w = WORKLOADS[1]
+        layout = h3.layout_of(w)
+        layout.video_t, layout.video_h, layout.video_w = 1, 1, n_video_w
+        layout.n_text, layout.n_audio = 0, 0
+        dims = h3.Dims(n_video_w, hidden, heads, 128, mlp, 1024, 1e-6)
+        return lib.h3dit_block_fwd(C.byref(dims), C.byref(layout), C.byref(blk), None, 0, None, C.byref(size), None)
+
+    assert query(52428, 20480) == 0                   # 52428 * 20480 * 2 < 2^31
+    assert query(52429, 20480) == h3.EINVAL
+    assert query(1024, 262144) == h3.EINVAL           # [mlp][d] weight: 262144 * 5120 * 2 B >= 2^31
+    assert query(1024, 196608) == 0                   # 196608 * 5120 * 2 B < 2^31
+    # a narrow MLP does not hide a wide [N][3d] projection
+    assert query(45000, 256, hidden=8192, heads=64) == h3.EINVAL   # 45000 * 3 * 8192 * 2 B >= 2^31
+    assert query(8192, 256, hidden=8192, heads=64) == 0
