@@ -534,6 +534,42 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   }
 }
 
+// Split-K sum for the bf16 output of the 4-wave 256 x 256 tile: the same segment-order fp32
+// sums and bf16 rounding as the fixup instantiation of k_gemm, spread over one thread per
+// 64-byte partial chunk (a lane's 16 accumulators of one 32 x 32 block) instead of one
+// workgroup per tile, so that the partial tiles are read by the whole chip.
+constexpr int SK_THREADS = 256;
+__global__ __launch_bounds__(SK_THREADS) void k_splitk_bf16(GemmP p, int n_split) {
+  constexpr int FM = 4, FN = 4, PER_TILE = 4 * FM * FN * 64;   // chunks per 256 x 256 tile
+  const int64_t t = (int64_t)blockIdx.x * SK_THREADS + threadIdx.x;
+  if (t >= (int64_t)n_split * PER_TILE) return;
+  const int ti = (int)(t / PER_TILE), rem = (int)(t % PER_TILE);
+  const int wid = rem / (FM * FN * 64), blk = (rem / 64) % (FM * FN), lane = rem % 64;
+  const int i = blk / FN, j = blk % FN;
+  float acc[16];
+  for (int sg = 0; sg < p.split; sg++) {
+    const int64_t slot = (int64_t)ti * p.split + sg;
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(p.part + slot * (256 * 256 * 4) + (int64_t)blk * 4096 +
+                                                       (int64_t)wid * FM * FN * 4096 + lane * 64);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const f32x4 v = src[q];
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc[4 * q + e] = sg == 0 ? v[e] : acc[4 * q + e] + v[e];
+    }
+  }
+  int tm, tn;
+  tile_coords(p.n_dp + ti, tm, tn, p.tiles_m, p.tiles_n);
+  const int wm = wid / 2, wn = wid % 2, hsel = lane >> 5;
+  const int64_t col = (int64_t)tn * 256 + wn * 128 + 32 * j + (lane & 31);
+  uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int64_t row = (int64_t)tm * 256 + wm * 128 + 32 * i + 8 * (r / 4) + 4 * hsel + (r % 4);
+    if (row < p.M) out[row * p.N + col] = f2bf(acc[r]);
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM>
 static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
   p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -545,8 +581,13 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
   k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM, false><<<grid, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
   if constexpr (!GROUPED && BN == 256) {
     if (pl.n_split > 0) {
-      k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM, true>
-          <<<(unsigned)pl.n_split, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+      if constexpr (!INT8 && OUT == H3DIT_OUT_BF16 && WGM == 2 && WGN == 2) {
+        const int64_t chunks = (int64_t)pl.n_split * 4 * 16 * 64;
+        k_splitk_bf16<<<(unsigned)((chunks + SK_THREADS - 1) / SK_THREADS), SK_THREADS, 0, st>>>(p, pl.n_split);
+      } else {
+        k_gemm<BM, BN, WGM, WGN, INT8, OUT, GROUPED, HM, true>
+            <<<(unsigned)pl.n_split, GemmCfg<BM, BN, WGM, WGN>::NT, 0, st>>>(p);
+      }
     }
   }
   return hipGetLastError();
