@@ -15,7 +15,8 @@
 //    stalls the schedule is explicit: slice k+1's LDS stores and slice k+2's loads are spread
 //    between the MFMAs of slice k, and the per-slice barrier sits before the last K step so
 //    that the next slice's first fragments are read under that step's MFMAs.
-//  * int8 (and the 256 x 128 shape): 8 waves (two per SIMD) of 128 x 64; while slice k is
+//  * int8 (and the 256 x 128 shape): 8 waves (two per SIMD) of 128 x 64 (the grouped int8
+//    FC2: 4-wave 128 x 128 tiles of 64 x 64, two workgroups per CU); while slice k is
 //    multiplied, slice k+1 is stored to the other LDS stage at the top of the iteration and
 //    the loads of slice k+3 are spread between the MFMAs, so each load has more than a whole
 //    iteration to arrive.
@@ -92,7 +93,7 @@ __device__ __forceinline__ u32x4 lds_frag(const uint8_t *base, int row, int chun
 // HM: A is the head-major attention output [K/hd][M][hd] (bf16 only).  FIX: the split-K fixup
 // launch (sums partial tiles and runs the epilogue; its own kernel so that profiles separate it).
 template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM, bool FIX>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
+__global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1) void k_gemm(GemmP p) {
   using C = GemmCfg<BM, BN, WGM, WGN>;
   constexpr int FM = C::FM, FN = C::FN, NW = C::NW, NT = C::NT, LA = C::LA, LW = C::LW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -223,8 +224,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
           acc[i][j] = sg == 0 ? val : acc[i][j] + val;
         }
   } else {
-  if constexpr (NW == 4) {
-    static_assert(!GROUPED, "grouped int8 keeps the 8-wave tiles");
+  if constexpr (NW == 4 && !GROUPED) {
     // One wave per SIMD, 128 x 128 each (accumulators in AGPRs): a third fewer LDS bytes per
     // MFMA than 8 waves of 128 x 64.  Iteration kt: MFMA steps 0..3 of slice kt from stage
     // kt&1 with fragments read one step ahead; the register set holding slice kt+1 goes to
@@ -602,7 +602,7 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
 //     ceil(segments / kCUs) / split, plus the partial tiles (measured on MI355X: ~50 us for
 //     64 tiles x 4 segments, modelled as 16 us per round of segments + 10 us + 6 us per
 //     segment read back by the fixup launch).
-// The grouped int8 FC2 keeps 256 x 128 tiles (its second accumulator set does not fit 256 wide).
+// The grouped int8 FC2 uses 128 x 128 tiles (its second accumulator set does not fit 256 wide).
 constexpr int kCUs = 256;
 
 LinearPlan plan_linear(const h3dit_linear_args &a) {
@@ -620,6 +620,7 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
   pl.part_bytes = 0;
   pl.bn = 128;
   pl.n_dp = (int)(tm * (a.N / 128));
+  if (grouped) pl.n_dp = (int)((a.M + 127) / 128 * (a.N / 128));   // 128 x 128 tiles
   if (!wide) return pl;
   const int64_t tiles = tm * (a.N / 256), full = tiles / kCUs, rem = tiles % kCUs;
   const double t_tile_us = (double)KT * 128 * 0.0277 / 2;   // one 256 x 256 tile over the whole K
@@ -651,9 +652,9 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
 template <bool INT8, int OUT, bool GROUPED, bool HM = false>
 static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st) {
   if constexpr (GROUPED) {
-    // two accumulator sets (int32 per group, fp32 across groups) per lane: 256 x 128 tiles,
-    // 8 waves of 64 x 64
-    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, false>(p, pl, st);
+    // two accumulator sets (int32 per group, fp32 across groups) per lane: 128 x 128 tiles of
+    // 4 waves of 64 x 64, two workgroups per CU (1280 tiles at 4096 x 5120: whole rounds)
+    return run_gemm<128, 128, 2, 2, INT8, OUT, GROUPED, false>(p, pl, st);
   } else {
     // bf16: four waves of 128 x 128; int8: eight waves of 128 x 64 (measured faster for int8)
     if (pl.bn == 256) {
