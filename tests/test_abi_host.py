@@ -373,3 +373,33 @@ def test_sizes_beyond_32bit_offsets_rejected():
     # a narrow MLP does not hide a wide [N][3d] projection
     assert query(45000, 256, hidden=8192, heads=64) == h3.EINVAL   # 45000 * 3 * 8192 * 2 B >= 2^31
     assert query(8192, 256, hidden=8192, heads=64) == 0
+
+
+def test_denoise_plan_random_options_agree_with_oracle():
+    """Random option sets: the library's plan and the oracle's agree step for step, and both
+    reject the same invalid requests."""
+    import random
+    import oracle
+    rng = random.Random(2026)
+    for _ in range(400):
+        steps = rng.randint(1, 60)
+        reuse = rng.randint(0, 5)
+        core = rng.randint(0, 6)
+        red = rng.choice([-1, -1, 0, 1, 3, 5])
+        early, late = rng.randint(0, 50), rng.randint(0, 50)
+        n_early = rng.randint(-1, 20)
+        layers = 50
+        opts = h3.denoise_opts(steps, reuse, core, layers, red, early, late, n_early)
+        arr = (h3.DenoiseStep * steps)()
+        rc = h3.lib().h3dit_denoise_plan(C.byref(opts), 50, arr)
+        try:
+            ref = oracle.denoise_plan(steps, reuse, core, red, early, late, n_early)
+        except ValueError:
+            ref = None
+        if ref is None:
+            assert rc == h3.EINVAL, (steps, reuse, core, red, early, late, n_early)
+            continue
+        assert rc == sum(s["core"] for s in ref)
+        for i, r in enumerate(ref):
+            assert (arr[i].fresh, arr[i].core, arr[i].eval, arr[i].restore_before) == \
+                (r["fresh"], r["core"], r["eval"], r["restore"])
