@@ -1,8 +1,9 @@
-"""Whole-stack parity at the headline size: the 50-block stack over 4096 tokens (d 5120,
-40x128 heads, MLP 20480), GPU against the CPU oracle.  Test infrastructure, run by hand in
+"""Whole-stack parity at the production sizes: the 50-block stack over 4096 tokens (d 5120,
+40x128 heads, MLP 20480; or another workload, e.g. 8192 tokens with token reduction), GPU
+against the CPU oracle.  Test infrastructure, run by hand in
 two phases because the oracle needs about half an hour of 16 CPU cores for 146 TFLOP:
 
-  python tests/full_stack_parity.py gpu OUT.pt [--int8] [--blocks B]
+  python tests/full_stack_parity.py gpu OUT.pt [--int8] [--blocks B] [--workload W]
                                                            # on an MI355X: the library's stack,
                                                            # launched as the benchmark launches it
   python tests/full_stack_parity.py oracle OUT.pt          # on any host: the oracle block by block
@@ -30,23 +31,24 @@ import synth  # noqa: E402
 WORKLOAD = 3
 
 
-def gpu_phase(path, int8, n_blocks=None):
+def gpu_phase(path, int8, n_blocks=None, workload=WORKLOAD):
     """The library's stack over the first n_blocks blocks (all by default), and the same stack
     from x with one element moved by one bf16 step: how far the two outputs end up apart is the
     sensitivity of the computation itself to one rounding-sized change, stored with the output."""
     import audio_diffusion_transformer_dit_amd as h3
     from parity import relerr
     dev = torch.device("cuda:0")
-    w = synth.WORKLOADS[WORKLOAD]
+    w = synth.WORKLOADS[workload]
     if n_blocks is not None:
         w = w.replace(blocks=n_blocks)
-    seed = synth.seed_for(WORKLOAD)
+    seed = synth.seed_for(workload)
+    red = (w.reduce_after, w.restore_before) if w.reduce_after >= 0 else None
     x = synth.make_x(w, seed, dev)
     blocks = []
     for b in range(w.blocks):
         p = synth.make_block(w, seed, b, dev)
         blocks.append(h3.quantize_block(p) if int8 else p)
-    stack = h3.Stack(w, blocks)
+    stack = h3.Stack(w, blocks, reduction=red)
     ws = h3.alloc_workspace(stack.workspace_bytes, dev)
     x0 = x.clone()
     stack(x, ws)
@@ -61,7 +63,7 @@ def gpu_phase(path, int8, n_blocks=None):
         noise_rel, noise_upd = relerr(xp, x), float((dp - du).abs().mean() / du.abs().mean())
         print(f"one-step input perturbation after {w.blocks} blocks ({'int8' if int8 else 'bf16'}): residual rel err "
               f"{noise_rel:.3e}, mean rel err of the total update {noise_upd:.3e}", flush=True)
-    torch.save({"workload": WORKLOAD, "int8": int8, "blocks": w.blocks, "x_out": x.cpu(), "noise_rel": noise_rel,
+    torch.save({"workload": workload, "int8": int8, "blocks": w.blocks, "x_out": x.cpu(), "noise_rel": noise_rel,
                 "noise_upd": noise_upd}, path)
     print(f"gpu stack ({'int8' if int8 else 'bf16'}, {w.blocks} blocks, N={w.n_tokens}) written to {path}", flush=True)
 
@@ -76,18 +78,34 @@ def oracle_phase(path, first=0, last=None, state=None):
     seed = synth.seed_for(saved["workload"])
     last = saved["blocks"] if last is None else last
     x0 = synth.make_x(w, seed)
-    x = torch.load(state, weights_only=True)["x"] if first > 0 else x0
+    # token reduction as the stack runs it: pair after block reduce_after (x stays as the
+    # bypass, r is the reduced input, z the reduced residual), restore before block
+    # restore_before or after the last block
+    ra, rb = (w.reduce_after, w.restore_before) if w.reduce_after >= 0 else (-1, -1)
+    cr, sr = oracle.rope_tables(w, reduced=True) if ra >= 0 else (None, None)
+    st = torch.load(state, weights_only=True) if first > 0 else {"x": x0, "z": None, "r": None}
+    x, z, r = st["x"], st["z"], st["r"]
     t0 = time.time()
     for b in range(first, last):
+        if z is not None and b == rb:
+            x, z, r = oracle.token_restore(w, x, z, r), None, None
         p = synth.make_block(w, seed, b)
         if saved["int8"]:
             p = oracle.quantize_block(p)
-        x = oracle.block_fwd(w, p, x, fused=True)
+        if z is not None:
+            z = oracle.block_fwd(w, p, z, cr, sr, fused=True)
+        else:
+            x = oracle.block_fwd(w, p, x, fused=True)
+        if b == ra:
+            r = oracle.token_pair(w, x)
+            z = r
         print(f"oracle block {b + 1}/{saved['blocks']} done, {time.time() - t0:.0f} s", flush=True)
     if state is not None:
-        torch.save({"x": x, "next_block": last}, state)
+        torch.save({"x": x, "z": z, "r": r, "next_block": last}, state)
     if last < saved["blocks"]:
         return 0
+    if z is not None:
+        x = oracle.token_restore(w, x, z, r)
     g = saved["x_out"]
     err = relerr(g, x)
     du, dr = g.double() - x0.double(), x.double() - x0.double()
@@ -103,7 +121,7 @@ def oracle_phase(path, first=0, last=None, state=None):
           f"perturbation on the GPU: {saved.get('noise_rel', float('nan')):.3e} / "
           f"{saved.get('noise_upd', float('nan')):.3e}: {'ok' if ok else 'FAIL'}", flush=True)
     if state is None:
-        torch.save({"x": x, "next_block": last}, path + ".oracle")
+        torch.save({"x": x, "z": None, "r": None, "next_block": last}, path + ".oracle")
     return 0 if ok else 1
 
 
@@ -113,7 +131,8 @@ if __name__ == "__main__":
         sys.exit(2)
     if sys.argv[1] == "gpu":
         nb = int(sys.argv[sys.argv.index("--blocks") + 1]) if "--blocks" in sys.argv else None
-        gpu_phase(sys.argv[2], "--int8" in sys.argv, nb)
+        wl = int(sys.argv[sys.argv.index("--workload") + 1]) if "--workload" in sys.argv else WORKLOAD
+        gpu_phase(sys.argv[2], "--int8" in sys.argv, nb, wl)
     else:
         args = sys.argv[3:]
         first = int(args[args.index("--from") + 1]) if "--from" in args else 0
