@@ -3,11 +3,12 @@
 against the CPU oracle.  Test infrastructure, run by hand in
 two phases because the oracle needs about half an hour of 16 CPU cores for 146 TFLOP:
 
-  python tests/full_stack_parity.py gpu OUT.pt [--int8] [--blocks B] [--workload W]
+  python tests/full_stack_parity.py gpu OUT.pt [--int8] [--blocks B] [--workload W] [--half H]
+  python tests/full_stack_parity.py join OUT.pt HALF0.pt HALF1.pt
                                                            # on an MI355X: the library's stack,
                                                            # launched as the benchmark launches it
   python tests/full_stack_parity.py oracle OUT.pt          # on any host: the oracle block by block
-      [--from B --to E --state S.pt]                       # (in sittings: blocks [B, E), residual in S.pt)
+      [--from B --to E --state S.pt] [--gen-device cuda]   # (in sittings: blocks [B, E), residual in S.pt)
 
 Both phases draw the same seeded inputs and weights (synth is bit-exact across devices).  The
 oracle runs the blocks one at a time, which equals its fused stack bit for bit (pinned in
@@ -31,7 +32,7 @@ import synth  # noqa: E402
 WORKLOAD = 3
 
 
-def gpu_phase(path, int8, n_blocks=None, workload=WORKLOAD):
+def gpu_phase(path, int8, n_blocks=None, workload=WORKLOAD, half=None):
     """The library's stack over the first n_blocks blocks (all by default), and the same stack
     from x with one element moved by one bf16 step: how far the two outputs end up apart is the
     sensitivity of the computation itself to one rounding-sized change, stored with the output."""
@@ -63,14 +64,21 @@ def gpu_phase(path, int8, n_blocks=None, workload=WORKLOAD):
         noise_rel, noise_upd = relerr(xp, x), float((dp - du).abs().mean() / du.abs().mean())
         print(f"one-step input perturbation after {w.blocks} blocks ({'int8' if int8 else 'bf16'}): residual rel err "
               f"{noise_rel:.3e}, mean rel err of the total update {noise_upd:.3e}", flush=True)
-    torch.save({"workload": workload, "int8": int8, "blocks": w.blocks, "x_out": x.cpu(), "noise_rel": noise_rel,
-                "noise_upd": noise_upd}, path)
+    out = x.cpu()
+    if half is not None:   # one half of the rows (a result file must stay small enough to copy back)
+        lo, hi = (0, w.n_tokens // 2) if half == 0 else (w.n_tokens // 2, w.n_tokens)
+        out = out[lo:hi].clone()
+    torch.save({"workload": workload, "int8": int8, "blocks": w.blocks, "x_out": out, "noise_rel": noise_rel,
+                "noise_upd": noise_upd, "half": half}, path)
     print(f"gpu stack ({'int8' if int8 else 'bf16'}, {w.blocks} blocks, N={w.n_tokens}) written to {path}", flush=True)
 
 
-def oracle_phase(path, first=0, last=None, state=None):
+def oracle_phase(path, first=0, last=None, state=None, gen_device="cpu"):
     """Blocks [first, last) of the oracle chain; with `state`, the residual is read from it
-    (first > 0) and written back to it, so the chain can run in several sittings."""
+    (first > 0) and written back to it, so the chain can run in several sittings.  Inside the
+    token-reduced span the state holds only the reduced residual: the bypass and the reduced
+    input are derived again by rerunning the blocks up to the pairing.  gen_device: where
+    synth draws the inputs (bit-identical on any device; the arithmetic stays in the oracle)."""
     import oracle
     from parity import BF16_TOL, relerr
     saved = torch.load(path, weights_only=True)
@@ -83,15 +91,24 @@ def oracle_phase(path, first=0, last=None, state=None):
     # restore_before or after the last block
     ra, rb = (w.reduce_after, w.restore_before) if w.reduce_after >= 0 else (-1, -1)
     cr, sr = oracle.rope_tables(w, reduced=True) if ra >= 0 else (None, None)
+    def block(b):
+        p = {k: v.cpu() for k, v in synth.make_block(w, seed, b, gen_device).items()}
+        return oracle.quantize_block(p) if saved["int8"] else p
+
     st = torch.load(state, weights_only=True) if first > 0 else {"x": x0, "z": None, "r": None}
     x, z, r = st["x"], st["z"], st["r"]
     t0 = time.time()
+    if z is not None and x is None:
+        # resume inside the reduced span: bypass = the residual after block reduce_after
+        x = x0
+        for b in range(ra + 1):
+            x = oracle.block_fwd(w, block(b), x, fused=True)
+        r = oracle.token_pair(w, x)
+        print(f"bypass and reduced input derived again ({ra + 1} blocks), {time.time() - t0:.0f} s", flush=True)
     for b in range(first, last):
         if z is not None and b == rb:
             x, z, r = oracle.token_restore(w, x, z, r), None, None
-        p = synth.make_block(w, seed, b)
-        if saved["int8"]:
-            p = oracle.quantize_block(p)
+        p = block(b)
         if z is not None:
             z = oracle.block_fwd(w, p, z, cr, sr, fused=True)
         else:
@@ -101,7 +118,8 @@ def oracle_phase(path, first=0, last=None, state=None):
             z = r
         print(f"oracle block {b + 1}/{saved['blocks']} done, {time.time() - t0:.0f} s", flush=True)
     if state is not None:
-        torch.save({"x": x, "z": z, "r": r, "next_block": last}, state)
+        inside = z is not None
+        torch.save({"x": None if inside else x, "z": z, "r": None, "next_block": last}, state)
     if last < saved["blocks"]:
         return 0
     if z is not None:
@@ -126,16 +144,24 @@ def oracle_phase(path, first=0, last=None, state=None):
 
 
 if __name__ == "__main__":
-    if len(sys.argv) < 3 or sys.argv[1] not in ("gpu", "oracle"):
+    if len(sys.argv) < 3 or sys.argv[1] not in ("gpu", "oracle", "join"):
         print(__doc__)
         sys.exit(2)
     if sys.argv[1] == "gpu":
         nb = int(sys.argv[sys.argv.index("--blocks") + 1]) if "--blocks" in sys.argv else None
         wl = int(sys.argv[sys.argv.index("--workload") + 1]) if "--workload" in sys.argv else WORKLOAD
-        gpu_phase(sys.argv[2], "--int8" in sys.argv, nb, wl)
+        hf = int(sys.argv[sys.argv.index("--half") + 1]) if "--half" in sys.argv else None
+        gpu_phase(sys.argv[2], "--int8" in sys.argv, nb, wl, hf)
+    elif sys.argv[1] == "join":
+        # join the two halves written with --half 0 and --half 1 into one result file
+        a, b = (torch.load(f, weights_only=True) for f in sys.argv[3:5])
+        assert (a["half"], b["half"]) == (0, 1) and a["noise_rel"] == b["noise_rel"]
+        a["x_out"], a["half"] = torch.cat([a["x_out"], b["x_out"]]), None
+        torch.save(a, sys.argv[2])
     else:
         args = sys.argv[3:]
         first = int(args[args.index("--from") + 1]) if "--from" in args else 0
         last = int(args[args.index("--to") + 1]) if "--to" in args else None
         state = args[args.index("--state") + 1] if "--state" in args else None
-        sys.exit(oracle_phase(sys.argv[2], first, last, state))
+        gen = args[args.index("--gen-device") + 1] if "--gen-device" in args else "cpu"
+        sys.exit(oracle_phase(sys.argv[2], first, last, state, gen))
