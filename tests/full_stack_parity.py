@@ -103,6 +103,7 @@ def oracle_phase(path, first=0, last=None, state=None, gen_device="cpu"):
         x = x0
         for b in range(ra + 1):
             x = oracle.block_fwd(w, block(b), x, fused=True)
+            print(f"bypass: block {b + 1}/{ra + 1} again, {time.time() - t0:.0f} s", flush=True)
         r = oracle.token_pair(w, x)
         print(f"bypass and reduced input derived again ({ra + 1} blocks), {time.time() - t0:.0f} s", flush=True)
     for b in range(first, last):
