@@ -562,18 +562,16 @@ int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h
     int64_t r0, n;
     uint16_t *out;
   } parts[2] = {{video, 0, n_video, out_video}, {audio, N - n_audio, n_audio, out_audio}};
-  size_t h_bytes = 0, sk_bytes = 0;
+  // per-row LayerNorm statistics (mean, 1/sqrt(var + eps)); the normalised rows themselves
+  // are formed inside the head GEMM's tile loads and never stored
+  size_t st_bytes = 0;
   for (const Part &q : parts) {
     if (!q.p) continue;
     if (!q.p->mod || !q.p->w || !aligned(q.p->mod, 16) || !aligned(q.p->w, 16)) return H3DIT_EINVAL;
     if (q.p->channels < 128 || q.p->channels % 128) return H3DIT_EINVAL;
-    h3dit_linear_args la{};
-    la.M = q.n; la.N = q.p->channels; la.K = d; la.precision = H3DIT_BF16; la.out_kind = H3DIT_OUT_BF16;
-    const size_t sk = linear_workspace(la);
-    if (sk > sk_bytes) sk_bytes = sk;
-    if ((size_t)(q.n * d * 2) > h_bytes) h_bytes = (size_t)(q.n * d * 2);
+    if ((size_t)q.n * 8 > st_bytes) st_bytes = (size_t)q.n * 8;
   }
-  const size_t h_off = 0, sk_off = up(h_bytes), total = sk_off + up(sk_bytes);
+  const size_t total = up(st_bytes);
   if (!workspace) {
     *workspace_bytes = total;
     return H3DIT_OK;
@@ -586,19 +584,13 @@ int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h
     return H3DIT_EWORKSPACE;
   }
   if ((rc = check_device())) return rc;
-  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
-  uint16_t *h = reinterpret_cast<uint16_t *>(ws + h_off);
+  float *stats = reinterpret_cast<float *>(workspace);
   const hipStream_t st = (hipStream_t)stream;
   for (const Part &q : parts) {
     if (!q.p || q.n == 0) continue;
-    // AdaLN of the modality's rows, read in place at their offset in the residual
-    TRY(launch_row(q.n, (int)d, dims->ln_eps, x + q.r0 * d, nullptr, nullptr, nullptr, q.p->mod, q.p->mod + d, h,
-                   nullptr, nullptr, st));
-    h3dit_linear_args la{};
-    la.M = q.n; la.N = q.p->channels; la.K = d; la.precision = H3DIT_BF16; la.out_kind = H3DIT_OUT_BF16;
-    la.a = h; la.w = q.p->w; la.out = q.out;
-    la.workspace = ws + sk_off; la.workspace_bytes = sk_bytes;
-    TRY(launch_linear(la, st));
+    // the modality's rows are read in place at their offset in the residual
+    TRY(launch_row_stats(q.n, (int)d, dims->ln_eps, x + q.r0 * d, stats, st));
+    TRY(launch_head_gemm(q.n, q.p->channels, (int)d, x + q.r0 * d, stats, q.p->mod, q.p->mod + d, q.p->w, q.out, st));
   }
   return H3DIT_OK;
 }

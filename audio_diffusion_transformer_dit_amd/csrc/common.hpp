@@ -112,6 +112,13 @@ hipError_t launch_row(int64_t n, int d, float eps, const uint16_t *x, const uint
                       const uint16_t *y, uint16_t *x_out, const uint16_t *shift, const uint16_t *scale,
                       uint16_t *h, int8_t *q, float *s, hipStream_t st, int64_t seg1 = 0, int64_t seg2 = 0,
                       int64_t set_stride = 0);
+// LayerNorm statistics of n rows: stats[2 r] = mean, stats[2 r + 1] = 1/sqrt(var + eps), as
+// launch_row's normalisation computes them
+hipError_t launch_row_stats(int64_t n, int d, float eps, const uint16_t *x, float *stats, hipStream_t st);
+// out = bf16(h W^T) with h = bf16(AdaLN(x; shift, scale)) formed while the A tiles are loaded,
+// from the row statistics above (x [n][d], W [c][d], out [n][c]; d % 64 == 0, c % 128 == 0)
+hipError_t launch_head_gemm(int64_t n, int c, int d, const uint16_t *x, const float *stats, const uint16_t *shift,
+                            const uint16_t *scale, const uint16_t *w, uint16_t *out, hipStream_t st);
 hipError_t launch_quant_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v, int hm_hd,
                              int8_t *q, float *s, hipStream_t st);
 hipError_t launch_gelu(int64_t count, const uint16_t *u, uint16_t *gl, hipStream_t st);

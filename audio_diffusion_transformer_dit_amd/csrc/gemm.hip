@@ -570,6 +570,108 @@ __global__ __launch_bounds__(SK_THREADS) void k_splitk_bf16(GemmP p, int n_split
   }
 }
 
+// Final head with its AdaLN applied while the A tiles are loaded ([DD] "DiT 融合内核": the bf16
+// head applies AdaLN as it loads its projection tiles, so no normalised copy of the rows is
+// stored).  A 128 x 128 output tile per workgroup, 4 waves of 64 x 64, K in 64-element slices
+// through one LDS stage.  Each A chunk of 8 values becomes bf16(((x - mean) * rstd) *
+// (1 + scale) + shift) with the row statistics of launch_row_stats, exactly the values the
+// row kernel would store, and the K order of the MFMAs is that of k_gemm, so the output
+// equals the two-kernel form byte for byte.  The head is a small GEMM (N = latent channels).
+constexpr int HT = 128;
+__global__ __launch_bounds__(256) void k_head_gemm(int64_t M, int N, int K, const uint16_t *__restrict__ x,
+                                                   const float *__restrict__ stats,
+                                                   const uint16_t *__restrict__ shift,
+                                                   const uint16_t *__restrict__ scale,
+                                                   const uint16_t *__restrict__ w, uint16_t *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t sa[HT * GKB];
+  __shared__ __attribute__((aligned(16))) uint8_t sb[HT * GKB];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wm = wid >> 1, wn = wid & 1, hsel = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.x * HT;
+  const int64_t n0 = (int64_t)blockIdx.y * HT;
+  // loads: thread = (row r = tid / 8 + 32 i, 16-byte chunk c = tid % 8) of the slice, i < 4
+  const int c = tid & 7, rb = tid >> 3;
+  float mu[4], rs[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int64_t row = m0 + rb + 32 * i;
+    mu[i] = row < M ? stats[2 * row] : 0.0f;
+    rs[i] = row < M ? stats[2 * row + 1] : 0.0f;
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) acc[i][j] = f32x16{0};
+  const int KT = K / 64;
+  for (int kt = 0; kt < KT; kt++) {
+    const int64_t k0 = (int64_t)kt * 64 + c * 8;
+    u32x4 av[4], wv[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t row = m0 + rb + 32 * i;
+      av[i] = row < M ? *reinterpret_cast<const u32x4 *>(x + row * K + k0) : u32x4{0, 0, 0, 0};
+      wv[i] = *reinterpret_cast<const u32x4 *>(w + (n0 + rb + 32 * i) * K + k0);
+    }
+    float sh[8], sc[8];
+    unpack8(*reinterpret_cast<const u32x4 *>(shift + k0), sh);
+    unpack8(*reinterpret_cast<const u32x4 *>(scale + k0), sc);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      float v[8];
+      unpack8(av[i], v);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        float t = (v[e] - mu[i]) * rs[i];
+        t = t * (1.0f + sc[e]) + sh[e];
+        v[e] = t;
+      }
+      av[i] = pack8(v);
+    }
+    __syncthreads();   // the previous slice's fragments have been read
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = rb + 32 * i;
+      const int slot = (c ^ ((r >> 1) & 7)) << 4;
+      *reinterpret_cast<u32x4 *>(sa + r * GKB + slot) = av[i];
+      *reinterpret_cast<u32x4 *>(sb + r * GKB + slot) = wv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      u32x4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) fa[i] = lds_frag(sa, wm * 64 + 32 * i + (lane & 31), 2 * ks + hsel);
+#pragma unroll
+      for (int j = 0; j < 2; j++) fb[j] = lds_frag(sb, wn * 64 + 32 * j + (lane & 31), 2 * ks + hsel);
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[i]),
+                                                              __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (r / 4) + 4 * hsel + (r % 4);
+        const int64_t col = n0 + wn * 64 + 32 * j + (lane & 31);
+        if (row < M) out[row * N + col] = f2bf(acc[i][j][r]);
+      }
+}
+
+hipError_t launch_head_gemm(int64_t n, int c, int d, const uint16_t *x, const float *stats, const uint16_t *shift,
+                            const uint16_t *scale, const uint16_t *w, uint16_t *out, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (d % 64 || c % HT) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((n + HT - 1) / HT), (unsigned)(c / HT));
+  k_head_gemm<<<grid, 256, 0, st>>>(n, c, d, x, stats, shift, scale, w, out);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM>
 static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
   p.tiles_m = (int)((p.M + BM - 1) / BM);

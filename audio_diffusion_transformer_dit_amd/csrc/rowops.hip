@@ -45,7 +45,7 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 // this kernel, so the fused and the two-kernel sequences give the same bytes.
 // Modulation sets: rows [0, seg1) use gate/shift/scale as given, rows [seg1, seg2) the vectors
 // set_stride elements further, rows from seg2 on 2*set_stride further (set_stride 0: one set).
-template <bool GATE, bool NORM>
+template <bool GATE, bool NORM, bool STATS = false>
 __global__ __launch_bounds__(ROW_THREADS) void k_row(int d, float eps, const uint16_t *__restrict__ x,
                                                      const uint16_t *__restrict__ gate,
                                                      const uint16_t *__restrict__ y, uint16_t *x_out,
@@ -104,6 +104,15 @@ __global__ __launch_bounds__(ROW_THREADS) void k_row(int d, float eps, const uin
         }
     const float var = block_sum<ROW_THREADS / 64>(part, red) / (float)d;
     const float rs = 1.0f / sqrtf(var + eps);
+    if constexpr (STATS) {
+      // statistics only (for a consumer that applies the modulation itself): s[2 row] = mean,
+      // s[2 row + 1] = 1 / sqrt(var + eps), the very values the modulation below uses
+      if (tid == 0) {
+        s[2 * row] = mu;
+        s[2 * row + 1] = rs;
+      }
+      return;
+    }
     const u32x4 *shr = reinterpret_cast<const u32x4 *>(shift);
     const u32x4 *scr = reinterpret_cast<const u32x4 *>(scale);
     float amax = 0.0f;
@@ -156,6 +165,13 @@ hipError_t launch_row(int64_t n, int d, float eps, const uint16_t *x, const uint
   else
     k_row<false, true><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s, seg1, seg2,
                                                set_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats(int64_t n, int d, float eps, const uint16_t *x, float *stats, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  k_row<false, true, true><<<(unsigned)n, ROW_THREADS, 0, st>>>(d, eps, x, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                                 nullptr, nullptr, stats, n, n, 0);
   return hipGetLastError();
 }
 

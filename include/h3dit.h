@@ -185,11 +185,15 @@ typedef struct {
 } h3dit_head_part;
 
 /* Final head after the stack ([DD] "DiT 融合内核", final audio/video AdaLN bound to the residual
- * stream): for the video rows [0, n_video) and the audio rows (the last n_audio) of x,
- * out = bf16(h W^T) with h = bf16(AdaLN(x_rows; shift, scale)) (as h3dit_block_fwd's AdaLN), no
- * bias.  The rows are read in place (no slice copies).  video / audio: NULL to skip that part;
- * out_video bf16 [n_video][video->channels], out_audio bf16 [n_audio][audio->channels] (device).
- * workspace as in h3dit_block_fwd (NULL queries the size).  x is not modified. */
+ * stream, the bf16 head applying AdaLN while it loads its projection tiles): for the video rows
+ * [0, n_video) and the audio rows (the last n_audio) of x, out = bf16(h W^T) with
+ * h = bf16(AdaLN(x_rows; shift, scale)) (as h3dit_block_fwd's AdaLN), no bias.  The rows are
+ * read in place (no slice copies) and h is formed inside the GEMM's tile loads, never stored:
+ * the workspace holds only each row's mean and 1/sqrt(var + eps) (8 bytes per row).  The output
+ * equals h3dit_row_gate_adaln followed by h3dit_linear byte for byte.  video / audio: NULL to
+ * skip that part; out_video bf16 [n_video][video->channels], out_audio bf16
+ * [n_audio][audio->channels] (device).  workspace as in h3dit_block_fwd (NULL queries the
+ * size).  x is not modified. */
 H3DIT_API int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,
                                const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video,
                                uint16_t *out_audio, void *workspace, size_t *workspace_bytes, void *stream);

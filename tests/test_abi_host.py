@@ -282,7 +282,8 @@ def test_final_head_validation_and_workspace():
     d, l = C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w))
     assert lib.h3dit_final_head(d, l, C.byref(good), None, None, None, None, None, C.byref(size), None) == 0
     n_video = w.n_tokens - w.n_text - w.n_audio
-    assert size.value >= n_video * w.hidden * 2
+    # only the row statistics: the normalised rows are formed in the GEMM's tile loads
+    assert n_video * 8 <= size.value < n_video * w.hidden * 2
     assert lib.h3dit_final_head(d, l, C.byref(bad), None, None, None, None, None, C.byref(size), None) == h3.EINVAL
     assert lib.h3dit_final_head(d, l, None, None, None, None, None, None, C.byref(size), None) == 0
     small = C.c_size_t(16)
