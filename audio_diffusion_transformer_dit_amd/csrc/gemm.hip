@@ -701,9 +701,11 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
 //   256 x 256 tiles: rounds = ceil(tiles / kCUs);
 //   256 x 128 tiles: rounds of half tiles, each ~0.52 of a whole one;
 //   256 x 256 with the last partial round cut into `split` K segments: full rounds +
-//     ceil(segments / kCUs) / split, plus the partial tiles (measured on MI355X: ~50 us for
-//     64 tiles x 4 segments, modelled as 16 us per round of segments + 10 us + 6 us per
-//     segment read back by the fixup launch).
+//     ceil(segments / kCUs) / split, plus the partial tiles: 16 us per round of segments
+//     for their fp32 stores, then the sum.  A fixup launch of one workgroup per split tile
+//     (measured on MI355X: ~50 us in all for 64 tiles x 4 segments) is modelled as 10 us +
+//     6 us per segment; the chip-wide sum of the bf16 4-wave form reads the partials at
+//     about 5 TB/s (13.6 us for 64 x 4 segments), modelled as 3 us + 0.05 us per segment.
 // The grouped int8 FC2 uses 128 x 128 tiles (its second accumulator set does not fit 256 wide).
 constexpr int kCUs = 256;
 
@@ -728,12 +730,14 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
   const double t_tile_us = (double)KT * 128 * 0.0277 / 2;   // one 256 x 256 tile over the whole K
   const double c256 = (double)(full + (rem ? 1 : 0));
   const double c128 = (double)((2 * tiles + kCUs - 1) / kCUs) * 0.52;
+  const bool chip_sum = !i8 && a.out_kind == H3DIT_OUT_BF16;
   double best = c256;
   int best_s = 1;
   for (int sp = 2; sp <= 8 && rem; sp++) {
     if (KT % sp || KT / sp < 2) continue;
     const int64_t seg_rounds = (rem * sp + kCUs - 1) / kCUs;
-    const double cost = (double)full + (double)seg_rounds / sp + (16.0 * seg_rounds + 10.0 + 6.0 * sp) / t_tile_us;
+    const double sum_us = chip_sum ? 3.0 + 0.05 * (double)(rem * sp) : 10.0 + 6.0 * sp;
+    const double cost = (double)full + (double)seg_rounds / sp + (16.0 * seg_rounds + sum_us) / t_tile_us;
     if (cost < best - 1e-9) {
       best = cost;
       best_s = sp;
