@@ -706,6 +706,11 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
 //     (measured on MI355X: ~50 us in all for 64 tiles x 4 segments) is modelled as 10 us +
 //     6 us per segment; the chip-wide sum of the bf16 4-wave form reads the partials at
 //     about 5 TB/s (13.6 us for 64 x 4 segments), modelled as 3 us + 0.05 us per segment.
+//     Every bf16 plan is costed with the chip-wide sum, whatever the output form, so that the
+//     plan depends only on shape and precision: a fused epilogue and its unfused sequence
+//     accumulate K in the same segments.  Where the per-tile fixup runs instead (fp32, GELU
+//     and rotary outputs) this under-costs it; at the block's shapes (2048-8192 tokens) it
+//     selects the same plans as costing that fixup would.
 // The grouped int8 FC2 uses 128 x 128 tiles (its second accumulator set does not fit 256 wide).
 constexpr int kCUs = 256;
 
@@ -730,7 +735,7 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
   const double t_tile_us = (double)KT * 128 * 0.0277 / 2;   // one 256 x 256 tile over the whole K
   const double c256 = (double)(full + (rem ? 1 : 0));
   const double c128 = (double)((2 * tiles + kCUs - 1) / kCUs) * 0.52;
-  const bool chip_sum = !i8 && a.out_kind == H3DIT_OUT_BF16;
+  const bool chip_sum = !i8;
   double best = c256;
   int best_s = 1;
   for (int sp = 2; sp <= 8 && rem; sp++) {

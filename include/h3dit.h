@@ -189,8 +189,10 @@ typedef struct {
  * [0, n_video) and the audio rows (the last n_audio) of x, out = bf16(h W^T) with
  * h = bf16(AdaLN(x_rows; shift, scale)) (as h3dit_block_fwd's AdaLN), no bias.  The rows are
  * read in place (no slice copies) and h is formed inside the GEMM's tile loads, never stored:
- * the workspace holds only each row's mean and 1/sqrt(var + eps) (8 bytes per row).  The output
- * equals h3dit_row_gate_adaln followed by h3dit_linear byte for byte.  video / audio: NULL to
+ * the workspace holds only each row's mean and 1/sqrt(var + eps) (8 bytes per row).  The head
+ * sums K in one pass: its output equals h3dit_row_gate_adaln followed by h3dit_linear byte for
+ * byte wherever that GEMM is not split along K (h3dit_linear_workspace 0), and differs from a
+ * split one in fp32 summation order only.  video / audio: NULL to
  * skip that part; out_video bf16 [n_video][video->channels], out_audio bf16
  * [n_audio][audio->channels] (device).  workspace as in h3dit_block_fwd (NULL queries the
  * size).  x is not modified. */

@@ -183,7 +183,8 @@ def test_linear_workspace_plan():
     assert ws(4096, 20480, 5120) == 0                              # FC1: 1280 tiles, whole rounds
     assert ws(4096, 5120, 20480, h3.INT8, 1024) == 0               # grouped FC2
     assert ws(4096, 5120, 5120) == 64 * 256 * 256 * 4 * 4         # out-projection: same split, summed chip-wide
-    assert ws(4096, 5120, 5120, h3.BF16, 0, h3.OUT_F32) == 0       # per-tile fixup: half-width tiles instead
+    for kind in (h3.OUT_F32, h3.OUT_GELU):                         # the plan depends on shape and precision only
+        assert ws(4096, 5120, 5120, h3.BF16, 0, kind) == ws(4096, 5120, 5120)
     assert ws(4096, 5120, 5120, h3.INT8) == 0                      # int8: half the K bytes, split does not pay
     assert ws(64, 256, 2048) == 8 * 256 * 256 * 4                  # one tile: 8 segments
     assert ws(64, 256, 256) == 0                                   # 4 K slices: too short to split
