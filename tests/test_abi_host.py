@@ -197,6 +197,23 @@ def test_linear_workspace_plan():
     assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EINVAL       # misaligned
 
 
+def test_linear_plan_depends_on_shape_and_precision_only():
+    """A fused epilogue and its unfused sequence (bf16 output, then the GELU or rotary kernel)
+    must split K alike for the fusion switches to stay byte-identical: the split-K workspace,
+    which encodes the plan's split tiles and segments, is the same for every output form."""
+    ws = h3.linear_workspace
+    heads, hd = 40, 128
+    for M in (1, 64, 256, 300, 1024, 2048, 2688, 4096, 4480, 8192):
+        for N, K in ((5120, 5120), (5120, 20480), (20480, 5120), (15360, 5120), (512, 5120), (256, 2048)):
+            for prec in (h3.BF16, h3.INT8):
+                base = ws(M, N, K, prec)
+                kinds = [h3.OUT_F32 if prec == h3.BF16 else h3.OUT_I32, h3.OUT_GELU]
+                for kind in kinds:
+                    assert ws(M, N, K, prec, 0, kind) == base, (M, N, K, prec, kind)
+                if N == 3 * heads * hd:
+                    assert ws(M, N, K, prec, 0, h3.OUT_QKV, heads, hd) == base, (M, N, K, prec, "qkv")
+
+
 def test_stack_streamed_workspace_and_validation():
     """The streamed stack's workspace is the resident stack's plus every block's mod rows and
     two slots of one block's matrices (each region 256-byte aligned); bad arguments are
