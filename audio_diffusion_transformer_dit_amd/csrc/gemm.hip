@@ -461,41 +461,45 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
     __syncthreads();
     const int tid = threadIdx.x;
     constexpr int CH = BN / 8;  // 16-byte chunks per tile row
+    // A thread stores chunk column tid % CH of rows tid / CH, + NT / CH, ... (NT is a multiple
+    // of CH), so its column, and everything derived from it, is computed once.
+    static_assert(NT % CH == 0, "whole tile rows per pass");
+    const int c = tid % CH;
     if constexpr (OUT == H3DIT_OUT_QKV) {
       const int d = p.heads * p.hd;
       const int part = (int)(n0 / d);
       if (part < 2) {
-        uint16_t *dst = part == 0 ? p.oq : p.ok;
         const int half = p.hd / 2;
-        for (int idx = tid; idx < BM * CH; idx += NT) {
-          const int r = idx / CH, c = idx % CH;
+        const int col = (int)(n0 % d) + c * 8;
+        const int h = col / p.hd, i0 = col % p.hd;
+        uint16_t *dst = (part == 0 ? p.oq : p.ok) + (int64_t)h * p.M * p.hd + i0;
+        const float *cos_c = p.cos_t + i0 / 2, *sin_c = p.sin_t + i0 / 2;
+        for (int r = tid / CH; r < BM; r += NT / CH) {
           const int64_t row = m0 + r;
-          if (row >= p.M) continue;
-          const int col = (int)(n0 % d) + c * 8;
-          const int h = col / p.hd, i0 = col % p.hd;
+          if (row >= p.M) break;   // later rows are past the end too
           float f[8], o[8];
           unpack8(*reinterpret_cast<const u32x4 *>(smem + r * C::CPITCH + c * 16), f);
-          const float4 cs = *reinterpret_cast<const float4 *>(p.cos_t + row * half + i0 / 2);
-          const float4 sn = *reinterpret_cast<const float4 *>(p.sin_t + row * half + i0 / 2);
+          const float4 cs = *reinterpret_cast<const float4 *>(cos_c + row * half);
+          const float4 sn = *reinterpret_cast<const float4 *>(sin_c + row * half);
           const float cc[4] = {cs.x, cs.y, cs.z, cs.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             o[2 * e] = f[2 * e] * cc[e] - f[2 * e + 1] * ss[e];
             o[2 * e + 1] = f[2 * e] * ss[e] + f[2 * e + 1] * cc[e];
           }
-          *reinterpret_cast<u32x4 *>(dst + ((int64_t)h * p.M + row) * p.hd + i0) = pack8(o);
+          *reinterpret_cast<u32x4 *>(dst + row * p.hd) = pack8(o);
         }
       } else {
         // V^T[h][i][vt_pos(m)]: one lane per (feature column, group of 16 tokens); inside a
         // group, tokens 0-3 | 8-11 | 4-7 | 12-15 land at slots 0-15 (two 16-byte stores)
         for (int idx = tid; idx < BN * (BM / 16); idx += NT) {
-          const int c = idx % BN, rb = idx / BN;
-          const int col = (int)(n0 % d) + c;
+          const int cv = idx % BN, rb = idx / BN;
+          const int col = (int)(n0 % d) + cv;
           const int h = col / p.hd, i = col % p.hd;
           uint16_t v16[16];
 #pragma unroll
           for (int e = 0; e < 16; e++)
-            v16[vt_pos(e)] = *reinterpret_cast<const uint16_t *>(smem + (rb * 16 + e) * C::CPITCH + c * 2);
+            v16[vt_pos(e)] = *reinterpret_cast<const uint16_t *>(smem + (rb * 16 + e) * C::CPITCH + cv * 2);
           const int64_t row = m0 + rb * 16;
           uint16_t *dst = p.ov + ((int64_t)h * p.hd + i) * p.ldv + row;
           if (row + 16 <= p.M) {
@@ -515,11 +519,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
         }
       }
     } else {
-      uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
-      for (int idx = tid; idx < BM * CH; idx += NT) {
-        const int r = idx / CH, c = idx % CH;
+      uint16_t *out = reinterpret_cast<uint16_t *>(p.out) + n0 + c * 8;
+      for (int r = tid / CH; r < BM; r += NT / CH) {
         const int64_t row = m0 + r;
-        if (row >= p.M) continue;
+        if (row >= p.M) break;   // later rows are past the end too
         u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * C::CPITCH + c * 16);
         if constexpr (OUT == H3DIT_OUT_GELU) {
           float f[8];
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
           for (int e = 0; e < 8; e++) f[e] = gelu_tanh(f[e]);
           v = pack8(f);
         }
-        *reinterpret_cast<u32x4 *>(out + row * p.N + n0 + c * 8) = v;
+        *reinterpret_cast<u32x4 *>(out + row * p.N) = v;
       }
     }
   }
