@@ -492,16 +492,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
       } else {
         // V^T[h][i][vt_pos(m)]: one lane per (feature column, group of 16 tokens); inside a
         // group, tokens 0-3 | 8-11 | 4-7 | 12-15 land at slots 0-15 (two 16-byte stores)
-        for (int idx = tid; idx < BN * (BM / 16); idx += NT) {
-          const int cv = idx % BN, rb = idx / BN;
-          const int col = (int)(n0 % d) + cv;
-          const int h = col / p.hd, i = col % p.hd;
+        // (a thread keeps one feature column: NT is a multiple of BN)
+        static_assert(NT % BN == 0, "whole feature columns per pass");
+        const int cv = tid % BN;
+        const int col = (int)(n0 % d) + cv;
+        const int h = col / p.hd, i = col % p.hd;
+        uint16_t *dst_c = p.ov + ((int64_t)h * p.hd + i) * p.ldv;
+        for (int rb = tid / BN; rb < BM / 16; rb += NT / BN) {
+          const int64_t row = m0 + rb * 16;
+          if (row >= p.M) break;   // later groups are past the end too
           uint16_t v16[16];
 #pragma unroll
           for (int e = 0; e < 16; e++)
             v16[vt_pos(e)] = *reinterpret_cast<const uint16_t *>(smem + (rb * 16 + e) * C::CPITCH + cv * 2);
-          const int64_t row = m0 + rb * 16;
-          uint16_t *dst = p.ov + ((int64_t)h * p.hd + i) * p.ldv + row;
+          uint16_t *dst = dst_c + row;
           if (row + 16 <= p.M) {
             u32x4 v0, v1;
 #pragma unroll
