@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
-BF16, INT8, INT8_MLP = 0, 1, 2
+BF16, INT8, INT8_MLP, INT8_ATTN = 0, 1, 2, 3
 NOFUSE_GATE_ADALN, NOFUSE_ROPE, NOFUSE_GELU, NOFUSE_QUANT, NOFUSE_CROSS_BLOCK, NO_ALIAS = 1, 2, 4, 8, 16, 32
 OUT_BF16, OUT_F32, OUT_I32, OUT_GELU, OUT_QKV = 0, 1, 2, 3, 4
 
@@ -32,7 +32,7 @@ EXPORTS = ("h3dit_quantize_weights", "h3dit_block_fwd", "h3dit_stack_fwd", "h3di
            "h3dit_row_gate_adaln", "h3dit_quantize_rows", "h3dit_linear", "h3dit_rope_split", "h3dit_gelu",
            "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore", "h3dit_linear_workspace",
            "h3dit_final_head", "h3dit_stack_fwd_streamed", "h3dit_denoise_plan", "h3dit_velocity_step",
-           "h3dit_denoise_fwd")
+           "h3dit_denoise_fwd", "h3dit_linear_a_extent")
 
 
 class H3Error(RuntimeError):
@@ -59,8 +59,16 @@ class BlockW(C.Structure):
                 ("s_fc2", C.c_void_p), ("mod", C.c_void_p)]
 
 
+class Rope(C.Structure):
+    _fields_ = [("cos", C.c_void_p), ("sin", C.c_void_p)]
+
+
 class TokenReduction(C.Structure):
-    _fields_ = [("reduce_after", C.c_int32), ("restore_before", C.c_int32)]
+    _fields_ = [("reduce_after", C.c_int32), ("restore_before", C.c_int32), ("rope_reduced", Rope)]
+
+
+class PatchEmbed(C.Structure):
+    _fields_ = [("w_video", C.c_void_p), ("w_audio", C.c_void_p)]
 
 
 class HeadPart(C.Structure):
@@ -89,18 +97,20 @@ class LinearArgs(C.Structure):
 
 _P = C.c_void_p
 _lib.h3dit_quantize_weights.argtypes = [_P, C.c_int64, C.c_int64, _P, _P, _P]
-_lib.h3dit_block_fwd.argtypes = [_P, _P, _P, _P, C.c_uint32, _P, _P, _P]
-_lib.h3dit_stack_fwd.argtypes = [_P, _P, C.c_int32, _P, _P, _P, C.c_uint32, _P, _P, _P]
-_lib.h3dit_stack_fwd_streamed.argtypes = [_P, _P, C.c_int32, _P, _P, _P, C.c_uint32, _P, _P, _P, _P]
+_lib.h3dit_block_fwd.argtypes = [_P, _P, _P, _P, _P, C.c_uint32, _P, _P, _P]
+_lib.h3dit_stack_fwd.argtypes = [_P, _P, C.c_int32, _P, _P, _P, _P, C.c_uint32, _P, _P, _P]
+_lib.h3dit_stack_fwd_streamed.argtypes = [_P, _P, C.c_int32, _P, _P, _P, _P, C.c_uint32, _P, _P, _P, _P]
 _lib.h3dit_rope_tables.argtypes = [_P, C.c_int32, C.c_int32, _P, _P, _P]
 _lib.h3dit_row_gate_adaln.argtypes = [C.c_int64, C.c_int32, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_quantize_rows.argtypes = [C.c_int64, C.c_int64, C.c_int64, _P, C.c_int32, _P, _P, _P]
 _lib.h3dit_linear.argtypes = [_P, _P]
 _lib.h3dit_linear_workspace.argtypes = [_P, _P]
+_lib.h3dit_linear_a_extent.argtypes = [_P, _P, _P]
 _lib.h3dit_final_head.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_denoise_plan.argtypes = [_P, C.c_int32, _P]
 _lib.h3dit_velocity_step.argtypes = [C.c_int64, C.c_float, _P, _P, _P]
-_lib.h3dit_denoise_fwd.argtypes = [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, C.c_uint32, _P, _P, _P]
+_lib.h3dit_denoise_fwd.argtypes = [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_uint32, _P,
+                                   _P, _P]
 _lib.h3dit_rope_split.argtypes = [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_gelu.argtypes = [C.c_int64, _P, _P, _P]
 _lib.h3dit_attention.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, _P, _P]
@@ -184,10 +194,14 @@ def quantize_weights(w: torch.Tensor, stream=None):
 
 def block_struct(p: dict) -> BlockW:
     """p: {wqkv, wo, w1, w2, mod} bf16 device tensors; or int8 codes {qqkv, qo, q1, q2} with
-    scales {sqkv, so, s1, s2} and mod; or bf16 {wqkv, wo} with int8 {q1, q2, s1, s2} (int8 MLP)."""
-    if "qqkv" in p:
+    scales {sqkv, so, s1, s2} and mod; or bf16 {wqkv, wo} with int8 {q1, q2, s1, s2} (int8 MLP);
+    or int8 {qqkv, qo, sqkv, so} with bf16 {w1, w2} (int8 attention projections only)."""
+    if "qqkv" in p and "q1" in p:
         return BlockW(INT8, _ptr(p["qqkv"]), _ptr(p["qo"]), _ptr(p["q1"]), _ptr(p["q2"]), _ptr(p["sqkv"]),
                       _ptr(p["so"]), _ptr(p["s1"]), _ptr(p["s2"]), _ptr(p["mod"]))
+    if "qqkv" in p:
+        return BlockW(INT8_ATTN, _ptr(p["qqkv"]), _ptr(p["qo"]), _ptr(p["w1"]), _ptr(p["w2"]), _ptr(p["sqkv"]),
+                      _ptr(p["so"]), None, None, _ptr(p["mod"]))
     if "q1" in p:
         return BlockW(INT8_MLP, _ptr(p["wqkv"]), _ptr(p["wo"]), _ptr(p["q1"]), _ptr(p["q2"]), None, None,
                       _ptr(p["s1"]), _ptr(p["s2"]), _ptr(p["mod"]))
@@ -195,33 +209,56 @@ def block_struct(p: dict) -> BlockW:
                   _ptr(p["mod"]))
 
 
-def quantize_block(p: dict, stream=None, mlp_only: bool = False) -> dict:
-    """int8 codes of the four projections, or (mlp_only) of FC1 and FC2 with QKV and the
-    output projection kept in bf16."""
+def quantize_block(p: dict, stream=None, mlp_only: bool = False, attn_only: bool = False) -> dict:
+    """int8 codes of the four projections; or (mlp_only) of FC1 and FC2 with QKV and the
+    output projection kept in bf16; or (attn_only) of QKV and the output projection with FC1
+    and FC2 kept in bf16."""
+    assert not (mlp_only and attn_only)
     out = {"mod": p["mod"]}
     pairs = (("wqkv", "qqkv", "sqkv"), ("wo", "qo", "so"), ("w1", "q1", "s1"), ("w2", "q2", "s2"))
     if mlp_only:
         out["wqkv"], out["wo"] = p["wqkv"], p["wo"]
-    for w, q, s in (pairs[2:] if mlp_only else pairs):
+        pairs = pairs[2:]
+    elif attn_only:
+        out["w1"], out["w2"] = p["w1"], p["w2"]
+        pairs = pairs[:2]
+    for w, q, s in pairs:
         out[q], out[s] = quantize_weights(p[w], stream)
     return out
+
+
+def rope_struct(rope):
+    """h3dit_rope of (cos, sin) fp32 device tensors [n][head_dim/2], or None (built-in tables)."""
+    return None if rope is None else Rope(_ptr(rope[0]), _ptr(rope[1]))
+
+
+def reduction_struct(reduction, rope_reduced=None):
+    if not reduction:
+        return None
+    tr = TokenReduction(int(reduction[0]), int(reduction[1]))
+    if rope_reduced is not None:
+        tr.rope_reduced = rope_struct(rope_reduced)
+    return tr
+
+
+def _ref(s):
+    return C.byref(s) if s is not None else None
 
 
 def block_workspace(w, p: dict, flags: int = 0) -> int:
     size = C.c_size_t(0)
     b = block_struct(p)
     _check("h3dit_block_fwd", _lib.h3dit_block_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), C.byref(b), None,
-                                                   flags, None, C.byref(size), None))
+                                                   None, flags, None, C.byref(size), None))
     return size.value
 
 
 def stack_workspace(w, blocks: list, flags: int = 0, reduction=None) -> int:
     size = C.c_size_t(0)
     arr = (BlockW * len(blocks))(*[block_struct(p) for p in blocks])
-    tr = TokenReduction(*reduction) if reduction else None
+    tr = reduction_struct(reduction)
     _check("h3dit_stack_fwd", _lib.h3dit_stack_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), len(blocks), arr,
-                                                   C.byref(tr) if tr else None, None, flags, None, C.byref(size),
-                                                   None))
+                                                   None, _ref(tr), None, flags, None, C.byref(size), None))
     return size.value
 
 
@@ -229,26 +266,31 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def block_fwd(w, p: dict, x: torch.Tensor, flags: int = 0, workspace: torch.Tensor = None, stream=None):
-    """x (bf16 [N][d], device) is updated in place and returned."""
+def block_fwd(w, p: dict, x: torch.Tensor, flags: int = 0, workspace: torch.Tensor = None, stream=None,
+              rope=None):
+    """x (bf16 [N][d], device) is updated in place and returned.  rope: (cos, sin) tables or
+    None for the built-in ones."""
     b = block_struct(p)
     if workspace is None:
         workspace = alloc_workspace(block_workspace(w, p, flags), x.device)
     size = C.c_size_t(workspace.numel())
-    _check("h3dit_block_fwd", _lib.h3dit_block_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), C.byref(b), _ptr(x),
-                                                   flags, _ptr(workspace), C.byref(size), _stream(stream)))
+    r = rope_struct(rope)
+    _check("h3dit_block_fwd", _lib.h3dit_block_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), C.byref(b), _ref(r),
+                                                   _ptr(x), flags, _ptr(workspace), C.byref(size), _stream(stream)))
     return x
 
 
 class Stack:
     """Holds the host-side block array of a stack so repeated calls marshal nothing new."""
 
-    def __init__(self, w, blocks: list, flags: int = 0, reduction=None):
+    def __init__(self, w, blocks: list, flags: int = 0, reduction=None, rope=None, rope_reduced=None):
         self.w = w
         self.blocks = blocks
         self.flags = flags
         self.arr = (BlockW * len(blocks))(*[block_struct(p) for p in blocks])
-        self.tr = TokenReduction(*reduction) if reduction else None
+        self.rope_tensors = (rope, rope_reduced)   # kept alive while the structs point at them
+        self.rope = rope_struct(rope)
+        self.tr = reduction_struct(reduction, rope_reduced)
         self.dims = dims_of(w)
         self.layout = layout_of(w)
         self.workspace_bytes = stack_workspace(w, blocks, flags, reduction)
@@ -256,13 +298,14 @@ class Stack:
     def __call__(self, x: torch.Tensor, workspace: torch.Tensor, stream=None):
         size = C.c_size_t(workspace.numel())
         _check("h3dit_stack_fwd", _lib.h3dit_stack_fwd(C.byref(self.dims), C.byref(self.layout), len(self.blocks),
-                                                       self.arr, C.byref(self.tr) if self.tr else None, _ptr(x),
+                                                       self.arr, _ref(self.rope), _ref(self.tr), _ptr(x),
                                                        self.flags, _ptr(workspace), C.byref(size), _stream(stream)))
         return x
 
 
-def stack_fwd(w, blocks: list, x: torch.Tensor, flags: int = 0, reduction=None, workspace=None, stream=None):
-    s = Stack(w, blocks, flags, reduction)
+def stack_fwd(w, blocks: list, x: torch.Tensor, flags: int = 0, reduction=None, workspace=None, stream=None,
+              rope=None, rope_reduced=None):
+    s = Stack(w, blocks, flags, reduction, rope, rope_reduced)
     if workspace is None:
         workspace = alloc_workspace(s.workspace_bytes, x.device)
     return s(x, workspace, stream)
@@ -277,10 +320,10 @@ def host_block(p: dict) -> dict:
 def stack_streamed_workspace(w, blocks: list, flags: int = 0, reduction=None) -> int:
     size = C.c_size_t(0)
     arr = (BlockW * len(blocks))(*[block_struct(p) for p in blocks])
-    tr = TokenReduction(*reduction) if reduction else None
+    tr = reduction_struct(reduction)
     _check("h3dit_stack_fwd_streamed",
-           _lib.h3dit_stack_fwd_streamed(C.byref(dims_of(w)), C.byref(layout_of(w)), len(blocks), arr,
-                                         C.byref(tr) if tr else None, None, flags, None, C.byref(size), None, None))
+           _lib.h3dit_stack_fwd_streamed(C.byref(dims_of(w)), C.byref(layout_of(w)), len(blocks), arr, None,
+                                         _ref(tr), None, flags, None, C.byref(size), None, None))
     return size.value
 
 
@@ -289,11 +332,13 @@ class StreamedStack:
     each block's matrices are copied into one of two device slots on `copy_stream` while the
     previous block computes."""
 
-    def __init__(self, w, host_blocks: list, flags: int = 0, reduction=None):
+    def __init__(self, w, host_blocks: list, flags: int = 0, reduction=None, rope=None, rope_reduced=None):
         self.blocks = host_blocks
         self.flags = flags
         self.arr = (BlockW * len(host_blocks))(*[block_struct(p) for p in host_blocks])
-        self.tr = TokenReduction(*reduction) if reduction else None
+        self.rope_tensors = (rope, rope_reduced)
+        self.rope = rope_struct(rope)
+        self.tr = reduction_struct(reduction, rope_reduced)
         self.dims = dims_of(w)
         self.layout = layout_of(w)
         self.workspace_bytes = stack_streamed_workspace(w, host_blocks, flags, reduction)
@@ -302,7 +347,7 @@ class StreamedStack:
         size = C.c_size_t(workspace.numel())
         _check("h3dit_stack_fwd_streamed",
                _lib.h3dit_stack_fwd_streamed(C.byref(self.dims), C.byref(self.layout), len(self.blocks), self.arr,
-                                             C.byref(self.tr) if self.tr else None, _ptr(x), self.flags,
+                                             _ref(self.rope), _ref(self.tr), _ptr(x), self.flags,
                                              _ptr(workspace), C.byref(size), _stream(stream), copy_stream))
         return x
 
@@ -327,22 +372,32 @@ def velocity_step(z, v, dt: float, stream=None):
 
 class Denoise:
     """The denoising loop of h3dit_denoise_fwd with its host-side arguments marshalled once:
-    blocks (device weights), the plan options, per-step dt, and the head parts (video / audio:
-    (mod bf16 [2][d], W bf16 [c][d]) device tensors or None)."""
+    blocks (device weights), the plan options, per-step dt, the head parts (video / audio:
+    (mod bf16 [2][d], W bf16 [c][d]) device tensors or None), the patch-embedding stand-in
+    (embed: (W_video bf16 [d][c_v] or None, W_audio bf16 [d][c_a] or None), or None), and
+    optional rotary tables (cos, sin) of the full and the paired sequence."""
 
-    def __init__(self, w, blocks: list, opts: DenoiseOpts, dt, video=None, audio=None, flags: int = 0):
+    def __init__(self, w, blocks: list, opts: DenoiseOpts, dt, video=None, audio=None, flags: int = 0, embed=None,
+                 rope=None, rope_reduced=None):
         self.blocks = blocks
         self.arr = (BlockW * len(blocks))(*[block_struct(p) for p in blocks])
         self.opts = opts
         self.dt = (C.c_float * int(opts.steps))(*[float(t) for t in dt])
+        self.part_tensors = (video, audio)   # kept alive while the structs point at them
         self.parts = [None if p is None else HeadPart(_ptr(p[0]), _ptr(p[1]), p[1].shape[0]) for p in (video, audio)]
+        self.embed_tensors = embed
+        self.embed = None if embed is None else PatchEmbed(_ptr(embed[0]), _ptr(embed[1]))
+        self.rope_tensors = (rope, rope_reduced)
+        self.rope, self.rope_reduced = rope_struct(rope), rope_struct(rope_reduced)
         self.flags = flags
         self.dims = dims_of(w)
         self.layout = layout_of(w)
         size = C.c_size_t(0)
         _check("h3dit_denoise_fwd", _lib.h3dit_denoise_fwd(C.byref(self.dims), C.byref(self.layout), len(blocks),
-                                                           self.arr, C.byref(opts), self.dt, None, *self._refs(),
-                                                           None, None, flags, None, C.byref(size), None))
+                                                           self.arr, _ref(self.rope), _ref(self.rope_reduced),
+                                                           C.byref(opts), self.dt, None, _ref(self.embed),
+                                                           *self._refs(), None, None, flags, None, C.byref(size),
+                                                           None))
         self.workspace_bytes = size.value
 
     def _refs(self):
@@ -351,7 +406,8 @@ class Denoise:
     def __call__(self, x_in, z_video, z_audio, workspace, stream=None):
         size = C.c_size_t(workspace.numel())
         _check("h3dit_denoise_fwd", _lib.h3dit_denoise_fwd(C.byref(self.dims), C.byref(self.layout), len(self.blocks),
-                                                           self.arr, C.byref(self.opts), self.dt, _ptr(x_in),
+                                                           self.arr, _ref(self.rope), _ref(self.rope_reduced),
+                                                           C.byref(self.opts), self.dt, _ptr(x_in), _ref(self.embed),
                                                            *self._refs(), _ptr(z_video), _ptr(z_audio), self.flags,
                                                            _ptr(workspace), C.byref(size), _stream(stream)))
         return z_video, z_audio
@@ -412,6 +468,19 @@ def linear_workspace(M, N, K, precision=BF16, a_group=0, out_kind=OUT_BF16, head
     need = C.c_uint64(0)
     _check("h3dit_linear_workspace", _lib.h3dit_linear_workspace(C.byref(args), C.byref(need)))
     return need.value
+
+
+def linear_a_extent(M, N, K, precision=BF16, a_group=0, out_kind=OUT_BF16, a_headmajor_hd=0, heads=0,
+                    head_dim=0):
+    """(largest byte end any unmasked A load of the planned launch reads, loads masked wrongly):
+    a host-only walk over the kernel's A-operand addressing (no device work)."""
+    dummy = 1 << 20
+    args = LinearArgs(M=M, N=N, K=K, precision=precision, a=dummy, a_headmajor_hd=a_headmajor_hd, a_scale=dummy,
+                      a_group=a_group, w=dummy, w_scale=dummy, out_kind=out_kind, out=dummy, cos_t=dummy,
+                      sin_t=dummy, heads=heads, head_dim=head_dim, out_q=dummy, out_k=dummy, out_v=dummy)
+    end, bad = C.c_uint64(0), C.c_uint64(0)
+    _check("h3dit_linear_a_extent", _lib.h3dit_linear_a_extent(C.byref(args), C.byref(end), C.byref(bad)))
+    return end.value, bad.value
 
 
 def final_head(w, x, video=None, audio=None, stream=None):

@@ -35,8 +35,10 @@ int check_dims(const h3dit_dims *D, const h3dit_layout *L, int precision) {
   if (D->head_dim != 64 && D->head_dim != 128) return H3DIT_EUNSUPPORTED;
   if (D->hidden % 256 || D->hidden > 8192 || D->mlp < 256 || D->mlp % 256) return H3DIT_EINVAL;
   if (!(D->ln_eps >= 0.0f)) return H3DIT_EINVAL;
-  if (precision != H3DIT_BF16 && precision != H3DIT_INT8 && precision != H3DIT_INT8_MLP) return H3DIT_EINVAL;
-  if (precision != H3DIT_BF16) {
+  if (precision != H3DIT_BF16 && precision != H3DIT_INT8 && precision != H3DIT_INT8_MLP &&
+      precision != H3DIT_INT8_ATTN)
+    return H3DIT_EINVAL;
+  if (precision == H3DIT_INT8 || precision == H3DIT_INT8_MLP) {
     // 1024-channel groups as on the pages, or one code per token over the whole FC2 input
     // (fc2_group == mlp, the row-level variant)
     if (D->fc2_group < 128 || D->fc2_group % 128 || (D->fc2_group > 8192 && D->fc2_group != D->mlp) ||
@@ -71,9 +73,22 @@ int check_block(const h3dit_block_w *b, int precision) {
     const float *s[2] = {b->s_fc1, b->s_fc2};
     for (const float *p : s)
       if (!p || !aligned(p, 4)) return H3DIT_EINVAL;
+  } else if (precision == H3DIT_INT8_ATTN) {
+    const float *s[2] = {b->s_qkv, b->s_o};
+    for (const float *p : s)
+      if (!p || !aligned(p, 4)) return H3DIT_EINVAL;
   }
   return H3DIT_OK;
 }
+
+// Caller rotary tables: NULL (or both pointers NULL) selects the built-in ones; otherwise both
+// must be given and 16-byte aligned (the QKV epilogue reads them four pairs at a time).
+int check_rope(const h3dit_rope *r) {
+  if (!r || (!r->cos && !r->sin)) return H3DIT_OK;
+  if (!r->cos || !r->sin || !aligned(r->cos, 16) || !aligned(r->sin, 16)) return H3DIT_EINVAL;
+  return H3DIT_OK;
+}
+bool has_rope(const h3dit_rope *r) { return r && r->cos && r->sin; }
 
 // gfx950 check, once per device
 std::atomic<int> g_arch_ok[64];
@@ -105,8 +120,12 @@ struct Plan {
 };
 
 // Precision of the attention projections (QKV, output) and of the MLP projections.
-int attn_prec(int precision) { return precision == H3DIT_INT8 ? H3DIT_INT8 : H3DIT_BF16; }
-int mlp_prec(int precision) { return precision == H3DIT_BF16 ? H3DIT_BF16 : H3DIT_INT8; }
+int attn_prec(int precision) {
+  return (precision == H3DIT_INT8 || precision == H3DIT_INT8_ATTN) ? H3DIT_INT8 : H3DIT_BF16;
+}
+int mlp_prec(int precision) {
+  return (precision == H3DIT_INT8 || precision == H3DIT_INT8_MLP) ? H3DIT_INT8 : H3DIT_BF16;
+}
 
 // Largest split-K workspace of the block's four projections at n tokens.
 size_t block_splitk_bytes(const h3dit_dims &D, int precision, int64_t n) {
@@ -132,7 +151,7 @@ size_t block_splitk_bytes(const h3dit_dims &D, int precision, int64_t n) {
 Plan make_plan(const h3dit_dims &D, const h3dit_layout &L, int precision, uint32_t flags, bool reduction) {
   const size_t N = (size_t)D.n_tokens, d = (size_t)D.hidden, f = (size_t)D.mlp, hd = (size_t)D.head_dim;
   const size_t ldv = (size_t)vt_pitch((int64_t)N);
-  const bool i8 = precision != H3DIT_BF16;   // the int8 buffers (a superset for int8-MLP blocks)
+  const bool i8 = precision != H3DIT_BF16;   // the int8 buffers (a superset for the partly int8 blocks)
   const size_t Nd2 = N * d * 2;
   Plan p;
   size_t off = 0;
@@ -157,7 +176,7 @@ Plan make_plan(const h3dit_dims &D, const h3dit_layout &L, int precision, uint32
   }
   if (p.sk_bytes) p.sk = take(p.sk_bytes);
   p.sa = take(N * 4);
-  if (i8) p.sg = take(N * (f / (size_t)D.fc2_group) * 4);
+  if (mlp_prec(precision) == H3DIT_INT8) p.sg = take(N * (f / (size_t)D.fc2_group) * 4);
   if (flags & H3DIT_NOFUSE_ROPE) p.t = take(3 * Nd2);
   if (flags & H3DIT_NOFUSE_QUANT) p.hb = take(Nd2);
   const size_t qkv = 2 * Nd2 + d * ldv * 2;
@@ -348,18 +367,29 @@ int prepare(const h3dit_dims *dims, const h3dit_layout *layout, int precision, u
 // after(b) once they are enqueued (both may enqueue work).  The next block's AdaLN1, fused into
 // block b's final gate, reads only blocks[b + 1].mod.
 template <class Before, class After>
-int run_stack(const Ctx &c, int32_t n_blocks, const h3dit_block_w *blocks, const h3dit_token_reduction *tr,
-              uint16_t *x, Before before, After after) {
+int run_stack(const Ctx &c, int32_t n_blocks, const h3dit_block_w *blocks, const h3dit_rope *rope,
+              const h3dit_token_reduction *tr, uint16_t *x, Before before, After after) {
   const h3dit_dims *dims = c.D;
   const h3dit_layout *layout = c.L;
   const Plan &plan = c.P;
-  float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
-  float *cr = nullptr, *sr = nullptr;
-  TRY(launch_rope_tables(*layout, dims->head_dim, 0, cf, sf, c.st));
+  // rotary tables: the caller's, or the built-in ones made in the workspace
+  const float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
+  const float *cr = nullptr, *sr = nullptr;
+  if (has_rope(rope)) {
+    cf = rope->cos;
+    sf = rope->sin;
+  } else {
+    TRY(launch_rope_tables(*layout, dims->head_dim, 0, c.at<float>(plan.cos_f), c.at<float>(plan.sin_f), c.st));
+  }
   if (tr) {
-    cr = c.at<float>(plan.cos_r);
-    sr = c.at<float>(plan.sin_r);
-    TRY(launch_rope_tables(*layout, dims->head_dim, 1, cr, sr, c.st));
+    if (has_rope(&tr->rope_reduced)) {
+      cr = tr->rope_reduced.cos;
+      sr = tr->rope_reduced.sin;
+    } else {
+      cr = c.at<float>(plan.cos_r);
+      sr = c.at<float>(plan.sin_r);
+      TRY(launch_rope_tables(*layout, dims->head_dim, 1, c.at<float>(plan.cos_r), c.at<float>(plan.sin_r), c.st));
+    }
   }
   const int64_t Nf = dims->n_tokens, Nr = layout_tokens(*layout, true);
   const int d = dims->hidden;
@@ -436,24 +466,30 @@ int h3dit_quantize_weights(const uint16_t *w, int64_t rows, int64_t cols, int8_t
   return H3DIT_OK;
 }
 
-int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_block_w *blk, uint16_t *x,
-                    uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream) {
+int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_block_w *blk,
+                    const h3dit_rope *rope, uint16_t *x, uint32_t flags, void *workspace, size_t *workspace_bytes,
+                    void *stream) {
   if (!blk) return H3DIT_EINVAL;
   Plan plan;
   int rc = prepare(dims, layout, blk->precision, flags, false, x, workspace, workspace_bytes, plan);
   if (rc == 1) return H3DIT_OK;
   if (rc) return rc;
-  if ((rc = check_block(blk, blk->precision))) return rc;
+  if ((rc = check_block(blk, blk->precision)) || (rc = check_rope(rope))) return rc;
   if ((rc = check_device())) return rc;
   Ctx c{dims, layout, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
-  float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
-  TRY(launch_rope_tables(*layout, dims->head_dim, 0, cf, sf, c.st));
+  const float *cf = c.at<float>(plan.cos_f), *sf = c.at<float>(plan.sin_f);
+  if (has_rope(rope)) {
+    cf = rope->cos;
+    sf = rope->sin;
+  } else {
+    TRY(launch_rope_tables(*layout, dims->head_dim, 0, c.at<float>(plan.cos_f), c.at<float>(plan.sin_f), c.st));
+  }
   return run_block(c, dims->n_tokens, cf, sf, *blk, x, false, nullptr);
 }
 
 int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks, const h3dit_block_w *blocks,
-                    const h3dit_token_reduction *tr, uint16_t *x, uint32_t flags, void *workspace,
-                    size_t *workspace_bytes, void *stream) {
+                    const h3dit_rope *rope, const h3dit_token_reduction *tr, uint16_t *x, uint32_t flags,
+                    void *workspace, size_t *workspace_bytes, void *stream) {
   if (!blocks || n_blocks < 1) return H3DIT_EINVAL;
   const int precision = blocks[0].precision;
   if (tr && (tr->reduce_after < 0 || tr->restore_before <= tr->reduce_after || tr->reduce_after >= n_blocks))
@@ -464,15 +500,17 @@ int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t 
   if (rc) return rc;
   for (int32_t b = 0; b < n_blocks; b++)
     if ((rc = check_block(&blocks[b], precision))) return rc;
+  if ((rc = check_rope(rope)) || (tr && (rc = check_rope(&tr->rope_reduced)))) return rc;
   if ((rc = check_device())) return rc;
   Ctx c{dims, layout, flags, reinterpret_cast<uint8_t *>(workspace), plan, (hipStream_t)stream};
   auto none = [](int32_t) { return H3DIT_OK; };
-  return run_stack(c, n_blocks, blocks, tr, x, none, none);
+  return run_stack(c, n_blocks, blocks, rope, tr, x, none, none);
 }
 
 int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
-                             const h3dit_block_w *blocks, const h3dit_token_reduction *tr, uint16_t *x, uint32_t flags,
-                             void *workspace, size_t *workspace_bytes, void *stream, void *copy_stream) {
+                             const h3dit_block_w *blocks, const h3dit_rope *rope, const h3dit_token_reduction *tr,
+                             uint16_t *x, uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream,
+                             void *copy_stream) {
   if (!blocks || n_blocks < 1 || !dims || !layout) return H3DIT_EINVAL;
   const int precision = blocks[0].precision;
   if (tr && (tr->reduce_after < 0 || tr->restore_before <= tr->reduce_after || tr->reduce_after >= n_blocks))
@@ -489,6 +527,7 @@ int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout,
   if (rc) return rc;
   for (int32_t b = 0; b < n_blocks; b++)
     if ((rc = check_block(&blocks[b], precision))) return rc;
+  if ((rc = check_rope(rope)) || (tr && (rc = check_rope(&tr->rope_reduced)))) return rc;
   if ((rc = check_device())) return rc;
   uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
   uint8_t *mods = ws + plan.total, *slot[2] = {mods + mods_region, mods + mods_region + sl.total};
@@ -515,16 +554,23 @@ int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout,
     v.mod = reinterpret_cast<const uint16_t *>(mods + (size_t)b * mb);
     TRY(hipMemcpyAsync(mods + (size_t)b * mb, blocks[b].mod, mb, hipMemcpyHostToDevice, st));
   }
-  // copied[s]: block weights in slot s are complete; freed[s]: the block that used slot s is done
+  // copied[s]: block weights in slot s are complete; freed[s]: the block that used slot s is
+  // done; entry: everything enqueued on `stream` before this call (an earlier call's blocks
+  // may still be reading the slots)
   struct Events {
-    hipEvent_t e[4] = {};
+    hipEvent_t e[5] = {};
     ~Events() {
       for (hipEvent_t x : e)
         if (x) (void)hipEventDestroy(x);
     }
   } ev;
   for (hipEvent_t &e : ev.e) TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  hipEvent_t *copied = ev.e, *freed = ev.e + 2;
+  hipEvent_t *copied = ev.e, *freed = ev.e + 2, entry = ev.e[4];
+  if (cs != st) {
+    // the first two copies overwrite slots the previous call's last blocks may still read
+    TRY(hipEventRecord(entry, st));
+    TRY(hipStreamWaitEvent(cs, entry, 0));
+  }
   auto copy_block = [&](int32_t b) -> int {
     const int s = b & 1;
     if (b >= 2) TRY(hipStreamWaitEvent(cs, freed[s], 0));
@@ -546,7 +592,7 @@ int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout,
     TRY(hipEventRecord(freed[b & 1], st));
     return H3DIT_OK;
   };
-  return run_stack(c, n_blocks, dev.data(), tr, x, before, after);
+  return run_stack(c, n_blocks, dev.data(), rope, tr, x, before, after);
 }
 
 int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,
@@ -631,10 +677,11 @@ int h3dit_velocity_step(int64_t count, float dt, const uint16_t *v, uint16_t *z,
 }
 
 int h3dit_denoise_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
-                      const h3dit_block_w *blocks, const h3dit_denoise_opts *opts, const float *dt,
-                      const uint16_t *x_in, const h3dit_head_part *video, const h3dit_head_part *audio,
-                      uint16_t *z_video, uint16_t *z_audio, uint32_t flags, void *workspace,
-                      size_t *workspace_bytes, void *stream) {
+                      const h3dit_block_w *blocks, const h3dit_rope *rope, const h3dit_rope *rope_reduced,
+                      const h3dit_denoise_opts *opts, const float *dt, const uint16_t *x_in,
+                      const h3dit_patch_embed *embed, const h3dit_head_part *video, const h3dit_head_part *audio,
+                      uint16_t *z_video, uint16_t *z_audio, uint32_t flags, void *workspace, size_t *workspace_bytes,
+                      void *stream) {
   if (!workspace_bytes || !dims || !layout || !blocks || !opts || n_blocks < 1 || (!video && !audio))
     return H3DIT_EINVAL;
   if (opts->steps < 1) return H3DIT_EINVAL;
@@ -646,23 +693,48 @@ int h3dit_denoise_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_
   }
   int rc = h3dit_denoise_plan(opts, n_blocks, plan.data());
   if (rc < 0) return rc;
+  if ((rc = check_rope(rope)) || (rc = check_rope(rope_reduced))) return rc;
   const bool red = opts->reduce_after >= 0;
-  // sizes: the working residual, the two velocity buffers, then the stack's or the head's
-  // workspace (they run one after the other on the stream, so they share it)
-  h3dit_token_reduction tr_q{opts->reduce_after, opts->restore_early > opts->restore_late ? opts->restore_early
-                                                                                          : opts->restore_late};
+  // sizes: the working residual, the two velocity buffers, then the stack's, the head's or the
+  // embedding's workspace (they run one after the other on the stream, so they share it)
+  h3dit_token_reduction tr_q{opts->reduce_after,
+                             opts->restore_early > opts->restore_late ? opts->restore_early : opts->restore_late,
+                             {nullptr, nullptr}};
   size_t stack_bytes = 0, head_bytes = 0;
-  if ((rc = h3dit_stack_fwd(dims, layout, opts->layers, blocks, red ? &tr_q : nullptr, nullptr, flags, nullptr,
-                            &stack_bytes, nullptr)))
+  if ((rc = h3dit_stack_fwd(dims, layout, opts->layers, blocks, nullptr, red ? &tr_q : nullptr, nullptr, flags,
+                            nullptr, &stack_bytes, nullptr)))
     return rc;
   if ((rc = h3dit_final_head(dims, layout, video, audio, nullptr, nullptr, nullptr, nullptr, &head_bytes, nullptr)))
     return rc;
   const int64_t N = dims->n_tokens, d = dims->hidden;
   const int64_t n_audio = layout->n_audio, n_video = N - layout->n_text - n_audio;
   const int64_t cv = video ? (int64_t)video->channels * n_video : 0, ca = audio ? (int64_t)audio->channels * n_audio : 0;
+  // patch embedding of each part: e = bf16(z W^T) into the shared region, then x_rows += e
+  struct Embed {
+    const uint16_t *w;
+    const uint16_t *z;
+    int64_t rows, r0, channels;
+  } emb[2] = {{embed && video ? embed->w_video : nullptr, z_video, n_video, 0, video ? video->channels : 0},
+              {embed && audio ? embed->w_audio : nullptr, z_audio, n_audio, N - n_audio, audio ? audio->channels : 0}};
+  size_t emb_bytes = 0;
+  h3dit_linear_args ela[2] = {};
+  for (int i = 0; i < 2; i++) {
+    Embed &e = emb[i];
+    if (!e.w || e.rows == 0) {
+      e.w = nullptr;
+      continue;
+    }
+    if (!aligned(e.w, 16)) return H3DIT_EINVAL;
+    h3dit_linear_args &la = ela[i];
+    la.M = e.rows; la.N = d; la.K = e.channels; la.precision = H3DIT_BF16; la.out_kind = H3DIT_OUT_BF16;
+    const size_t need = up((size_t)(e.rows * d * 2)) + linear_workspace(la);
+    if (need > emb_bytes) emb_bytes = need;
+  }
   const size_t x_off = 0, vv_off = up((size_t)(N * d * 2)), va_off = vv_off + up((size_t)cv * 2),
                rest_off = va_off + up((size_t)ca * 2);
-  const size_t rest = stack_bytes > head_bytes ? stack_bytes : head_bytes, total = rest_off + rest;
+  size_t rest = stack_bytes > head_bytes ? stack_bytes : head_bytes;
+  if (emb_bytes > rest) rest = emb_bytes;
+  const size_t total = rest_off + rest;
   if (!workspace) {
     *workspace_bytes = total;
     return H3DIT_OK;
@@ -684,10 +756,23 @@ int h3dit_denoise_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_
   for (const h3dit_denoise_step &s : plan) {
     if (s.core) {
       TRY(hipMemcpyAsync(x, x_in, (size_t)(N * d * 2), hipMemcpyDeviceToDevice, st));
-      h3dit_token_reduction tr{opts->reduce_after, s.restore_before};
+      for (int i = 0; i < 2; i++) {
+        const Embed &e = emb[i];
+        if (!e.w) continue;
+        uint16_t *eb = reinterpret_cast<uint16_t *>(ws + rest_off);
+        h3dit_linear_args la = ela[i];
+        la.a = e.z; la.w = e.w; la.out = eb;
+        la.workspace = ws + rest_off + up((size_t)(e.rows * d * 2));
+        la.workspace_bytes = rest - up((size_t)(e.rows * d * 2));
+        TRY(launch_linear(la, st));
+        // x_rows = bf16(x_rows + 1 * e): the velocity-step kernel with dt = 1 is exactly this sum
+        TRY(launch_velocity_step(e.rows * d, 1.0f, eb, x + e.r0 * d, st));
+      }
+      h3dit_token_reduction tr{opts->reduce_after, s.restore_before,
+                               {rope_reduced ? rope_reduced->cos : nullptr, rope_reduced ? rope_reduced->sin : nullptr}};
       size_t sb = rest;
-      if ((rc = h3dit_stack_fwd(dims, layout, s.n_blocks, blocks, red ? &tr : nullptr, x, flags, ws + rest_off, &sb,
-                                stream)))
+      if ((rc = h3dit_stack_fwd(dims, layout, s.n_blocks, blocks, rope, red ? &tr : nullptr, x, flags, ws + rest_off,
+                                &sb, stream)))
         return rc;
     }
     if (s.fresh) {
@@ -786,6 +871,16 @@ int h3dit_linear_workspace(const h3dit_linear_args *a, uint64_t *bytes) {
   int rc = check_linear(a);
   if (rc) return rc;
   *bytes = linear_workspace(*a);
+  return H3DIT_OK;
+}
+
+int h3dit_linear_a_extent(const h3dit_linear_args *a, uint64_t *max_end, uint64_t *bad) {
+  if (!max_end || !bad) return H3DIT_EINVAL;
+  int rc = check_linear(a);
+  if (rc) return rc;
+  *max_end = 0;
+  *bad = 0;
+  if (a->M > 0) linear_a_extent(*a, max_end, bad);
   return H3DIT_OK;
 }
 

@@ -71,7 +71,10 @@ __device__ __forceinline__ void att_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
 }
 
 template <int HD>
-__global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+// q and o may be the same buffer (the output written over the queries): neither is marked
+// __restrict__.  Every Q load of a wave precedes its first O store, and waves read and write
+// only their own query rows.
+__global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, const uint16_t *__restrict__ k,
                                                            const uint16_t *__restrict__ vt, uint16_t *o, int64_t N,
                                                            int ldv, int heads, float *row_max, float *row_sum) {
   using C = AttCfg<HD>;

@@ -140,6 +140,7 @@ struct LinearPlan {
 };
 LinearPlan plan_linear(const h3dit_linear_args &a);
 size_t linear_workspace(const h3dit_linear_args &a);
+void linear_a_extent(const h3dit_linear_args &a, uint64_t *max_end, uint64_t *bad);
 hipError_t launch_linear(const h3dit_linear_args &a, hipStream_t st);
 hipError_t launch_attention(int heads, int64_t n, int hd, const uint16_t *q, const uint16_t *k,
                             const uint16_t *vt, uint16_t *o, float *row_max, float *row_sum, hipStream_t st);

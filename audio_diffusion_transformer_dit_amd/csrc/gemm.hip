@@ -20,7 +20,7 @@
 //    multiplied, slice k+1 is stored to the other LDS stage at the top of the iteration and
 //    the loads of slice k+3 are spread between the MFMAs, so each load has more than a whole
 //    iteration to arrive.
-// Rows past M read as zeros (buffer range check).  The epilogue stages the bf16 tile in LDS
+// Rows past M read as zeros (buffer range check, see a_load).  The epilogue stages the bf16 tile in LDS
 // and writes 16-byte row chunks (or, for V, 16-byte token chunks of V^T).  Workgroups are
 // dealt round-robin to the 8 XCDs; the tile order is remapped so that each XCD sweeps a
 // contiguous band of tiles, 8 tile-rows at a time, sharing A and W in its L2.
@@ -85,6 +85,60 @@ __device__ __forceinline__ void tile_coords(int b, int &tm, int &tn, int tiles_m
   tn = r / gsize;
 }
 
+// Byte addressing of one 16-byte load of the A operand: block li of a lane whose block-0 row
+// is tile row r0, 16-byte chunk cl, K slice kt.  The range check of a raw buffer load covers
+// the vector offset (plus the instruction offset), not the scalar offset, so everything that
+// depends on the row sits in the vector offset or in the resource: block li reads through a
+// resource based li block strides further on with its record count shortened to match, and a
+// head-major A (the attention output [K/hd][M][hd]) has the head in the resource base and
+// one head's rows as its records.  A load returns zeros exactly when its row is >= M
+// (voff >= nrec); every other load stays inside [base, base + nrec).
+struct ALoad {
+  int64_t base;   // byte offset of the resource base from A
+  int64_t nrec;   // bytes the resource covers (>= 0)
+  uint32_t voff;  // per-lane vector offset
+  uint32_t soff;  // wave-uniform scalar offset (the K position inside a row)
+};
+__host__ __device__ __forceinline__ ALoad a_load(int64_t M, int64_t K, int esz, int hm_hd, int nw, int64_t m0,
+                                                 int r0, int cl, int li, int kt) {
+  ALoad L;
+  const int64_t rows_before = (int64_t)nw * 8 * li;   // rows of the blocks before block li
+  const int64_t left = M - rows_before > 0 ? M - rows_before : 0;
+  if (hm_hd) {
+    const int64_t kel = (int64_t)kt * (GKB / 2);         // first element of the slice (bf16)
+    const int64_t head = kel / hm_hd;
+    L.base = (head * M + rows_before) * hm_hd * 2;
+    L.nrec = left * hm_hd * 2;
+    L.voff = (uint32_t)((m0 + r0) * hm_hd * 2 + cl * 16);
+    L.soff = (uint32_t)((kel % hm_hd) * 2);
+  } else {
+    L.base = rows_before * K * esz;
+    L.nrec = left * K * esz;
+    L.voff = (uint32_t)((m0 + r0) * K * esz + cl * 16);
+    L.soff = (uint32_t)kt * GKB;
+  }
+  return L;
+}
+
+// Addressing of the group scale of grouped-FC2 accumulator row u + v + e, group g: u = m0 +
+// 32 i + 8 q (the tile's part, wave-uniform), v = the wave's and lane's row offset, e < 4.
+// The resource starts at scale (u, g) and holds (M - u) * n_groups - g scales; v + e goes into
+// the vector offset.  A row >= M reads 0 (its sums are never stored); no read leaves the
+// [M][n_groups] scale array.
+struct ScLoad {
+  int64_t base;   // first scale (element index) of the resource
+  int64_t nrec;   // bytes the resource covers (>= 0)
+  uint32_t voff;  // per-lane vector offset (bytes)
+};
+__host__ __device__ __forceinline__ ScLoad sc_load(int64_t M, int n_groups, int64_t u, int v, int e, int g) {
+  ScLoad L;
+  const int64_t left = (M - u) * n_groups - g;
+  L.base = u * n_groups + g;
+  L.nrec = left > 0 ? left * 4 : 0;
+  L.voff = (uint32_t)((v + e) * n_groups * 4);
+  return L;
+}
+
 __device__ __forceinline__ u32x4 lds_frag(const uint8_t *base, int row, int chunk) {
   return *reinterpret_cast<const u32x4 *>(base + row * GKB + ((chunk ^ ((row >> 1) & 7)) << 4));
 }
@@ -120,32 +174,37 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
   constexpr int esz = INT8 ? 1 : 2;
-  const uint32_t a_bytes = (uint32_t)(p.M * p.K * esz), w_bytes = (uint32_t)(p.N * p.K * esz);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, a_bytes), rw = make_rsrc(p.w, w_bytes);
+  const uint32_t w_bytes = (uint32_t)(p.N * p.K * esz);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, w_bytes);
 
   // Per-lane load offsets.  A slice of the tile is (BM + BN) rows x 128 B; lanes take it in
   // 1 KiB blocks of 8 rows (8 consecutive lanes = one row's 8 chunks), so every global load
   // instruction reads whole 128-byte lines.  Block i of wave w covers rows (i*NW + w)*8 .. +7.
-  // Within a lane all blocks share the row-in-block and chunk, and (NW even) the
-  // swizzle too, so each operand needs one per-lane offset; the block stride and the slice
-  // offset go into the scalar offset of the buffer load.
+  // Within a lane all blocks share the row-in-block and chunk, and (NW even) the swizzle
+  // too, so each operand needs one per-lane offset.  W rows are all inside the matrix (N is a
+  // multiple of BN): the block stride and the slice offset go into the scalar offset.  A rows
+  // may run past M: each block of A reads through its own resource (a_load).
   static_assert(NW % 2 == 0, "blocks of one lane share the swizzle when the block stride is a multiple of 16 rows");
   const int rl = lane >> 3, cl = lane & 7;
   static_assert(!(HM && INT8), "head-major input is bf16");
   constexpr bool hm = HM;
+  const int hm_hd = hm ? p.hm_hd : 0;
   const int r0 = wid * 8 + rl;                         // row of block 0
   const int sw = (cl ^ ((r0 >> 1) & 7)) << 4;          // swizzled 16-byte slot (same for every block)
-  const uint32_t a_voff = hm ? (uint32_t)((m0 + r0) * p.hm_hd * 2 + cl * 16) : (uint32_t)((m0 + r0) * p.K * esz + cl * 16);
+  const uint32_t a_voff = a_load(p.M, p.K, esz, hm_hd, NW, m0, r0, cl, 0, 0).voff;   // the same for every block
   const uint32_t w_voff = (uint32_t)((n0 + r0) * p.K * esz + cl * 16);
-  const uint32_t a_bstride = hm ? (uint32_t)(NW * 8 * p.hm_hd * 2) : (uint32_t)(NW * 8 * p.K * esz);
   const uint32_t w_bstride = (uint32_t)(NW * 8 * p.K * esz);
   const uint32_t lds0 = (uint32_t)(r0 * GKB + sw);     // LDS byte offset of block 0 (A); blocks step NW*1 KiB
-  // Offset of K slice kt inside an A row, without branches: head-major bf16 input places
-  // element k at (k / hd) * (M*hd*2) + (k % hd) * 2 bytes past the row start; token-major is
-  // the same formula with shift 31, head stride 0 and a full mask (k * 2 bytes).
-  const uint32_t hm_head = hm ? (uint32_t)(p.M * p.hm_hd * 2) : 0u;
-  const uint32_t hm_shift = hm ? (p.hm_hd == 128 ? 7u : 6u) : 31u;
-  const uint32_t hm_mask = hm ? (uint32_t)(p.hm_hd - 1) : 0xFFFFFFFFu;
+  auto a_rsrc = [&](int li, int kt) {
+    const ALoad L = a_load(p.M, p.K, esz, hm_hd, NW, m0, r0, cl, li, kt);
+    return make_rsrc(p.a + L.base, (uint32_t)L.nrec);
+  };
+  // token-major A: the block resources do not depend on the slice (built once, scalar registers)
+  __amdgpu_buffer_rsrc_t ra[LA];
+  if constexpr (!hm) {
+#pragma unroll
+    for (int li = 0; li < LA; li++) ra[li] = a_rsrc(li, 0);
+  }
 
   // Slices travel global -> registers -> LDS through two register sets (the loop forms below
   // say which slices they hold when).
@@ -154,9 +213,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
   auto load_one = [&](u32x4 *dst, int kt, int li) {
     const uint32_t kb = (uint32_t)kt * GKB;   // byte offset of the slice inside a W row
     if (li < LA) {
-      const uint32_t kel = kb >> 1;           // a slice never crosses a head
-      const uint32_t ka = INT8 ? kb : (kel >> hm_shift) * hm_head + ((kel & hm_mask) << 1);
-      dst[li] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff, ka + li * a_bstride, 0));
+      if constexpr (hm) {
+        // head-major: the slice's head moves the resource base (a slice never crosses a head)
+        const ALoad L = a_load(p.M, p.K, esz, hm_hd, NW, m0, r0, cl, li, kt);
+        dst[li] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc(li, kt), a_voff, L.soff, 0));
+      } else {
+        dst[li] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra[li], a_voff, kb, 0));
+      }
     } else {
       dst[li] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, kb + (li - LA) * w_bstride, 0));
     }
@@ -183,9 +246,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
   }
   const int kt_per_group = GROUPED ? p.a_group * esz / GKB : 0;
   const int n_groups = GROUPED ? (int)(p.K / p.a_group) : 0;
-  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.a_scale, GROUPED ? (uint32_t)(p.M * n_groups * 4) : 0u);
-  const uint32_t sc_voff =
-      (uint32_t)((m0 + wm * (BM / WGM) + 4 * (lane >> 5)) * n_groups * 4);   // this lane's first row
+  const int sc_v = wm * (BM / WGM) + 4 * (lane >> 5);   // the wave's and lane's part of an accumulator row
 
   const int arow0 = wm * (BM / WGM) + (lane & 31);
   const int brow0 = wn * (BN / WGN) + (lane & 31);
@@ -349,16 +410,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
     if constexpr (GROUPED) {
       if ((kt + 1) % kt_per_group == 0) {
         const int g = kt / kt_per_group;
-        // one 32-row block at a time, so that only 16 row scales are live; scales are read
-        // through a buffer resource (rows past M read 0): per-lane row base in the vector
-        // offset, row-in-block and group in the scalar offset
+        // one 32-row block at a time, so that only 16 row scales are live; accumulator r of
+        // block i sits at row (m0 + 32 i + 8 (r / 4)) + sc_v + r % 4 (sc_load)
 #pragma unroll
         for (int i = 0; i < FM; i++) {
           float sc[16];
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const uint32_t soff = (uint32_t)(((32 * i + 8 * (r / 4) + (r % 4)) * n_groups + g) * 4);
-            sc[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, sc_voff, soff, 0));
+          for (int q4 = 0; q4 < 4; q4++) {
+            const int64_t u = m0 + 32 * i + 8 * q4;
+            const ScLoad L0 = sc_load(p.M, n_groups, u, sc_v, 0, g);
+            const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.a_scale + L0.base, (uint32_t)L0.nrec);
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              sc[4 * q4 + e] = __builtin_bit_cast(
+                  float, __builtin_amdgcn_raw_buffer_load_b32(rsc, sc_load(p.M, n_groups, u, sc_v, e, g).voff, 0, 0));
           }
 #pragma unroll
           for (int r = 0; r < 16; r++)
@@ -784,6 +849,72 @@ static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st)
 }
 
 size_t linear_workspace(const h3dit_linear_args &a) { return plan_linear(a).part_bytes; }
+
+// Host walk over every A load of the launch plan_linear chooses (all tiles, waves, lanes,
+// blocks and K slices), with the kernel's own addressing (a_load): the largest byte end of
+// a load the range check lets through, and the number of loads whose masking is wrong (a row
+// < M returning zeros, a row >= M reading memory, or a load that straddles its resource end).
+void linear_a_extent(const h3dit_linear_args &a, uint64_t *max_end, uint64_t *bad) {
+  const LinearPlan pl = plan_linear(a);
+  const bool i8 = a.precision == H3DIT_INT8;
+  const bool grouped = i8 && a.a_group > 0;
+  const int esz = i8 ? 1 : 2;
+  int BM, NW;
+  if (grouped) {
+    BM = 128; NW = 4;
+  } else if (pl.bn == 256) {
+    BM = 256; NW = i8 ? 8 : 4;
+  } else {
+    BM = 256; NW = 8;
+  }
+  const int LA = BM / (8 * NW);
+  const int KT = (int)(a.K * esz / GKB);
+  const int hm_hd = i8 ? 0 : a.a_headmajor_hd;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  uint64_t top = 0, nbad = 0;
+  for (int64_t tm = 0; tm < tiles_m; tm++)
+    for (int r0 = 0; r0 < NW * 8; r0++)
+      for (int cl = 0; cl < 8; cl++)
+        for (int li = 0; li < LA; li++)
+          for (int kt = 0; kt < KT; kt++) {
+            const int64_t m0 = tm * BM;
+            const ALoad L = a_load(a.M, a.K, esz, hm_hd, NW, m0, r0, cl, li, kt);
+            const int64_t row = m0 + r0 + (int64_t)NW * 8 * li;
+            const bool masked = (int64_t)L.voff >= L.nrec;
+            if (masked != (row >= a.M)) nbad++;
+            if (!masked) {
+              if ((int64_t)L.voff + L.soff + 16 > L.nrec) nbad++;
+              const uint64_t end = (uint64_t)(L.base + L.voff + L.soff + 16);
+              if (end > top) top = end;
+            }
+          }
+  if (grouped) {
+    // the group scales [M][K / a_group] fp32 of the grouped FC2 (4 waves of 64 x 64, 2 x 2)
+    const int ng = (int)(a.K / a.a_group);
+    uint64_t stop = 0;
+    for (int64_t tm = 0; tm < tiles_m; tm++)
+      for (int wm = 0; wm < 2; wm++)
+        for (int hsel = 0; hsel < 2; hsel++)
+          for (int i = 0; i < 2; i++)
+            for (int q4 = 0; q4 < 4; q4++)
+              for (int e = 0; e < 4; e++)
+                for (int g = 0; g < ng; g++) {
+                  const int64_t u = tm * BM + 32 * i + 8 * q4;
+                  const int v = wm * 64 + 4 * hsel;
+                  const ScLoad L = sc_load(a.M, ng, u, v, e, g);
+                  const bool masked = (int64_t)L.voff >= L.nrec;
+                  if (masked != (u + v + e >= a.M)) nbad++;
+                  if (!masked) {
+                    if ((int64_t)L.voff + 4 > L.nrec) nbad++;
+                    const uint64_t end = (uint64_t)(L.base * 4 + L.voff + 4);
+                    if (end > stop) stop = end;
+                  }
+                }
+    if (stop > (uint64_t)a.M * ng * 4) nbad++;
+  }
+  *max_end = top;
+  *bad = nbad;
+}
 
 hipError_t launch_linear(const h3dit_linear_args &a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;

@@ -45,8 +45,10 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 // this kernel, so the fused and the two-kernel sequences give the same bytes.
 // Modulation sets: rows [0, seg1) use gate/shift/scale as given, rows [seg1, seg2) the vectors
 // set_stride elements further, rows from seg2 on 2*set_stride further (set_stride 0: one set).
+// x_out may equal x (the residual updated in place): neither is marked __restrict__; a row's
+// loads all precede its stores and each workgroup touches only its own row.
 template <bool GATE, bool NORM, bool STATS = false>
-__global__ __launch_bounds__(ROW_THREADS) void k_row(int d, float eps, const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(ROW_THREADS) void k_row(int d, float eps, const uint16_t *x,
                                                      const uint16_t *__restrict__ gate,
                                                      const uint16_t *__restrict__ y, uint16_t *x_out,
                                                      const uint16_t *__restrict__ shift,

@@ -30,7 +30,7 @@
  *    the host weights of h3dit_stack_fwd_streamed, which its copies read later.
  *  - The caller owns every buffer.  Calls are asynchronous on `stream` (a hipStream_t;
  *    NULL means the default stream); no memory is allocated and the host never waits
- *    (h3dit_stack_fwd_streamed creates four HIP events per call, and its copies from
+ *    (h3dit_stack_fwd_streamed creates five HIP events per call, and its copies from
  *    pageable host memory may run synchronously).
  *  - bf16 is passed as uint16_t bit patterns.  Matrices are row-major; weights are
  *    [out][in].  Device pointers must be 16-byte aligned.
@@ -60,6 +60,7 @@ extern "C" {
 #define H3DIT_BF16 0
 #define H3DIT_INT8 1
 #define H3DIT_INT8_MLP 2   /* FC1 and FC2 in int8, QKV and output projection in bf16 */
+#define H3DIT_INT8_ATTN 3  /* QKV and output projection in int8, FC1 and FC2 in bf16 */
 
 /* Fusion switches ([DD] "DiT 融合内核": every fusion can be turned back into its step-wise
  * form for a byte-identical A/B).  Each flag selects the unfused sequence; the results are
@@ -89,7 +90,8 @@ typedef struct {
  * head-dim pairs (2j, 2j+1) by their t, h and w position in three consecutive sections of
  * rope_t, rope_h, rope_w dims (even, summing to head_dim) with frequencies
  * theta^(-2j/section); text and audio use 1-D rotary over the whole head dim at their
- * index within their own segment.  Tables are built on the device in double precision. */
+ * index within their own segment.  These built-in tables are made on the device in double
+ * precision whenever the caller passes no h3dit_rope tables of its own. */
 typedef struct {
   int32_t video_t, video_h, video_w, n_text, n_audio;
   int32_t rope_t, rope_h, rope_w;
@@ -107,8 +109,11 @@ typedef struct {
  * precision H3DIT_INT8: w_* are int8 codes of the same shapes and s_* fp32 per-output-row
  *   scales, as written by h3dit_quantize_weights.
  * precision H3DIT_INT8_MLP ([DD] "int8 量化", the table's int8-MLP row): w_qkv, w_o bf16 as
- *   in H3DIT_BF16; w_fc1, w_fc2 int8 codes with s_fc1, s_fc2.  Every block of a stack has the
- *   same precision.
+ *   in H3DIT_BF16; w_fc1, w_fc2 int8 codes with s_fc1, s_fc2.
+ * precision H3DIT_INT8_ATTN ([DD] "int8 量化", the int8-QKV-only path set against the full int8
+ *   path after the table): w_qkv, w_o int8 codes with s_qkv, s_o (the output projection's
+ *   input coded per token as in H3DIT_INT8); w_fc1, w_fc2 bf16 as in H3DIT_BF16.
+ * Every block of a stack has the same precision.
  * mod: bf16 [mod_sets][6][d] modulation rows shift1, scale1, gate1, shift2, scale2, gate2 per
  *   set, each set broadcast over its tokens ([DD] AdaLN branches are precomputable per block). */
 typedef struct {
@@ -117,6 +122,17 @@ typedef struct {
   const float *s_qkv, *s_o, *s_fc1, *s_fc2;
   const uint16_t *mod;
 } h3dit_block_w;
+
+/* Rotary tables ([DD] "h3.c 的核心设计": rotary positions applied to q and k before attention;
+ * [DD] "引用系统：Ref2VA 的多模态条件控制" and the preview note of [NS] "极简主控逻辑" place tokens
+ * on the rotary timeline in more than one way, so positions are data): cos, sin fp32
+ * [n][head_dim/2] (device, 16-byte aligned), n the tokens of the sequence they serve.  Token t's
+ * q and k pairs (2j, 2j+1) become (a cos[t][j] - b sin[t][j], a sin[t][j] + b cos[t][j]).
+ * A NULL h3dit_rope pointer, or NULL cos and sin, selects the built-in tables of the layout
+ * (h3dit_layout above; h3dit_rope_tables writes them out). */
+typedef struct {
+  const float *cos, *sin;
+} h3dit_rope;
 
 /* Token reduction ([DD] "Token 缩减"): after block index reduce_after (0-based) adjacent
  * horizontal video tokens (t,h,2k),(t,h,2k+1) are averaged into one token (the odd last
@@ -127,6 +143,7 @@ typedef struct {
  * reduce_after < n_blocks. */
 typedef struct {
   int32_t reduce_after, restore_before;
+  h3dit_rope rope_reduced;   /* rotary tables of the paired sequence; NULL pointers: built-in */
 } h3dit_token_reduction;
 
 /* Per-output-channel int8 weight codes ([DD] "int8 量化"): for each row r of w (bf16
@@ -144,19 +161,22 @@ H3DIT_API int h3dit_quantize_weights(const uint16_t *w, int64_t rows, int64_t co
  * to bf16.  int8 path: each projection input is quantised per token (FC2 input per
  * fc2_group channels), accumulated in int32 and dequantised as (acc * s_act) * s_w.
  * x: bf16 [n_tokens][hidden] device, in/out.  layout: token layout and rotary (host).
+ * rope: rotary tables of the n_tokens tokens, or NULL for the built-in ones.
  * workspace: device scratch of *workspace_bytes bytes; with workspace == NULL the required
  * size is written to *workspace_bytes and H3DIT_OK returned without launching. */
 H3DIT_API int h3dit_block_fwd(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_block_w *blk,
-                    uint16_t *x, uint32_t flags, void *workspace, size_t *workspace_bytes,
-                    void *stream);
+                              const h3dit_rope *rope, uint16_t *x, uint32_t flags, void *workspace,
+                              size_t *workspace_bytes, void *stream);
 
 /* A stack of n_blocks blocks for one denoising evaluation ([RV] README: 50-layer DiT;
  * [DD] fusion of each block's final gate with the next block's AdaLN1, and activation
  * arenas reused across lifetimes).  blocks: host array of n_blocks entries (device
- * pointers inside).  tr: NULL for no token reduction.  Other arguments as h3dit_block_fwd. */
+ * pointers inside).  rope: tables of the full sequence (NULL: built-in).  tr: NULL for no
+ * token reduction; its rope_reduced serves the blocks inside the paired span.  Other
+ * arguments as h3dit_block_fwd. */
 H3DIT_API int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
-                    const h3dit_block_w *blocks, const h3dit_token_reduction *tr, uint16_t *x,
-                    uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream);
+                              const h3dit_block_w *blocks, const h3dit_rope *rope, const h3dit_token_reduction *tr,
+                              uint16_t *x, uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream);
 
 /* h3dit_stack_fwd with the block matrices left in host memory ([RV] section "h3-metal 的 SSD
  * 串流：用速度換常駐記憶體": the small per-block weights stay resident while two full matrix
@@ -165,16 +185,17 @@ H3DIT_API int h3dit_stack_fwd(const h3dit_dims *dims, const h3dit_layout *layout
  * pointers (16-byte aligned; allocate them pinned, e.g. hipHostMalloc, or the copies run
  * synchronously and nothing overlaps).  Every block's mod rows are copied once into the
  * workspace; block b's matrices and scales are copied into slot b % 2 of the workspace on
- * copy_stream, after the block that last used that slot has finished on `stream`, and block b
- * waits for its copy.  Results are byte-identical to h3dit_stack_fwd with the same weights
+ * copy_stream, after the block that last used that slot has finished on `stream` (for blocks 0
+ * and 1: after all work enqueued on `stream` before the call, so back-to-back calls on one
+ * workspace are safe), and block b waits for its copy.  Results are byte-identical to h3dit_stack_fwd with the same weights
  * resident.  copy_stream: a second stream for the copies (NULL or equal to `stream`: copies
  * on `stream`, no overlap).  workspace: as h3dit_stack_fwd plus the mod rows and two slots
  * (NULL queries the size).  The host weights must stay valid until `stream` has completed
  * the call's work.  Errors as h3dit_stack_fwd. */
 H3DIT_API int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
-                                       const h3dit_block_w *blocks, const h3dit_token_reduction *tr, uint16_t *x,
-                                       uint32_t flags, void *workspace, size_t *workspace_bytes, void *stream,
-                                       void *copy_stream);
+                                       const h3dit_block_w *blocks, const h3dit_rope *rope,
+                                       const h3dit_token_reduction *tr, uint16_t *x, uint32_t flags,
+                                       void *workspace, size_t *workspace_bytes, void *stream, void *copy_stream);
 
 /* One modality of the final head: mod bf16 [2][d] (shift, scale), w bf16 [channels][d],
  * channels % 128 == 0 (device pointers). */
@@ -238,21 +259,33 @@ H3DIT_API int h3dit_denoise_plan(const h3dit_denoise_opts *opts, int32_t n_block
  * [count] (device), count % 8 == 0. */
 H3DIT_API int h3dit_velocity_step(int64_t count, float dt, const uint16_t *v, uint16_t *z, void *stream);
 
+/* Stand-in for the patch embedding of the latents (the pages name latents and a velocity
+ * head but not the embedding, so this linear map is a reading): w_video bf16 [hidden][c_v] and
+ * w_audio bf16 [hidden][c_a] (device; c_v, c_a the head parts' channels).  A core evaluation
+ * starts from x = x_in with video row r replaced by bf16(x_in[r] + bf16(z_video[r] w_video^T))
+ * and audio row r by bf16(x_in[r] + bf16(z_audio[r] w_audio^T)) (text rows: x_in), so the
+ * current latents feed the stack.  A NULL matrix leaves its rows at x_in. */
+typedef struct {
+  const uint16_t *w_video, *w_audio;
+} h3dit_patch_embed;
+
 /* A denoising loop over the plan of `opts`: for each step, a core step copies x_in into the
- * workspace residual and runs h3dit_stack_fwd over the first plan.n_blocks blocks (with the
- * step's token reduction), a fresh step runs h3dit_final_head on that residual into velocity
- * buffers, and every step applies h3dit_velocity_step with dt[step] to z_video and z_audio.
- * x_in (bf16 [n_tokens][hidden], device) is the residual every core evaluation starts from: it
- * stands in for the patch embedding of the current latents, which the pages do not describe,
- * so the latents do not feed back into the stack.  dt: host fp32 [steps].  video / audio and
- * z_video / z_audio as in h3dit_final_head (bf16 [n_video][channels], [n_audio][channels],
- * updated in place; at least one part).  workspace: NULL queries the size.  Errors as
- * h3dit_denoise_plan, h3dit_stack_fwd and h3dit_final_head. */
+ * workspace residual, adds the patch embedding of the current latents (embed non-NULL), and
+ * runs h3dit_stack_fwd over the first plan.n_blocks blocks (with the step's token reduction
+ * and the rotary tables rope / rope_reduced, NULL for built-in); a fresh step runs
+ * h3dit_final_head on that residual into velocity buffers; every step applies
+ * h3dit_velocity_step with dt[step] to z_video and z_audio.  x_in (bf16 [n_tokens][hidden],
+ * device) is the conditioning residual every core evaluation starts from; with embed == NULL
+ * it is the whole stack input and the latents do not feed back.  dt: host fp32 [steps].
+ * video / audio and z_video / z_audio as in h3dit_final_head (bf16 [n_video][channels],
+ * [n_audio][channels], updated in place; at least one part).  workspace: NULL queries the
+ * size.  Errors as h3dit_denoise_plan, h3dit_stack_fwd and h3dit_final_head. */
 H3DIT_API int h3dit_denoise_fwd(const h3dit_dims *dims, const h3dit_layout *layout, int32_t n_blocks,
-                                const h3dit_block_w *blocks, const h3dit_denoise_opts *opts, const float *dt,
-                                const uint16_t *x_in, const h3dit_head_part *video, const h3dit_head_part *audio,
-                                uint16_t *z_video, uint16_t *z_audio, uint32_t flags, void *workspace,
-                                size_t *workspace_bytes, void *stream);
+                                const h3dit_block_w *blocks, const h3dit_rope *rope, const h3dit_rope *rope_reduced,
+                                const h3dit_denoise_opts *opts, const float *dt, const uint16_t *x_in,
+                                const h3dit_patch_embed *embed, const h3dit_head_part *video,
+                                const h3dit_head_part *audio, uint16_t *z_video, uint16_t *z_audio, uint32_t flags,
+                                void *workspace, size_t *workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

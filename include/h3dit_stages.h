@@ -104,6 +104,13 @@ typedef struct {
 H3DIT_API int h3dit_linear(const h3dit_linear_args *args, void *stream);
 /* Workspace bytes h3dit_linear needs for these arguments, written to *bytes. */
 H3DIT_API int h3dit_linear_workspace(const h3dit_linear_args *args, uint64_t *bytes);
+/* Host only (no device work, pointers not dereferenced): walks every A-operand load of the
+ * launch h3dit_linear would make for these arguments, with the kernel's own addressing, and
+ * writes the largest byte offset past `a` that any load not masked by the buffer range check
+ * reads (*max_end, at most M*K*element size when the addressing is right) and the number of
+ * loads whose masking is wrong (*bad: a row < M masked, a row >= M not masked, or a load
+ * straddling the end of its buffer resource).  Validation as h3dit_linear. */
+H3DIT_API int h3dit_linear_a_extent(const h3dit_linear_args *args, uint64_t *max_end, uint64_t *bad);
 
 /* Rotary + head split of a token-major projection t bf16 [n][3*heads*head_dim] into q, k
  * head-major and v as V^T; the same arithmetic as H3DIT_OUT_QKV. */

@@ -250,7 +250,8 @@ def final_head(w, x, video=None, audio=None):
 def _block_struct(p: dict, keep: list) -> Block:
     """p: bf16 weights {wqkv, wo, w1, w2, mod} and, for int8, {qqkv, sqkv, qo, so, q1, s1, q2, s2}."""
     b = Block()
-    b.int8 = 1 if "qqkv" in p else (2 if "q1" in p else 0)
+    has_attn, has_mlp = "qqkv" in p, "q1" in p
+    b.int8 = 1 if (has_attn and has_mlp) else 3 if has_attn else 2 if has_mlp else 0
     b.mod_sets = p["mod"].shape[0] // 6
     for name in ("wqkv", "wo", "w1", "w2", "qqkv", "qo", "q1", "q2", "sqkv", "so", "s1", "s2", "mod"):
         t = p.get(name)
@@ -261,12 +262,15 @@ def _block_struct(p: dict, keep: list) -> Block:
     return b
 
 
-def quantize_block(p: dict, mlp_only: bool = False) -> dict:
-    """Adds the int8 codes and scales of the four weight matrices (or of FC1 and FC2 only, the
-    "int8 MLP" row of the pages' table) to a bf16 block dict."""
+def quantize_block(p: dict, mlp_only: bool = False, attn_only: bool = False) -> dict:
+    """Adds the int8 codes and scales of the four weight matrices to a bf16 block dict; or of
+    FC1 and FC2 only (mlp_only: the "int8 MLP" row of the pages' table); or of QKV and the
+    output projection only (attn_only: the int8-QKV-only path the pages set against it)."""
+    assert not (mlp_only and attn_only)
     out = dict(p)
     pairs = (("wqkv", "qqkv", "sqkv"), ("wo", "qo", "so"), ("w1", "q1", "s1"), ("w2", "q2", "s2"))
-    for w, q, s in (pairs[2:] if mlp_only else pairs):
+    sel = pairs[2:] if mlp_only else pairs[:2] if attn_only else pairs
+    for w, q, s in sel:
         out[q], out[s] = quantize_weights(p[w])
     return out
 
@@ -301,12 +305,22 @@ def block_fwd(w, p: dict, x, cos=None, sin=None, fused=False, taps=False, n_toke
     return (xo, tapd) if taps else xo
 
 
-def stack_fwd(w, blocks: list, x, reduce_after=-1, restore_before=-1, fused=False):
+def stack_fwd(w, blocks: list, x, reduce_after=-1, restore_before=-1, fused=False, rope=None, rope_reduced=None):
+    """rope / rope_reduced: (cos, sin) fp32 tables of the full / paired sequence, or None for
+    the layout's own (orc_rope_tables)."""
     keep = []
     arr = (Block * len(blocks))(*[_block_struct(p, keep) for p in blocks])
     xo = x.contiguous().clone()
+    tabs = []
+    for r in (rope, rope_reduced):
+        if r is None:
+            tabs += [None, None]
+        else:
+            c_, s_ = r[0].contiguous().to(torch.float32), r[1].contiguous().to(torch.float32)
+            keep += [c_, s_]
+            tabs += [_p(c_), _p(s_)]
     rc = lib().orc_stack_fwd(C.byref(dims_of(w)), C.byref(layout_of(w)), C.c_int32(len(blocks)), arr,
-                             C.c_int32(reduce_after), C.c_int32(restore_before), _p(xo), int(fused))
+                             C.c_int32(reduce_after), C.c_int32(restore_before), _p(xo), int(fused), *tabs)
     if rc != 0:
         raise ValueError(f"orc_stack_fwd failed: {rc}")
     return xo
@@ -333,21 +347,46 @@ def denoise_plan(steps, reuse=1, core_reuse=1, reduce_after=-1, restore_early=40
     return [dict(fresh=arrs[0][i], core=arrs[1][i], eval=arrs[2][i], restore=arrs[3][i]) for i in range(steps)]
 
 
-def denoise(w, blocks: list, x_in, opts: dict, dt, video=None, audio=None, z_video=None, z_audio=None):
-    """The denoising loop of the plan: a core step runs the first `layers` blocks from x_in
-    (with the step's token restore), a fresh step runs the final head on that residual, and
-    every step moves the latents by dt[i] times the current velocity.  Returns (z_video, z_audio)."""
-    plan = denoise_plan(opts["steps"], opts.get("reuse", 1), opts.get("core_reuse", 1), opts.get("reduce_after", -1),
-                        opts.get("restore_early", 40), opts.get("restore_late", 30), opts.get("early_evals", 10))
+def patch_embed(x_in, z, E):
+    """x_in rows (bf16 [n][d]) plus the patch-embedding stand-in of latents z (bf16 [n][c]) by
+    E (bf16 [d][c]): bf16(x_in + bf16(z E^T)) (orc_patch_embed)."""
+    n, d = x_in.shape
+    c = z.shape[1]
+    out = bf16((n, d))
+    lib().orc_patch_embed(_i64(n), C.c_int32(d), C.c_int32(c), _p(x_in.contiguous()), _p(z.contiguous()),
+                          _p(E.contiguous()), _p(out))
+    return out
+
+
+def denoise(w, blocks: list, x_in, opts: dict, dt, video=None, audio=None, z_video=None, z_audio=None, embed=None,
+            plan=None, rope=None, rope_reduced=None):
+    """The denoising loop of the plan: a core step starts from x_in (plus the patch embedding of
+    the current latents when embed = (E_video or None, E_audio or None) is given) and runs the
+    first `layers` blocks (with the step's token restore), a fresh step runs the final head on
+    that residual, and every step moves the latents by dt[i] times the latest velocity.
+    plan: a per-step list as denoise_plan returns, to replace the plan of opts (tests plant
+    wrong schedules through it).  Returns (z_video, z_audio)."""
+    if plan is None:
+        plan = denoise_plan(opts["steps"], opts.get("reuse", 1), opts.get("core_reuse", 1),
+                            opts.get("reduce_after", -1), opts.get("restore_early", 40), opts.get("restore_late", 30),
+                            opts.get("early_evals", 10))
     layers = opts.get("layers", len(blocks))
     zv = None if z_video is None else z_video.clone()
     za = None if z_audio is None else z_audio.clone()
     x = vv = va = None
+    n_video = x_in.shape[0] - w.n_text - w.n_audio
     for i, s in enumerate(plan):
         if s["core"]:
             red = opts.get("reduce_after", -1)
-            x = stack_fwd(w, blocks[:layers], x_in, reduce_after=red, restore_before=s["restore"] if red >= 0 else -1,
-                          fused=True)
+            xs = x_in
+            if embed is not None:
+                xs = x_in.clone()
+                if embed[0] is not None and zv is not None and n_video > 0:
+                    xs[:n_video] = patch_embed(x_in[:n_video], zv, embed[0])
+                if embed[1] is not None and za is not None and w.n_audio > 0:
+                    xs[-w.n_audio:] = patch_embed(x_in[-w.n_audio:], za, embed[1])
+            x = stack_fwd(w, blocks[:layers], xs, reduce_after=red, restore_before=s["restore"] if red >= 0 else -1,
+                          fused=True, rope=rope, rope_reduced=rope_reduced)
         if s["fresh"]:
             vv, va = final_head(w, x, video, audio)
         if zv is not None:

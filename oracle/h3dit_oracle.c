@@ -571,8 +571,9 @@ static int32_t block_body(const orc_dims *D, const orc_block *B, const float *co
                           uint16_t *h1_next, int32_t fused, orc_taps *T) {
   int64_t N = D->n_tokens;
   int32_t d = D->hidden, H = D->heads, hd = D->head_dim, f = D->mlp;
-  const int32_t i8_attn = B->int8 == 1, i8_mlp = B->int8 == 1 || B->int8 == 2;
-  if (d != H * hd || N <= 0 || f <= 0 || B->int8 < 0 || B->int8 > 2 ||
+  /* which projections run on int8 codes: 1 all four, 2 the MLP pair, 3 the attention pair */
+  const int32_t i8_attn = B->int8 == 1 || B->int8 == 3, i8_mlp = B->int8 == 1 || B->int8 == 2;
+  if (d != H * hd || N <= 0 || f <= 0 || B->int8 < 0 || B->int8 > 3 ||
       (i8_mlp && (D->fc2_group <= 0 || f % D->fc2_group)))
     return -1;
   if (D->n_video < 0 || D->n_text < 0 || (int64_t)D->n_video + D->n_text > N || (B->mod_sets != 1 && B->mod_sets != 3))
@@ -668,15 +669,25 @@ int32_t orc_block_fwd(const orc_dims *dims, const orc_block *blk, const float *c
  * if the stack ends first) every token is restored.  fused != 0 lets each block's final
  * gate also produce the next block's AdaLN1, except across a pair or restore step. */
 int32_t orc_stack_fwd(const orc_dims *dims, const orc_layout *L, int32_t n_blocks, const orc_block *blocks,
-                      int32_t reduce_after, int32_t restore_before, uint16_t *x, int32_t fused) {
+                      int32_t reduce_after, int32_t restore_before, uint16_t *x, int32_t fused,
+                      const float *cf_in, const float *sf_in, const float *cr_in, const float *sr_in) {
   int32_t reduce = reduce_after >= 0;
   int32_t hd = dims->head_dim, d = dims->hidden;
   int32_t Nf = orc_layout_tokens(L, 0), Nr = orc_layout_tokens(L, 1);
   if (Nf != dims->n_tokens || n_blocks <= 0) return -1;
   if (reduce && (restore_before <= reduce_after || reduce_after >= n_blocks)) return -1;
+  /* rotary tables: the caller's, else the layout's own */
   float *cf = xmalloc(sizeof(float) * (size_t)Nf * hd / 2), *sf = xmalloc(sizeof(float) * (size_t)Nf * hd / 2);
   float *cr = xmalloc(sizeof(float) * (size_t)Nr * hd / 2), *sr = xmalloc(sizeof(float) * (size_t)Nr * hd / 2);
   if (orc_rope_tables(L, hd, 0, cf, sf) < 0 || orc_rope_tables(L, hd, 1, cr, sr) < 0) return -1;
+  if (cf_in && sf_in) {
+    memcpy(cf, cf_in, sizeof(float) * (size_t)Nf * hd / 2);
+    memcpy(sf, sf_in, sizeof(float) * (size_t)Nf * hd / 2);
+  }
+  if (cr_in && sr_in) {
+    memcpy(cr, cr_in, sizeof(float) * (size_t)Nr * hd / 2);
+    memcpy(sr, sr_in, sizeof(float) * (size_t)Nr * hd / 2);
+  }
   uint16_t *bypass = xmalloc(2 * (size_t)Nf * d), *red = xmalloc(2 * (size_t)Nr * d),
            *r_in = xmalloc(2 * (size_t)Nr * d), *h1a = xmalloc(2 * (size_t)Nf * d),
            *h1b = xmalloc(2 * (size_t)Nf * d);
@@ -711,4 +722,19 @@ int32_t orc_stack_fwd(const orc_dims *dims, const orc_layout *L, int32_t n_block
   if (reduced) orc_token_restore(L, d, bypass, red, r_in, x);
   free(cf); free(sf); free(cr); free(sr); free(bypass); free(red); free(r_in); free(h1a); free(h1b);
   return rc;
+}
+
+/* Patch-embedding stand-in of the denoising loop (a reading: the pages name the latents and the
+ * velocity head, not the map from latents to the residual): the embedding of a latent row is
+ * its product with E rounded to bf16, added to the conditioning residual and rounded again. */
+void orc_patch_embed(int64_t n, int32_t d, int32_t c, const uint16_t *x_in, const uint16_t *z, const uint16_t *E,
+                     uint16_t *x_out) {
+  float *acc = xmalloc(sizeof(float) * (size_t)(n * d));
+  uint16_t *e = xmalloc(2 * (size_t)(n * d));
+  orc_gemm_f32(n, d, c, z, E, acc);
+  orc_f32_to_bf16(acc, e, n * d);
+  for (int64_t i = 0; i < n * d; i++) acc[i] = bf2f(x_in[i]) + bf2f(e[i]);
+  orc_f32_to_bf16(acc, x_out, n * d);
+  free(acc);
+  free(e);
 }

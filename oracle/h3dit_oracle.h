@@ -37,7 +37,9 @@ typedef struct {
 
 typedef struct {
   int32_t int8;                         /* int8 projections ([DD] "int8 量化" table rows): 0 none
-                                           (bf16); 1 all four; 2 FC1 and FC2 only ("int8 MLP") */
+                                           (bf16); 1 all four; 2 FC1 and FC2 only ("int8 MLP");
+                                           3 QKV and the output projection only (the int8-QKV-only
+                                           path compared with the full int8 path) */
   const uint16_t *wqkv, *wo, *w1, *w2;  /* bf16 [3d][d], [d][d], [f][d], [d][f] */
   const int8_t *qqkv, *qo, *q1, *q2;    /* int8, same shapes */
   const float *sqkv, *so, *s1, *s2;     /* fp32 per output row */
@@ -92,7 +94,14 @@ int32_t orc_token_restore(const orc_layout *L, int32_t d, const uint16_t *bypass
 /* whole block and stack */
 int32_t orc_block_fwd(const orc_dims *dims, const orc_block *blk, const float *cosv,
                       const float *sinv, uint16_t *x, int32_t fused, orc_taps *taps);
+/* cf/sf: rotary tables of the full sequence, cr/sr of the paired one (fp32 [n][head_dim/2]);
+ * NULL: the tables of orc_rope_tables for the layout. */
 int32_t orc_stack_fwd(const orc_dims *dims, const orc_layout *L, int32_t n_blocks,
                       const orc_block *blocks, int32_t reduce_after, int32_t restore_before,
-                      uint16_t *x, int32_t fused);
+                      uint16_t *x, int32_t fused, const float *cf, const float *sf, const float *cr,
+                      const float *sr);
+/* patch-embedding stand-in of the denoising loop: x_out[r] = bf16(x_in[r] + bf16(z[r] . E[j]))
+ * per row r < n and feature j < d; z bf16 [n][c], E bf16 [d][c] */
+void orc_patch_embed(int64_t n, int32_t d, int32_t c, const uint16_t *x_in, const uint16_t *z,
+                     const uint16_t *E, uint16_t *x_out);
 #endif

@@ -61,3 +61,43 @@ def assert_close_bf16(g, r, what="", max_frac_diff=0.02):
     rf = r.detach().to("cpu", torch.float64)
     big = rf.abs() > 0.01 * float(rf.abs().max())
     assert ulp_max(g.detach().to("cpu")[big], r.detach().to("cpu")[big]) <= 1, what
+
+
+def bf16_ulp(r):
+    """Spacing of bf16 numbers at |r| (float64 tensor): 2^(e - 7) for |r| in [2^e, 2^(e+1))."""
+    a = r.abs().clamp_min(2.0 ** -126)
+    return torch.exp2(torch.floor(torch.log2(a)) - 7)
+
+
+def update_stats(out, ref, x):
+    """Errors of a block or stack output judged on its update out - x (x is the input residual):
+    (residual max-norm relative error, largest per-element error in units of
+    (one bf16 step of |ref| + 2e-2 * max|ref - x|), largest per-row ratio of the mean update
+    error to the row's mean |ref - x|)."""
+    o = out.detach().to("cpu", torch.float64)
+    r = ref.detach().to("cpu", torch.float64)
+    x0 = x.detach().to("cpu", torch.float64)
+    dr = r - x0
+    err = (o - r).abs()
+    scale = float(dr.abs().max())
+    elem = float((err / (bf16_ulp(r) + BF16_TOL * scale)).max()) if err.numel() else 0.0
+    row_err = err.mean(dim=1)
+    row_upd = dr.abs().mean(dim=1)
+    row = float((row_err / row_upd.clamp_min(1e-30)).max()) if err.numel() else 0.0
+    if bool(((row_upd == 0) & (row_err > 0)).any()):
+        row = float("inf")
+    return relerr(out, ref), elem, row
+
+
+def assert_update_close(out, ref, x, what="", ulps=2.0, row_frac=0.1):
+    """The bf16 bar on the output, and its update out - x checked element by element and row by
+    row, so that one wrong token row, a ragged tail or one modulation segment fails even where
+    the update is small next to x:
+      - every element within `ulps` bf16 steps of |ref| plus 2e-2 of the update's max-norm (the
+        output is bf16(x + update): a rounding-sized change of the update moves it by a step);
+      - every row's mean |update error| within `row_frac` of that row's mean |update|."""
+    res, elem, row = update_stats(out, ref, x)
+    assert res <= BF16_TOL, (what, "residual", res)
+    assert elem <= ulps, (what, "element", elem)
+    assert row <= row_frac, (what, "row", row)
+    return res, elem, row

@@ -40,7 +40,9 @@ def test_struct_sizes_match_header_layout():
     assert C.sizeof(h3.Dims) == 28
     assert C.sizeof(h3.Layout) == 40
     assert C.sizeof(h3.BlockW) == 8 + 9 * 8
-    assert C.sizeof(h3.TokenReduction) == 8
+    assert C.sizeof(h3.TokenReduction) == 24   # two int32, then the two table pointers of rope_reduced
+    assert C.sizeof(h3.Rope) == 16
+    assert C.sizeof(h3.PatchEmbed) == 16
     assert C.sizeof(h3.LinearArgs) == 160   # 14 pointer-sized / int64 fields + 4 int32 pairs + 2 padded int32
 
 
@@ -53,7 +55,7 @@ def fake_block(precision=h3.BF16):
 
 def query(w, blk, flags=0):
     size = C.c_size_t(0)
-    rc = h3.lib().h3dit_block_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), C.byref(blk), None, flags,
+    rc = h3.lib().h3dit_block_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), C.byref(blk), None, None, flags,
                                   None, C.byref(size), None)
     return rc, size.value
 
@@ -91,9 +93,9 @@ def test_stack_workspace_with_reduction_is_larger():
     s0, s1 = C.c_size_t(0), C.c_size_t(0)
     tr = h3.TokenReduction(3, 40)
     lib = h3.lib()
-    assert lib.h3dit_stack_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), 50, arr, None, None, 0, None,
+    assert lib.h3dit_stack_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), 50, arr, None, None, None, 0, None,
                                C.byref(s0), None) == 0
-    assert lib.h3dit_stack_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), 50, arr, C.byref(tr), None, 0, None,
+    assert lib.h3dit_stack_fwd(C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w)), 50, arr, None, C.byref(tr), None, 0, None,
                                C.byref(s1), None) == 0
     nr = w.video_t * w.video_h * (w.video_w // 2 + 1) + w.n_text + w.n_audio
     assert s1.value - s0.value >= 2 * nr * w.hidden * 2
@@ -122,7 +124,7 @@ def test_bad_dims_rejected(change, code):
         layout.n_text = change["n_text"]
     size = C.c_size_t(0)
     blk = fake_block()
-    rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(layout), C.byref(blk), None, 0, None, C.byref(size), None)
+    rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(layout), C.byref(blk), None, None, 0, None, C.byref(size), None)
     assert rc == code
 
 
@@ -133,7 +135,7 @@ def test_int8_group_rules():
     blk = fake_block(h3.INT8)
     for g in (1000, 64, 3 * 1024):  # not a multiple of 128 / too small / does not divide mlp
         dims.fc2_group = g
-        rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(h3.layout_of(w)), C.byref(blk), None, 0, None,
+        rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(h3.layout_of(w)), C.byref(blk), None, None, 0, None,
                                       C.byref(size), None)
         assert rc == h3.EINVAL, g
 
@@ -146,22 +148,35 @@ def test_call_argument_errors_before_launch():
     ws = 1 << 24
     x = 1 << 22
     d, l = C.byref(h3.dims_of(w)), C.byref(h3.layout_of(w))
-    assert lib.h3dit_block_fwd(d, l, C.byref(blk), None, 0, ws, C.byref(size), None) == h3.EINVAL     # x NULL
-    assert lib.h3dit_block_fwd(d, l, C.byref(blk), x + 2, 0, ws, C.byref(size), None) == h3.EINVAL   # misaligned x
-    assert lib.h3dit_block_fwd(d, l, C.byref(blk), x, 0, ws + 16, C.byref(size), None) == h3.EINVAL  # workspace align
-    assert lib.h3dit_block_fwd(d, l, C.byref(blk), x, 1 << 9, ws, C.byref(size), None) == h3.EINVAL  # unknown flag
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), None, None, 0, ws, C.byref(size), None) == h3.EINVAL     # x NULL
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), None, x + 2, 0, ws, C.byref(size), None) == h3.EINVAL   # misaligned x
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), None, x, 0, ws + 16, C.byref(size), None) == h3.EINVAL  # workspace align
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), None, x, 1 << 9, ws, C.byref(size), None) == h3.EINVAL  # unknown flag
     small = C.c_size_t(1024)
-    assert lib.h3dit_block_fwd(d, l, C.byref(blk), x, 0, ws, C.byref(small), None) == h3.EWORKSPACE
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), None, x, 0, ws, C.byref(small), None) == h3.EWORKSPACE
     assert small.value > 1024                                                                          # size written back
     bad = fake_block()
     bad.w_fc1 = None
-    assert lib.h3dit_block_fwd(d, l, C.byref(bad), x, 0, ws, C.byref(size), None) == h3.EINVAL
+    assert lib.h3dit_block_fwd(d, l, C.byref(bad), None, x, 0, ws, C.byref(size), None) == h3.EINVAL
     mixed = fake_block(h3.INT8)
     mixed.s_o = None
-    assert lib.h3dit_block_fwd(d, l, C.byref(mixed), x, 0, ws, C.byref(size), None) == h3.EINVAL
+    assert lib.h3dit_block_fwd(d, l, C.byref(mixed), None, x, 0, ws, C.byref(size), None) == h3.EINVAL
+    # int8 attention projections only: their two scale arrays are required, the MLP's are not
+    attn = fake_block(h3.INT8_ATTN)
+    attn.s_fc1 = attn.s_fc2 = None
+    assert lib.h3dit_block_fwd(d, l, C.byref(attn), None, x, 0, ws, C.byref(size), None) not in (h3.EINVAL, h3.OK)
+    attn.s_qkv = None
+    assert lib.h3dit_block_fwd(d, l, C.byref(attn), None, x, 0, ws, C.byref(size), None) == h3.EINVAL
+    # caller rotary tables: both or neither, 16-byte aligned
+    for rope in (h3.Rope(x, None), h3.Rope(None, x), h3.Rope(x + 4, x), h3.Rope(x, x + 8)):
+        assert lib.h3dit_block_fwd(d, l, C.byref(blk), C.byref(rope), x, 0, ws, C.byref(size), None) == h3.EINVAL
+    ok = h3.Rope(x, x + 256)
+    assert lib.h3dit_block_fwd(d, l, C.byref(blk), C.byref(ok), x, 0, ws, C.byref(size), None) not in (h3.EINVAL, h3.OK)
     arr = (h3.BlockW * 2)(fake_block(), fake_block())
+    tr = h3.TokenReduction(0, 1, h3.Rope(x + 4, x))
+    assert lib.h3dit_stack_fwd(d, l, 2, arr, None, C.byref(tr), x, 0, ws, C.byref(size), None) == h3.EINVAL
     for tr in (h3.TokenReduction(3, 3), h3.TokenReduction(-1, 4), h3.TokenReduction(2, 5)):
-        assert lib.h3dit_stack_fwd(d, l, 2, arr, C.byref(tr), x, 0, ws, C.byref(size), None) == h3.EINVAL
+        assert lib.h3dit_stack_fwd(d, l, 2, arr, None, C.byref(tr), x, 0, ws, C.byref(size), None) == h3.EINVAL
     assert lib.h3dit_quantize_weights(x, 4, 12, x, x, None) == h3.EINVAL      # cols % 8
     assert lib.h3dit_attention(4, 100, 96, x, x, x, x, None, None, None) == h3.EINVAL
     args = h3.LinearArgs(M=10, N=100, K=128, precision=h3.BF16, a=x, w=x, out=x, out_kind=h3.OUT_BF16)
@@ -197,6 +212,25 @@ def test_linear_workspace_plan():
     assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EINVAL       # misaligned
 
 
+@pytest.mark.parametrize("M", [1, 7, 64, 129, 255, 256, 257, 300, 513, 2048, 4097, 4480])
+def test_linear_a_loads_stay_inside_a(M):
+    """Walks every A-operand load (and, for the grouped FC2, every group-scale load) of the
+    launch h3dit_linear plans, with the kernel's own addressing: a ragged last tile reads
+    nothing past the M rows of A (largest byte end == M*K*element size), rows past M are the
+    ones masked by the range check, and no load straddles its resource end."""
+    for N, K, prec, group, hm in ((256, 256, h3.BF16, 0, 0),          # small: 256 x 128 tiles
+                                  (5120, 5120, h3.BF16, 0, 0),        # 256 x 256 bf16, split-K tail
+                                  (15360, 5120, h3.INT8, 0, 0),       # 256 x 256 int8 (8 waves)
+                                  (5120, 5120, h3.BF16, 0, 128),      # head-major attention output
+                                  (768, 256, h3.BF16, 0, 64),         # head-major, head_dim 64
+                                  (1024, 4096, h3.INT8, 1024, 0),     # grouped FC2 (128 x 128)
+                                  (256, 8192, h3.INT8, 128, 0)):      # grouped, many groups
+        end, bad = h3.linear_a_extent(M, N, K, prec, group, a_headmajor_hd=hm)
+        esz = 1 if prec == h3.INT8 else 2
+        assert bad == 0, (M, N, K, prec, group, hm, bad)
+        assert end == M * K * esz, (M, N, K, prec, group, hm, end)
+
+
 def test_linear_plan_depends_on_shape_and_precision_only():
     """A fused epilogue and its unfused sequence (bf16 output, then the GELU or rotary kernel)
     must split K alike for the fusion switches to stay byte-identical: the split-K workspace,
@@ -226,9 +260,9 @@ def test_stack_streamed_workspace_and_validation():
         arr = (h3.BlockW * n)(*[fake_block(prec) for _ in range(n)])
         dims, lay = h3.dims_of(w), h3.layout_of(w)
         res, stm = C.c_size_t(0), C.c_size_t(0)
-        assert h3.lib().h3dit_stack_fwd(C.byref(dims), C.byref(lay), n, arr, None, None, 0, None, C.byref(res),
+        assert h3.lib().h3dit_stack_fwd(C.byref(dims), C.byref(lay), n, arr, None, None, None, 0, None, C.byref(res),
                                         None) == 0
-        assert h3.lib().h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), n, arr, None, None, 0, None,
+        assert h3.lib().h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), n, arr, None, None, None, 0, None,
                                                  C.byref(stm), None, None) == 0
         mats = [3 * d * d * ea, d * d * ea, f * d * em, d * f * em]
         scales = [3 * d * 4 if ea == 1 else 0, d * 4 if ea == 1 else 0, f * 4 if em == 1 else 0,
@@ -239,18 +273,18 @@ def test_stack_streamed_workspace_and_validation():
     size = C.c_size_t(0)
     dims, lay = h3.dims_of(w), h3.layout_of(w)
     lib = h3.lib()
-    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 0, arr, None, None, 0, None, C.byref(size),
+    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 0, arr, None, None, None, 0, None, C.byref(size),
                                         None, None) == h3.EINVAL                        # no blocks
     bad = h3.TokenReduction(1, 1)
-    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, arr, C.byref(bad), None, 0, None,
+    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, arr, None, C.byref(bad), None, 0, None,
                                         C.byref(size), None, None) == h3.EINVAL         # empty reduced span
-    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, None, None, None, 0, None, C.byref(size),
+    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, None, None, None, None, 0, None, C.byref(size),
                                         None, None) == h3.EINVAL                        # NULL block array
     arr2 = (h3.BlockW * 1)(fake_block(h3.BF16))
     arr2[0].w_o = (1 << 20) + 8
     x = 1 << 20
     size = C.c_size_t(1 << 40)
-    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, arr2, None, x, 0, x, C.byref(size), None,
+    assert lib.h3dit_stack_fwd_streamed(C.byref(dims), C.byref(lay), 1, arr2, None, None, x, 0, x, C.byref(size), None,
                                         None) == h3.EINVAL                              # misaligned host matrix
 
 
@@ -263,7 +297,7 @@ def test_int8_row_level_fc2_group_accepted():
     blk = fake_block(h3.INT8)
     for g, ok in ((w.mlp, True), (10240, False), (4096, True)):
         dims.fc2_group = g
-        rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(h3.layout_of(w)), C.byref(blk), None, 0, None,
+        rc = h3.lib().h3dit_block_fwd(C.byref(dims), C.byref(h3.layout_of(w)), C.byref(blk), None, None, 0, None,
                                       C.byref(size), None)
         assert (rc == 0) == ok, g
 
@@ -274,7 +308,7 @@ def test_mod_sets_validated():
     for m, ok in ((0, True), (1, True), (3, True), (2, False), (6, False)):
         lay = h3.layout_of(w)
         lay.mod_sets = m
-        rc = h3.lib().h3dit_block_fwd(C.byref(h3.dims_of(w)), C.byref(lay), C.byref(fake_block()), None, 0, None,
+        rc = h3.lib().h3dit_block_fwd(C.byref(h3.dims_of(w)), C.byref(lay), C.byref(fake_block()), None, None, 0, None,
                                       C.byref(size), None)
         assert (rc == 0) == ok, m
 
@@ -351,26 +385,41 @@ def test_velocity_step_and_denoise_validation():
     dt = (C.c_float * 20)(*([-0.05] * 20))
     size = C.c_size_t(0)
     opts = h3.denoise_opts(20, reuse=2, layers=45)
-    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(opts), dt, None, C.byref(head), None, None, None, 0, None,
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, None, None, C.byref(opts), dt, None, None, C.byref(head), None, None, None, 0, None,
                                  C.byref(size), None) == 0
     stack = h3.stack_workspace(w, [dict(wqkv=a, wo=a, w1=a, w2=a, mod=a)] * 45)
     n_video = w.n_tokens - w.n_text - w.n_audio
     assert size.value >= w.n_tokens * w.hidden * 2 + n_video * 128 * 2 + stack
     red = h3.denoise_opts(20, reuse=2, layers=45, reduce_after=3)
     rsize = C.c_size_t(0)
-    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(red), dt, None, C.byref(head), None, None, None, 0, None,
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, None, None, C.byref(red), dt, None, None, C.byref(head), None, None, None, 0, None,
                                  C.byref(rsize), None) == 0
     assert rsize.value > size.value
     # no head part, a bad plan, a short workspace: rejected before any launch
-    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(opts), dt, None, None, None, None, None, 0, None,
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, None, None, C.byref(opts), dt, None, None, None, None, None, None, 0, None,
                                  C.byref(size), None) == h3.EINVAL
     bad = h3.denoise_opts(20, reuse=2, core_reuse=2, layers=45)
-    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(bad), dt, None, C.byref(head), None, None, None, 0, None,
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, None, None, C.byref(bad), dt, None, None, C.byref(head), None, None, None, 0, None,
                                  C.byref(size), None) == h3.EINVAL
     small = C.c_size_t(256)
-    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(opts), dt, a, C.byref(head), None, a, None, 0, a,
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, None, None, C.byref(opts), dt, a, None, C.byref(head), None, a, None, 0, a,
                                  C.byref(small), None) == h3.EWORKSPACE
     assert small.value == size.value
+    # the patch-embedding stand-in: its product and row buffer fit the shared region (the size
+    # does not grow at 4096 tokens, where the stack's arenas are larger), a misaligned matrix
+    # is rejected, and so are misaligned caller tables
+    emb = h3.PatchEmbed(a, None)
+    esize = C.c_size_t(0)
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, None, None, C.byref(opts), dt, None, C.byref(emb), C.byref(head),
+                                 None, None, None, 0, None, C.byref(esize), None) == 0
+    assert esize.value == size.value
+    emb = h3.PatchEmbed(a + 2, None)
+    big = C.c_size_t(size.value)
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, None, None, C.byref(opts), dt, a, C.byref(emb), C.byref(head),
+                                 None, a, None, 0, a, C.byref(big), None) == h3.EINVAL
+    rope = h3.Rope(a + 4, a)
+    assert lib.h3dit_denoise_fwd(d, l, 50, blocks, C.byref(rope), None, C.byref(opts), dt, None, None, C.byref(head),
+                                 None, None, None, 0, None, C.byref(esize), None) == h3.EINVAL
 
 
 def test_sizes_beyond_32bit_offsets_rejected():
@@ -387,7 +436,7 @@ def test_sizes_beyond_32bit_offsets_rejected():
         layout.video_t, layout.video_h, layout.video_w = 1, 1, n_video_w
         layout.n_text, layout.n_audio = 0, 0
         dims = h3.Dims(n_video_w, hidden, heads, 128, mlp, 1024, 1e-6)
-        return lib.h3dit_block_fwd(C.byref(dims), C.byref(layout), C.byref(blk), None, 0, None, C.byref(size), None)
+        return lib.h3dit_block_fwd(C.byref(dims), C.byref(layout), C.byref(blk), None, None, 0, None, C.byref(size), None)
 
     assert query(52428, 20480) == 0                   # 52428 * 20480 * 2 < 2^31
     assert query(52429, 20480) == h3.EINVAL

@@ -253,3 +253,42 @@ def test_stack_streamed_equals_resident_full_size():
     cs = torch.cuda.Stream()
     s(xs, ws, copy_stream=cs.cuda_stream)
     assert_bitexact(cpu(xs), cpu(xr), "streamed vs resident, 4096 tokens")
+
+
+# A production-width stack the oracle finishes in seconds: d 5120, 40 x 128 heads, MLP 20480,
+# 576 tokens (2 x 16 x 15 video, odd width, + 64 text + 32 audio), six blocks with their own
+# seeded weights and real gates, token pairing after block 1 (352 tokens in blocks 2 and 3) and
+# the restore before block 4.
+PROD_TR = WORKLOADS[4].replace(video_t=2, video_h=16, video_w=15, n_text=64, n_audio=32, blocks=6,
+                               reduce_after=1, restore_before=4)
+
+
+@pytest.mark.parametrize("int8", [False, True], ids=["bf16", "int8"])
+def test_stack_production_width_matches_oracle(int8):
+    """The whole stack call at production width against the oracle's stack, judged on the
+    update x_out - x_in: its max-norm relative error within 2e-2 (the bf16 bar), and element
+    by element and row by row as in the block tests."""
+    from parity import assert_update_close
+    w = PROD_TR
+    assert w.n_tokens == 576
+    seed = 1077
+    x = synth.make_x(w, seed, DEV)
+    pg, pc = [], []
+    for b in range(w.blocks):
+        p = synth.make_block(w, seed, b, DEV)
+        if int8:
+            p = h3.quantize_block(p)
+        pg.append(p)
+        pc.append({k: cpu(v) for k, v in p.items()})
+    xg = x.clone()
+    h3.stack_fwd(w, pg, xg, reduction=(w.reduce_after, w.restore_before))
+    out = cpu(xg)
+    xc = cpu(x)
+    ref = oracle.stack_fwd(w, pc, xc, reduce_after=w.reduce_after, restore_before=w.restore_before, fused=True)
+    du = out.double() - xc.double()
+    dr = ref.double() - xc.double()
+    upd = relerr(du, dr)
+    res, elem, row = assert_update_close(out, ref, xc, "production-width stack")
+    print(f"[prod stack {'int8' if int8 else 'bf16'}] update max-norm {upd:.3e}, residual {res:.3e}, "
+          f"element {elem:.3f}, row {row:.3f}", flush=True)
+    assert upd <= BF16_TOL

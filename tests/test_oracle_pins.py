@@ -823,3 +823,156 @@ def test_denoise_loop_is_euler_over_the_plan():
     a, _ = oracle.denoise(w, blocks, x, opts, [-1.0, 0.0, 0.0], video=(mv, wv), z_video=z0)
     b, _ = oracle.denoise(w, blocks, x, opts, [0.0, 0.0, -1.0], video=(mv, wv), z_video=z0)
     assert not torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- int8 attention projections only
+
+def _gate_zero(p, which):
+    q = dict(p)
+    mod = p["mod"].clone()
+    mod[which] = 0
+    q["mod"] = mod
+    return q
+
+
+def test_int8_attn_only_block():
+    """QKV and the output projection in int8, FC1 and FC2 in bf16 (the int8-QKV-only path):
+    its attention half is the full int8 block's, bytewise (both with gate2 = 0, whose output is
+    x1 exactly, I1); its MLP half is the bf16 block's given the same x1 (a bf16 block with
+    gate1 = 0 run from that x1), bytewise."""
+    x, p = _tiny_inputs()
+    pa = oracle.quantize_block(p, attn_only=True)
+    assert "qqkv" in pa and "q1" not in pa
+    out = oracle.block_fwd(W0, pa, x)
+    x1_attn = oracle.block_fwd(W0, _gate_zero(pa, 5), x)
+    x1_full = oracle.block_fwd(W0, _gate_zero(oracle.quantize_block(p), 5), x)
+    assert torch.equal(x1_attn.view(torch.int16), x1_full.view(torch.int16))
+    mlp_bf16 = oracle.block_fwd(W0, _gate_zero(p, 2), x1_attn)
+    assert torch.equal(out.view(torch.int16), mlp_bf16.view(torch.int16))
+    # and it is neither the bf16 block nor the full int8 block
+    for other in (p, oracle.quantize_block(p)):
+        assert not torch.equal(out.view(torch.int16), oracle.block_fwd(W0, other, x).view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- caller rotary tables
+
+def _random_tables(n, hd, seed):
+    g = torch.Generator().manual_seed(seed)
+    ang = torch.rand(n, hd // 2, generator=g, dtype=torch.float64) * 2 * math.pi
+    return torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)
+
+
+def test_stack_uses_caller_rotary_tables():
+    """The stack with caller tables equals the blocks chained with those tables, bytewise (the
+    block takes its tables as an input); the layout's own tables passed explicitly equal the
+    default; other tables give another result; and the paired span uses the reduced tables
+    (against the step-wise composition of block, pair, blocks, restore)."""
+    w = _small_tr(7)
+    x, blocks = _stack_inputs(w, 4)
+    ct, st = _random_tables(w.n_tokens, w.head_dim, 1)
+    a = oracle.stack_fwd(w, blocks[:2], x, fused=True, rope=(ct, st))
+    y = x
+    for p in blocks[:2]:
+        y = oracle.block_fwd(w, p, y, ct, st)
+    assert torch.equal(a.view(torch.int16), y.view(torch.int16))
+    own = oracle.rope_tables(w)
+    b = oracle.stack_fwd(w, blocks[:2], x, fused=True, rope=own)
+    c = oracle.stack_fwd(w, blocks[:2], x, fused=True)
+    assert torch.equal(b.view(torch.int16), c.view(torch.int16))
+    assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
+    cr, sr = _random_tables(oracle.layout_tokens(w, True), w.head_dim, 2)
+    out = oracle.stack_fwd(w, blocks, x, reduce_after=0, restore_before=3, fused=True, rope=(ct, st),
+                           rope_reduced=(cr, sr))
+    y = oracle.block_fwd(w, blocks[0], x, ct, st)
+    r = oracle.token_pair(w, y)
+    z = oracle.block_fwd(w, blocks[1], r, cr, sr)
+    z = oracle.block_fwd(w, blocks[2], z, cr, sr)
+    y = oracle.token_restore(w, y, z, r)
+    y = oracle.block_fwd(w, blocks[3], y, ct, st)
+    assert torch.equal(out.view(torch.int16), y.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- patch-embedding stand-in
+
+def test_patch_embed_exact_cases():
+    """bf16(x + bf16(z E^T)): with small-integer z and E every fp32 sum is exact, so the result
+    equals the float64 composition bit for bit; E = 0 leaves x; a one-hot E row copies one
+    latent channel into one feature (E is [d][c])."""
+    g = torch.Generator().manual_seed(21)
+    n, d, c = 37, 256, 128
+    x = bf(torch.randn(n, d, generator=g, dtype=torch.float64))
+    z = torch.randint(-4, 5, (n, c), generator=g).to(torch.bfloat16)
+    E = torch.randint(-3, 4, (d, c), generator=g).to(torch.bfloat16)
+    out = oracle.patch_embed(x, z, E)
+    e = bf(z.to(torch.float64) @ E.to(torch.float64).T)
+    ref = bf(x.to(torch.float64) + e.to(torch.float64))
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    zero = torch.zeros((d, c), dtype=torch.bfloat16)
+    assert torch.equal(oracle.patch_embed(x, z, zero).view(torch.int16), x.view(torch.int16))
+    one = torch.zeros((d, c), dtype=torch.bfloat16)
+    one[5, 3] = 1.0
+    xz = torch.zeros((n, d), dtype=torch.bfloat16)
+    got = oracle.patch_embed(xz, z, one)
+    assert torch.equal(got[:, 5].view(torch.int16), z[:, 3].view(torch.int16))
+    assert float(got[:, :5].abs().max()) == 0.0
+
+
+def test_denoise_latents_feed_back_through_the_embedding():
+    """With the embedding stand-in the loop is closed: E = 0 gives the loop without it, bytewise;
+    otherwise each core evaluation starts from x_in plus the embedding of the latents of its own
+    step (composition of the oracle's parts over a 3-step plan with reuse 2: steps 0 and 2
+    evaluate, step 1 repeats the velocity of step 0)."""
+    w = W0
+    d = w.hidden
+    x = synth.make_x(w, 1013)
+    blocks = [synth.make_block(w, 1013, b) for b in range(2)]
+    g = torch.Generator().manual_seed(6)
+    mv = bf(torch.randn(2, d, generator=g) * 0.1)
+    wv = bf(torch.randn(128, d, generator=g) * 0.02)
+    ev = bf(torch.randn(d, 128, generator=g) * 0.2)
+    nv = w.n_tokens - w.n_text - w.n_audio
+    z0 = bf(torch.randn(nv, 128, generator=g))
+    dt = [-0.3, -0.3, -0.4]
+    opts = dict(steps=3, reuse=2, layers=2)
+    plain, _ = oracle.denoise(w, blocks, x, opts, dt, video=(mv, wv), z_video=z0)
+    zero, _ = oracle.denoise(w, blocks, x, opts, dt, video=(mv, wv), z_video=z0,
+                             embed=(torch.zeros_like(ev), None))
+    assert torch.equal(plain.view(torch.int16), zero.view(torch.int16))
+    got, _ = oracle.denoise(w, blocks, x, opts, dt, video=(mv, wv), z_video=z0, embed=(ev, None))
+
+    def velocity(z):
+        xs = x.clone()
+        xs[:nv] = oracle.patch_embed(x[:nv], z, ev)
+        v, _ = oracle.final_head(w, oracle.stack_fwd(w, blocks, xs, fused=True), video=(mv, wv))
+        return v
+
+    v0 = velocity(z0)
+    z1 = oracle.velocity_step(z0, v0, dt[0])
+    z2 = oracle.velocity_step(z1, v0, dt[1])
+    z3 = oracle.velocity_step(z2, velocity(z2), dt[2])
+    assert torch.equal(got.view(torch.int16), z3.view(torch.int16))
+    assert not torch.equal(got.view(torch.int16), plain.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- the update check itself
+
+def test_update_check_rejects_one_wrong_row():
+    """The GPU tests judge a block's update (out - x) per element and per row: the oracle's own
+    output passes, a one-step change of scattered elements passes, and one token row whose update
+    is dropped, doubled or taken from another row fails (the residual max-norm alone accepts all
+    of them, the update being small next to x)."""
+    from parity import assert_update_close, update_stats
+    x, p = _tiny_inputs()
+    ref = oracle.block_fwd(W0, p, x)
+    assert_update_close(ref, ref, x)
+    nudged = ref.clone().view(torch.int16)
+    nudged.view(-1)[::97] += 1                       # one bf16 step on 1% of the elements
+    assert_update_close(nudged.view(torch.bfloat16), ref, x)
+    for name, row_fn in (("dropped", lambda r: x[r]), ("doubled", lambda r: bf(2 * ref[r].double() - x[r].double())),
+                         ("swapped", lambda r: bf(x[r].double() + ref[r + 1].double() - x[r + 1].double()))):
+        bad = ref.clone()
+        bad[200] = row_fn(200)
+        res, elem, row = update_stats(bad, ref, x)
+        assert res <= 2e-2, name                     # invisible on the residual
+        with pytest.raises(AssertionError):
+            assert_update_close(bad, ref, x, name)
