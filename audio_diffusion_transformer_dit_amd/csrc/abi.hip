@@ -595,10 +595,15 @@ int h3dit_stack_fwd_streamed(const h3dit_dims *dims, const h3dit_layout *layout,
   return run_stack(c, n_blocks, dev.data(), rope, tr, x, before, after);
 }
 
-int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,
-                     const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video, uint16_t *out_audio,
-                     void *workspace, size_t *workspace_bytes, void *stream) {
-  if (!workspace_bytes) return H3DIT_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// The final head's checks, its statistics bytes (8 per row of the larger part), and, with
+// stats != nullptr, its launches.  Returns H3DIT_OK, 1 for a size query answered, or an error.
+int final_head_impl(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,
+                    const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video, uint16_t *out_audio,
+                    float *stats, size_t *stats_bytes, hipStream_t st) {
   int rc = check_dims(dims, layout, H3DIT_BF16);
   if (rc) return rc;
   const int64_t N = dims->n_tokens, d = dims->hidden;
@@ -617,28 +622,59 @@ int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h
     if (q.p->channels < 128 || q.p->channels % 128) return H3DIT_EINVAL;
     if ((size_t)q.n * 8 > st_bytes) st_bytes = (size_t)q.n * 8;
   }
-  const size_t total = up(st_bytes);
-  if (!workspace) {
-    *workspace_bytes = total;
-    return H3DIT_OK;
-  }
-  if (!x || !aligned(x, 16) || !aligned(workspace, ALIGN)) return H3DIT_EINVAL;
+  *stats_bytes = up(st_bytes);
+  if (!stats) return 1;
+  if (!x || !aligned(x, 16)) return H3DIT_EINVAL;
   for (const Part &q : parts)
     if (q.p && q.n > 0 && (!q.out || !aligned(q.out, 16))) return H3DIT_EINVAL;
-  if (*workspace_bytes < total) {
-    *workspace_bytes = total;
-    return H3DIT_EWORKSPACE;
-  }
-  if ((rc = check_device())) return rc;
-  float *stats = reinterpret_cast<float *>(workspace);
-  const hipStream_t st = (hipStream_t)stream;
-  for (const Part &q : parts) {
+  return H3DIT_OK;
+}
+
+int final_head_launch(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,
+                      const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video, uint16_t *out_audio,
+                      float *stats, hipStream_t st) {
+  const int64_t N = dims->n_tokens, d = dims->hidden;
+  const int64_t n_video = N - layout->n_text - layout->n_audio, n_audio = layout->n_audio;
+  const struct {
+    const h3dit_head_part *p;
+    int64_t r0, n;
+    uint16_t *out;
+  } parts[2] = {{video, 0, n_video, out_video}, {audio, N - n_audio, n_audio, out_audio}};
+  for (const auto &q : parts) {
     if (!q.p || q.n == 0) continue;
     // the modality's rows are read in place at their offset in the residual
     TRY(launch_row_stats(q.n, (int)d, dims->ln_eps, x + q.r0 * d, stats, st));
     TRY(launch_head_gemm(q.n, q.p->channels, (int)d, x + q.r0 * d, stats, q.p->mod, q.p->mod + d, q.p->w, q.out, st));
   }
   return H3DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,
+                     const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video, uint16_t *out_audio,
+                     void *workspace, size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes) return H3DIT_EINVAL;
+  size_t total = 0;
+  int rc = final_head_impl(dims, layout, video, audio, nullptr, nullptr, nullptr, nullptr, &total, nullptr);
+  if (rc < 0) return rc;
+  if (!workspace) {
+    *workspace_bytes = total;
+    return H3DIT_OK;
+  }
+  if (!aligned(workspace, ALIGN)) return H3DIT_EINVAL;
+  rc = final_head_impl(dims, layout, video, audio, x, out_video, out_audio, reinterpret_cast<float *>(workspace),
+                       &total, (hipStream_t)stream);
+  if (rc) return rc;
+  if (*workspace_bytes < total) {
+    *workspace_bytes = total;
+    return H3DIT_EWORKSPACE;
+  }
+  if ((rc = check_device())) return rc;
+  return final_head_launch(dims, layout, video, audio, x, out_video, out_audio, reinterpret_cast<float *>(workspace),
+                           (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- denoising loop

@@ -89,10 +89,12 @@ __device__ __forceinline__ void tile_coords(int b, int &tm, int &tn, int tiles_m
 // is tile row r0, 16-byte chunk cl, K slice kt.  The range check of a raw buffer load covers
 // the vector offset (plus the instruction offset), not the scalar offset, so everything that
 // depends on the row sits in the vector offset or in the resource: block li reads through a
-// resource based li block strides further on with its record count shortened to match, and a
-// head-major A (the attention output [K/hd][M][hd]) has the head in the resource base and
-// one head's rows as its records.  A load returns zeros exactly when its row is >= M
-// (voff >= nrec); every other load stays inside [base, base + nrec).
+// resource based li block strides further on with its record count shortened to match.
+// Token-major A: a load returns zeros exactly when its row is >= M (voff >= nrec).  Head-major
+// A (the attention output [K/hd][M][hd]): the slice's head offset goes into the vector offset
+// too (one add per slice), so a row >= M of head h reads row (row - M) of head h + 1 (its sums
+// are never stored) and past the last head the range check returns zeros.  Every load that is
+// not masked stays inside [base, base + nrec), i.e. inside A.
 struct ALoad {
   int64_t base;   // byte offset of the resource base from A
   int64_t nrec;   // bytes the resource covers (>= 0)
@@ -107,9 +109,10 @@ __host__ __device__ __forceinline__ ALoad a_load(int64_t M, int64_t K, int esz, 
   if (hm_hd) {
     const int64_t kel = (int64_t)kt * (GKB / 2);         // first element of the slice (bf16)
     const int64_t head = kel / hm_hd;
-    L.base = (head * M + rows_before) * hm_hd * 2;
-    L.nrec = left * hm_hd * 2;
-    L.voff = (uint32_t)((m0 + r0) * hm_hd * 2 + cl * 16);
+    const int64_t total = M * K * 2;
+    L.base = rows_before * hm_hd * 2;
+    L.nrec = total - L.base > 0 ? total - L.base : 0;
+    L.voff = (uint32_t)((m0 + r0) * hm_hd * 2 + cl * 16 + head * M * hm_hd * 2);
     L.soff = (uint32_t)((kel % hm_hd) * 2);
   } else {
     L.base = rows_before * K * esz;
@@ -191,7 +194,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
   const int hm_hd = hm ? p.hm_hd : 0;
   const int r0 = wid * 8 + rl;                         // row of block 0
   const int sw = (cl ^ ((r0 >> 1) & 7)) << 4;          // swizzled 16-byte slot (same for every block)
-  const uint32_t a_voff = a_load(p.M, p.K, esz, hm_hd, NW, m0, r0, cl, 0, 0).voff;   // the same for every block
+  const uint32_t a_voff = a_load(p.M, p.K, esz, hm_hd, NW, m0, r0, cl, 0, 0).voff;   // every block, head 0
+  const uint32_t hm_head = hm ? (uint32_t)(p.M * p.hm_hd * 2) : 0u;                    // bytes per head
+  const uint32_t hm_shift = hm ? (p.hm_hd == 128 ? 7u : 6u) : 0u;
+  const uint32_t hm_mask = hm ? (uint32_t)(p.hm_hd - 1) : 0u;
   const uint32_t w_voff = (uint32_t)((n0 + r0) * p.K * esz + cl * 16);
   const uint32_t w_bstride = (uint32_t)(NW * 8 * p.K * esz);
   const uint32_t lds0 = (uint32_t)(r0 * GKB + sw);     // LDS byte offset of block 0 (A); blocks step NW*1 KiB
@@ -199,12 +205,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
     const ALoad L = a_load(p.M, p.K, esz, hm_hd, NW, m0, r0, cl, li, kt);
     return make_rsrc(p.a + L.base, (uint32_t)L.nrec);
   };
-  // token-major A: the block resources do not depend on the slice (built once, scalar registers)
+  // the block resources do not depend on the slice (built once, scalar registers)
   __amdgpu_buffer_rsrc_t ra[LA];
-  if constexpr (!hm) {
 #pragma unroll
-    for (int li = 0; li < LA; li++) ra[li] = a_rsrc(li, 0);
-  }
+  for (int li = 0; li < LA; li++) ra[li] = a_rsrc(li, 0);
 
   // Slices travel global -> registers -> LDS through two register sets (the loop forms below
   // say which slices they hold when).
@@ -214,9 +218,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
     const uint32_t kb = (uint32_t)kt * GKB;   // byte offset of the slice inside a W row
     if (li < LA) {
       if constexpr (hm) {
-        // head-major: the slice's head moves the resource base (a slice never crosses a head)
-        const ALoad L = a_load(p.M, p.K, esz, hm_hd, NW, m0, r0, cl, li, kt);
-        dst[li] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc(li, kt), a_voff, L.soff, 0));
+        // head-major: the slice's head moves the vector offset (a slice never crosses a head);
+        // the same arithmetic as a_load
+        const uint32_t kel = kb >> 1;
+        dst[li] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra[li], a_voff + (kel >> hm_shift) * hm_head,
+                                                         (kel & hm_mask) << 1, 0));
       } else {
         dst[li] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra[li], a_voff, kb, 0));
       }
@@ -881,7 +888,9 @@ void linear_a_extent(const h3dit_linear_args &a, uint64_t *max_end, uint64_t *ba
             const ALoad L = a_load(a.M, a.K, esz, hm_hd, NW, m0, r0, cl, li, kt);
             const int64_t row = m0 + r0 + (int64_t)NW * 8 * li;
             const bool masked = (int64_t)L.voff >= L.nrec;
-            if (masked != (row >= a.M)) nbad++;
+            // a row < M is always read; a row >= M reads zeros (token-major A) or, head-major,
+            // a row of the next head inside A, masked only past the last head
+            if ((row < a.M && masked) || (!hm_hd && row >= a.M && !masked)) nbad++;
             if (!masked) {
               if ((int64_t)L.voff + L.soff + 16 > L.nrec) nbad++;
               const uint64_t end = (uint64_t)(L.base + L.voff + L.soff + 16);

@@ -11,21 +11,9 @@
 
 namespace h3 {
 
-constexpr int ROW_THREADS = 128;
-constexpr int ROW_MAXJ = 8;  // chunks per lane: d <= 128 * 8 * 8 = 8192
+constexpr int ROW_THREADS = 128;   // workgroup of the two-pass kernel for spans past 32768
+constexpr int RW_WAVES = 4;        // rows (one per wave) per workgroup of the row kernels
 
-template <int NW>
-__device__ __forceinline__ float block_sum(float v, float *red) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  if (lane == 0) red[wid] = v;
-  __syncthreads();
-  float t = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NW; w++) t += red[w];
-  __syncthreads();
-  return t;
-}
 template <int NW>
 __device__ __forceinline__ float block_max(float v, float *red) {
   v = wave_max(v);
@@ -39,77 +27,105 @@ __device__ __forceinline__ float block_max(float v, float *red) {
   return t;
 }
 
-// Gated residual and/or AdaLN of one row per workgroup.  GATE: x_out = bf16(x + g*y).
-// NORM: LN of the rounded row (two passes over registers), modulation, bf16 rounding, and
-// optionally the row's int8 code.  The LN part is the same code whether or not GATE ran in
-// this kernel, so the fused and the two-kernel sequences give the same bytes.
+// int8 codes of 8 values with scale sa, packed little-endian into two words
+__device__ __forceinline__ uint2 q8_pack8(const float *v, float sa) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q8_code(v[e], sa) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q8_code(v[4 + e], sa) << (8 * e);
+  return make_uint2(lo, hi);
+}
+
+// Gated residual and/or AdaLN, one token row per wave (four rows per workgroup): lane l holds
+// the 16-byte chunks l, l + 64, ... of its row in registers (MAXJ of them), so the row is read
+// once and every reduction is a wave reduction (no LDS, no barrier).  GATE: x_out = bf16(x +
+// g*y).  NORM: LN of the rounded row (mean, then the variance about it, both over the
+// registers), modulation, bf16 rounding, and optionally the row's int8 code.  The LN part is
+// the same code whether or not GATE ran in this kernel, so the fused and the two-kernel
+// sequences give the same bytes.
 // Modulation sets: rows [0, seg1) use gate/shift/scale as given, rows [seg1, seg2) the vectors
 // set_stride elements further, rows from seg2 on 2*set_stride further (set_stride 0: one set).
 // x_out may equal x (the residual updated in place): neither is marked __restrict__; a row's
-// loads all precede its stores and each workgroup touches only its own row.
-template <bool GATE, bool NORM, bool STATS = false>
-__global__ __launch_bounds__(ROW_THREADS) void k_row(int d, float eps, const uint16_t *x,
-                                                     const uint16_t *__restrict__ gate,
-                                                     const uint16_t *__restrict__ y, uint16_t *x_out,
-                                                     const uint16_t *__restrict__ shift,
-                                                     const uint16_t *__restrict__ scale, uint16_t *__restrict__ h,
-                                                     int8_t *__restrict__ q, float *__restrict__ s, int64_t seg1,
-                                                     int64_t seg2, int64_t set_stride) {
-  __shared__ float red[ROW_THREADS / 64];
-  const int64_t row = blockIdx.x;
+// loads all precede its stores and each wave touches only its own row.
+template <bool GATE, bool NORM, bool STATS, int MAXJ>
+__global__ __launch_bounds__(64 * RW_WAVES) void k_row(int64_t n, int d, float eps, const uint16_t *x,
+                                                       const uint16_t *__restrict__ gate,
+                                                       const uint16_t *__restrict__ y, uint16_t *x_out,
+                                                       const uint16_t *__restrict__ shift,
+                                                       const uint16_t *__restrict__ scale, uint16_t *__restrict__ h,
+                                                       int8_t *__restrict__ q, float *__restrict__ s, int64_t seg1,
+                                                       int64_t seg2, int64_t set_stride) {
+  const int64_t row = (int64_t)blockIdx.x * RW_WAVES + (threadIdx.x >> 6);
+  if (row >= n) return;   // whole waves
   const int64_t mset = (int64_t)(row >= seg1) + (int64_t)(row >= seg2);
   gate += mset * set_stride;
   shift += mset * set_stride;
   scale += mset * set_stride;
   const int nch = d >> 3;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  // the row stays packed (8 bf16 per 16-byte chunk): every value it holds is a bf16 already
+  u32x4 xv[MAXJ];
   const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + row * d);
-  float v[ROW_MAXJ][8];
 #pragma unroll
-  for (int j = 0; j < ROW_MAXJ; j++) {
-    const int c = tid + j * ROW_THREADS;
-    if (c < nch) unpack8(xr[c], v[j]);
+  for (int j = 0; j < MAXJ; j++) {
+    const int c = lane + 64 * j;
+    if (c < nch) xv[j] = xr[c];
   }
   if constexpr (GATE) {
     const u32x4 *yr = reinterpret_cast<const u32x4 *>(y + row * d);
     const u32x4 *gr = reinterpret_cast<const u32x4 *>(gate);
+    u32x4 yw[MAXJ];
+#pragma unroll
+    for (int j = 0; j < MAXJ; j++) {
+      const int c = lane + 64 * j;
+      if (c < nch) yw[j] = yr[c];
+    }
     u32x4 *xo = reinterpret_cast<u32x4 *>(x_out + row * d);
 #pragma unroll
-    for (int j = 0; j < ROW_MAXJ; j++) {
-      const int c = tid + j * ROW_THREADS;
+    for (int j = 0; j < MAXJ; j++) {
+      const int c = lane + 64 * j;
       if (c < nch) {
-        float yv[8], gv[8];
-        unpack8(yr[c], yv);
+        float a[8], yv[8], gv[8];
+        unpack8(xv[j], a);
+        unpack8(yw[j], yv);
         unpack8(gr[c], gv);
 #pragma unroll
-        for (int e = 0; e < 8; e++) v[j][e] = bf2f(f2bf(v[j][e] + gv[e] * yv[e]));
-        xo[c] = pack8(v[j]);
+        for (int e = 0; e < 8; e++) a[e] = a[e] + gv[e] * yv[e];
+        xv[j] = pack8(a);
+        xo[c] = xv[j];
       }
     }
   }
   if constexpr (NORM) {
     float part = 0.0f;
 #pragma unroll
-    for (int j = 0; j < ROW_MAXJ; j++)
-      if (tid + j * ROW_THREADS < nch)
+    for (int j = 0; j < MAXJ; j++)
+      if (lane + 64 * j < nch) {
+        float a[8];
+        unpack8(xv[j], a);
 #pragma unroll
-        for (int e = 0; e < 8; e++) part += v[j][e];
-    const float mu = block_sum<ROW_THREADS / 64>(part, red) / (float)d;
+        for (int e = 0; e < 8; e++) part += a[e];
+      }
+    const float mu = wave_sum(part) / (float)d;
     part = 0.0f;
 #pragma unroll
-    for (int j = 0; j < ROW_MAXJ; j++)
-      if (tid + j * ROW_THREADS < nch)
+    for (int j = 0; j < MAXJ; j++)
+      if (lane + 64 * j < nch) {
+        float a[8];
+        unpack8(xv[j], a);
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          const float c = v[j][e] - mu;
+          const float c = a[e] - mu;
           part += c * c;
         }
-    const float var = block_sum<ROW_THREADS / 64>(part, red) / (float)d;
+      }
+    const float var = wave_sum(part) / (float)d;
     const float rs = 1.0f / sqrtf(var + eps);
     if constexpr (STATS) {
       // statistics only (for a consumer that applies the modulation itself): s[2 row] = mean,
       // s[2 row + 1] = 1 / sqrt(var + eps), the very values the modulation below uses
-      if (tid == 0) {
+      if (lane == 0) {
         s[2 * row] = mu;
         s[2 * row + 1] = rs;
       }
@@ -119,151 +135,144 @@ __global__ __launch_bounds__(ROW_THREADS) void k_row(int d, float eps, const uin
     const u32x4 *scr = reinterpret_cast<const u32x4 *>(scale);
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < ROW_MAXJ; j++) {
-      const int c = tid + j * ROW_THREADS;
+    for (int j = 0; j < MAXJ; j++) {
+      const int c = lane + 64 * j;
       if (c < nch) {
-        float sh[8], sc[8];
+        float a[8], sh[8], sc[8];
+        unpack8(xv[j], a);
         unpack8(shr[c], sh);
         unpack8(scr[c], sc);
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          float t = (v[j][e] - mu) * rs;
+          float t = (a[e] - mu) * rs;
           t = t * (1.0f + sc[e]) + sh[e];
-          v[j][e] = bf2f(f2bf(t));
-          amax = fmaxf(amax, fabsf(v[j][e]));
+          a[e] = t;
         }
-        if (h) reinterpret_cast<u32x4 *>(h + row * d)[c] = pack8(v[j]);
+        xv[j] = pack8(a);   // the normalised row, rounded to bf16
+        if (h) reinterpret_cast<u32x4 *>(h + row * d)[c] = xv[j];
+        float r[8];
+        unpack8(xv[j], r);
+#pragma unroll
+        for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(r[e]));
       }
     }
     if (q) {
-      const float sa = block_max<ROW_THREADS / 64>(amax, red) / 127.0f;
-      if (tid == 0) s[row] = sa;
+      const float sa = wave_max(amax) / 127.0f;
+      if (lane == 0) s[row] = sa;
 #pragma unroll
-      for (int j = 0; j < ROW_MAXJ; j++) {
-        const int c = tid + j * ROW_THREADS;
+      for (int j = 0; j < MAXJ; j++) {
+        const int c = lane + 64 * j;
         if (c < nch) {
-          uint32_t lo = 0, hi = 0;
-#pragma unroll
-          for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q8_code(v[j][e], sa) << (8 * e);
-#pragma unroll
-          for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q8_code(v[j][4 + e], sa) << (8 * e);
-          reinterpret_cast<uint2 *>(q + row * d)[c] = make_uint2(lo, hi);
+          float r[8];
+          unpack8(xv[j], r);
+          reinterpret_cast<uint2 *>(q + row * d)[c] = q8_pack8(r, sa);
         }
       }
     }
   }
+}
+
+// chunks per lane of a d-wide row: the smallest instantiated count >= ceil(d / 512)
+static int row_maxj(int d) {
+  const int need = (d / 8 + 63) / 64;
+  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : need <= 10 ? 10 : 16;
+}
+
+template <bool GATE, bool NORM, bool STATS>
+static void row_dispatch(int64_t n, int d, float eps, const uint16_t *x, const uint16_t *gate, const uint16_t *y,
+                         uint16_t *x_out, const uint16_t *shift, const uint16_t *scale, uint16_t *h, int8_t *q,
+                         float *s, hipStream_t st, int64_t seg1, int64_t seg2, int64_t set_stride) {
+  const dim3 grid((unsigned)((n + RW_WAVES - 1) / RW_WAVES)), block(64 * RW_WAVES);
+#define H3_ROW(J)                                                                                                   \
+  k_row<GATE, NORM, STATS, J><<<grid, block, 0, st>>>(n, d, eps, x, gate, y, x_out, shift, scale, h, q, s, seg1, seg2, \
+                                                       set_stride)
+  switch (row_maxj(d)) {
+    case 1: H3_ROW(1); break;
+    case 2: H3_ROW(2); break;
+    case 4: H3_ROW(4); break;
+    case 8: H3_ROW(8); break;
+    case 10: H3_ROW(10); break;
+    default: H3_ROW(16); break;
+  }
+#undef H3_ROW
 }
 
 hipError_t launch_row(int64_t n, int d, float eps, const uint16_t *x, const uint16_t *gate, const uint16_t *y,
                       uint16_t *x_out, const uint16_t *shift, const uint16_t *scale, uint16_t *h, int8_t *q,
                       float *s, hipStream_t st, int64_t seg1, int64_t seg2, int64_t set_stride) {
   if (n == 0) return hipSuccess;
-  dim3 grid((unsigned)n), block(ROW_THREADS);
   if (gate && shift)
-    k_row<true, true><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s, seg1, seg2, set_stride);
+    row_dispatch<true, true, false>(n, d, eps, x, gate, y, x_out, shift, scale, h, q, s, st, seg1, seg2, set_stride);
   else if (gate)
-    k_row<true, false><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s, seg1, seg2,
-                                               set_stride);
+    row_dispatch<true, false, false>(n, d, eps, x, gate, y, x_out, shift, scale, h, q, s, st, seg1, seg2, set_stride);
   else
-    k_row<false, true><<<grid, block, 0, st>>>(d, eps, x, gate, y, x_out, shift, scale, h, q, s, seg1, seg2,
-                                               set_stride);
+    row_dispatch<false, true, false>(n, d, eps, x, gate, y, x_out, shift, scale, h, q, s, st, seg1, seg2, set_stride);
   return hipGetLastError();
 }
 
 hipError_t launch_row_stats(int64_t n, int d, float eps, const uint16_t *x, float *stats, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  k_row<false, true, true><<<(unsigned)n, ROW_THREADS, 0, st>>>(d, eps, x, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                                                 nullptr, nullptr, stats, n, n, 0);
+  row_dispatch<false, true, true>(n, d, eps, x, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, stats,
+                                  st, n, n, 0);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- int8 codes of spans
 
-// One workgroup per (row, group).  Head-major input: element (r, c) of the token-major view
-// sits at ((c / hd) * rows + r) * hd + c % hd; a chunk of 8 never crosses a head.
-__global__ __launch_bounds__(ROW_THREADS) void k_quant_rows(int64_t rows, int64_t cols, int group,
-                                                            const uint16_t *__restrict__ v, int hm_hd,
-                                                            int8_t *__restrict__ q, float *__restrict__ s) {
-  __shared__ float red[ROW_THREADS / 64];
-  const int64_t r = blockIdx.x;
-  const int g = blockIdx.y;
-  const int nch = group >> 3;
-  const int tid = threadIdx.x;
-  float val[ROW_MAXJ][8];
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < ROW_MAXJ; j++) {
-    const int c = tid + j * ROW_THREADS;
-    if (c < nch) {
-      const int64_t col = (int64_t)g * group + 8 * c;
-      int64_t off = r * cols + col;
-      if (hm_hd > 0) off = ((col / hm_hd) * rows + r) * hm_hd + col % hm_hd;
-      unpack8(*reinterpret_cast<const u32x4 *>(v + off), val[j]);
-#pragma unroll
-      for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(val[j][e]));
-    }
-  }
-  const float sa = block_max<ROW_THREADS / 64>(amax, red) / 127.0f;
-  if (tid == 0) s[r * (cols / group) + g] = sa;
-#pragma unroll
-  for (int j = 0; j < ROW_MAXJ; j++) {
-    const int c = tid + j * ROW_THREADS;
-    if (c < nch) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q8_code(val[j][e], sa) << (8 * e);
-#pragma unroll
-      for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q8_code(val[j][4 + e], sa) << (8 * e);
-      *reinterpret_cast<uint2 *>(q + r * cols + (int64_t)g * group + 8 * c) = make_uint2(lo, hi);
-    }
-  }
-}
-
-// Token-major groups of at most 64 * 8 * QW_MAXJ columns (the 1024-channel FC2-input groups):
-// one wave per (row, group), four groups per workgroup; the absmax is a wave reduction, no
-// barrier.  Same arithmetic as k_quant_rows.
-constexpr int QW_MAXJ = 4;
-__global__ __launch_bounds__(256) void k_quant_groups(int64_t rows, int64_t cols, int group,
-                                                      const uint16_t *__restrict__ v, int8_t *__restrict__ q,
-                                                      float *__restrict__ s) {
-  const int64_t r = blockIdx.x;
-  const int lane = threadIdx.x & 63;
+// Spans of up to 8192 columns (the per-token codes of a d-wide row, the 1024-channel groups of
+// the FC2 input): one wave per GPW consecutive spans of one row, lane l holding chunks l, l + 64,
+// ... of each span (CPL per span), so that a lane has several 16-byte loads in flight and every
+// absmax is a wave reduction.  Head-major input (hm_hd > 0): element (r, c) of the token-major
+// view sits at ((c / hd) * rows + r) * hd + c % hd; a chunk of 8 never crosses a head.
+template <int CPL, int GPW>
+__global__ __launch_bounds__(64 * RW_WAVES) void k_quant_span(int64_t rows, int64_t cols, int group,
+                                                              const uint16_t *__restrict__ v, int hm_hd,
+                                                              int8_t *__restrict__ q, float *__restrict__ s) {
   const int64_t ng = cols / group;
-  const int64_t g = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (g >= ng) return;
+  const int64_t r = blockIdx.x;
+  const int64_t g0 = ((int64_t)blockIdx.y * RW_WAVES + (threadIdx.x >> 6)) * GPW;
+  if (g0 >= ng) return;   // whole waves
+  const int lane = threadIdx.x & 63;
   const int nch = group >> 3;
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(v + r * cols + g * group);
-  float val[QW_MAXJ][8];
-  float amax = 0.0f;
+  u32x4 raw[GPW][CPL];
 #pragma unroll
-  for (int j = 0; j < QW_MAXJ; j++) {
-    const int c = lane + 64 * j;
-    if (c < nch) {
-      unpack8(src[c], val[j]);
+  for (int k = 0; k < GPW; k++)
 #pragma unroll
-      for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(val[j][e]));
+    for (int j = 0; j < CPL; j++) {
+      const int c = lane + 64 * j;
+      if (g0 + k < ng && c < nch) {
+        const int64_t col = (g0 + k) * group + 8 * c;
+        int64_t off = r * cols + col;
+        if (hm_hd > 0) off = ((col / hm_hd) * rows + r) * hm_hd + col % hm_hd;
+        raw[k][j] = *reinterpret_cast<const u32x4 *>(v + off);
+      }
     }
-  }
-  const float sa = wave_max(amax) / 127.0f;
-  if (lane == 0) s[r * ng + g] = sa;
-  uint2 *dst = reinterpret_cast<uint2 *>(q + r * cols + g * group);
 #pragma unroll
-  for (int j = 0; j < QW_MAXJ; j++) {
-    const int c = lane + 64 * j;
-    if (c < nch) {
-      uint32_t lo = 0, hi = 0;
+  for (int k = 0; k < GPW; k++) {
+    if (g0 + k >= ng) break;   // wave-uniform
+    float val[CPL][8];
+    float amax = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q8_code(val[j][e], sa) << (8 * e);
+    for (int j = 0; j < CPL; j++)
+      if (lane + 64 * j < nch) {
+        unpack8(raw[k][j], val[j]);
 #pragma unroll
-      for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q8_code(val[j][4 + e], sa) << (8 * e);
-      dst[c] = make_uint2(lo, hi);
+        for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(val[j][e]));
+      }
+    const float sa = wave_max(amax) / 127.0f;
+    if (lane == 0) s[r * ng + g0 + k] = sa;
+    uint2 *dst = reinterpret_cast<uint2 *>(q + r * cols + (g0 + k) * group);
+#pragma unroll
+    for (int j = 0; j < CPL; j++) {
+      const int c = lane + 64 * j;
+      if (c < nch) dst[c] = q8_pack8(val[j], sa);
     }
   }
 }
 
 // Token-major spans of 8193..32768 columns (a whole FC2-input row of 20480 channels, the
 // 20480-wide weight rows): one 256-lane workgroup per span, values in registers, one pass
-// over global memory.  Same arithmetic as k_quant_rows.
+// over global memory.  Same arithmetic as k_quant_span.
 constexpr int QWIDE_THREADS = 256;
 constexpr int QWIDE_MAXJ = 16;
 __global__ __launch_bounds__(QWIDE_THREADS) void k_quant_wide(int64_t cols, int group, const uint16_t *__restrict__ v,
@@ -291,14 +300,7 @@ __global__ __launch_bounds__(QWIDE_THREADS) void k_quant_wide(int64_t cols, int 
 #pragma unroll
   for (int j = 0; j < QWIDE_MAXJ; j++) {
     const int c = tid + j * QWIDE_THREADS;
-    if (c < nch) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q8_code(val[j][e], sa) << (8 * e);
-#pragma unroll
-      for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q8_code(val[j][4 + e], sa) << (8 * e);
-      dst[c] = make_uint2(lo, hi);
-    }
+    if (c < nch) dst[c] = q8_pack8(val[j], sa);
   }
 }
 
@@ -324,31 +326,33 @@ __global__ __launch_bounds__(ROW_THREADS) void k_quant_long(int64_t cols, int64_
   for (int64_t c = threadIdx.x; c < nch; c += ROW_THREADS) {
     float f[8];
     unpack8(src[c], f);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q8_code(f[e], sa) << (8 * e);
-#pragma unroll
-    for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q8_code(f[4 + e], sa) << (8 * e);
-    dst[c] = make_uint2(lo, hi);
+    dst[c] = q8_pack8(f, sa);
   }
 }
 
 hipError_t launch_quant_rows(int64_t rows, int64_t cols, int64_t group, const uint16_t *v, int hm_hd, int8_t *q,
                              float *s, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  dim3 grid((unsigned)rows, (unsigned)(cols / group)), block(ROW_THREADS);
-  if (group > (int64_t)ROW_THREADS * ROW_MAXJ * 8) {
+  const int64_t ng = cols / group;
+  if (group > 8192) {
     if (hm_hd > 0) return hipErrorInvalidValue;
+    dim3 grid((unsigned)rows, (unsigned)ng);
     if (group <= (int64_t)QWIDE_THREADS * QWIDE_MAXJ * 8)
       k_quant_wide<<<grid, QWIDE_THREADS, 0, st>>>(cols, (int)group, v, q, s);
     else
-      k_quant_long<<<grid, block, 0, st>>>(cols, group, v, q, s);
-  } else if (hm_hd == 0 && group <= 64 * 8 * QW_MAXJ && cols / group >= 4) {
-    dim3 g4((unsigned)rows, (unsigned)((cols / group + 3) / 4));
-    k_quant_groups<<<g4, 256, 0, st>>>(rows, cols, (int)group, v, q, s);
-  } else {
-    k_quant_rows<<<grid, block, 0, st>>>(rows, cols, (int)group, v, hm_hd, q, s);
+      k_quant_long<<<grid, ROW_THREADS, 0, st>>>(cols, group, v, q, s);
+    return hipGetLastError();
   }
+  // chunks per lane and span, and spans per wave (at least about eight 16-byte loads per lane)
+  const int need = (int)((group / 8 + 63) / 64);
+#define H3_QS(CPL, GPW)                                                                                           k_quant_span<CPL, GPW><<<dim3((unsigned)rows, (unsigned)((ng + RW_WAVES * GPW - 1) / (RW_WAVES * GPW))),                                64 * RW_WAVES, 0, st>>>(rows, cols, (int)group, v, hm_hd, q, s)
+  if (need <= 1) H3_QS(1, 8);
+  else if (need <= 2) H3_QS(2, 4);
+  else if (need <= 4) H3_QS(4, 2);
+  else if (need <= 8) H3_QS(8, 1);
+  else if (need <= 10) H3_QS(10, 1);
+  else H3_QS(16, 1);
+#undef H3_QS
   return hipGetLastError();
 }
 

