@@ -32,7 +32,7 @@ EXPORTS = ("h3dit_quantize_weights", "h3dit_block_fwd", "h3dit_stack_fwd", "h3di
            "h3dit_row_gate_adaln", "h3dit_quantize_rows", "h3dit_linear", "h3dit_rope_split", "h3dit_gelu",
            "h3dit_attention", "h3dit_token_pair", "h3dit_token_restore", "h3dit_linear_workspace",
            "h3dit_final_head", "h3dit_stack_fwd_streamed", "h3dit_denoise_plan", "h3dit_velocity_step",
-           "h3dit_denoise_fwd", "h3dit_linear_a_extent")
+           "h3dit_denoise_fwd", "h3dit_linear_a_extent", "h3dit_final_head_noalloc")
 
 
 class H3Error(RuntimeError):
@@ -107,6 +107,7 @@ _lib.h3dit_linear.argtypes = [_P, _P]
 _lib.h3dit_linear_workspace.argtypes = [_P, _P]
 _lib.h3dit_linear_a_extent.argtypes = [_P, _P, _P]
 _lib.h3dit_final_head.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.h3dit_final_head_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P]
 _lib.h3dit_denoise_plan.argtypes = [_P, C.c_int32, _P]
 _lib.h3dit_velocity_step.argtypes = [C.c_int64, C.c_float, _P, _P, _P]
 _lib.h3dit_denoise_fwd.argtypes = [_P, _P, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_uint32, _P,
@@ -506,6 +507,25 @@ def final_head(w, x, video=None, audio=None, stream=None):
     size = C.c_size_t(ws.numel())
     _check("h3dit_final_head", _lib.h3dit_final_head(d, l, refs[0], refs[1], _ptr(x), _ptr(outs[0]), _ptr(outs[1]),
                                                      _ptr(ws), C.byref(size), _stream(stream)))
+    return tuple(outs)
+
+
+def final_head_noalloc(w, x, video=None, audio=None, outs=None, stream=None):
+    """h3dit_final_head_noalloc: as final_head, with the row statistics in the library's static
+    device array instead of a workspace.  outs: (out_video, out_audio) to write into, or None
+    to allocate them here."""
+    import torch
+    n_video = w.n_tokens - w.n_text - w.n_audio
+    parts = []
+    if outs is None:
+        outs = tuple(None if p is None else torch.empty((n, p[1].shape[0]), dtype=torch.bfloat16, device=x.device)
+                     for p, n in ((video, n_video), (audio, w.n_audio)))
+    for part in (video, audio):
+        parts.append(None if part is None else HeadPart(_ptr(part[0]), _ptr(part[1]), part[1].shape[0]))
+    refs = [C.byref(p) if p is not None else None for p in parts]
+    _check("h3dit_final_head_noalloc",
+           _lib.h3dit_final_head_noalloc(C.byref(dims_of(w)), C.byref(layout_of(w)), refs[0], refs[1], _ptr(x),
+                                         _ptr(outs[0]), _ptr(outs[1]), _stream(stream)))
     return tuple(outs)
 
 

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "common.hpp"
@@ -649,6 +650,29 @@ int final_head_launch(const h3dit_dims *dims, const h3dit_layout *layout, const 
   return H3DIT_OK;
 }
 
+// Scratch of the allocation-free final head: the row statistics of one part, in a file-scope
+// device array (one copy per device, held until the process ends).  In host code `scratch`
+// names a host-side stand-in, never the device memory: its device address is taken once per
+// device with hipGetSymbolAddress and kept in g_scratch.
+constexpr size_t kNoallocScratchBytes = (size_t)512 << 10;   // 65536 rows x 8 bytes
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch[64];
+
+int scratch_ptr(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return H3DIT_EHIP;
+  if (dev < 0 || dev >= 64) return H3DIT_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return H3DIT_EHIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return H3DIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -674,6 +698,23 @@ int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layout, const h
   }
   if ((rc = check_device())) return rc;
   return final_head_launch(dims, layout, video, audio, x, out_video, out_audio, reinterpret_cast<float *>(workspace),
+                           (hipStream_t)stream);
+}
+
+int h3dit_final_head_noalloc(const h3dit_dims *dims, const h3dit_layout *layout, const h3dit_head_part *video,
+                             const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video,
+                             uint16_t *out_audio, void *stream) {
+  size_t total = 0;
+  int rc = final_head_impl(dims, layout, video, audio, nullptr, nullptr, nullptr, nullptr, &total, nullptr);
+  if (rc < 0) return rc;
+  if (total > kNoallocScratchBytes) return H3DIT_EWORKSPACE;
+  if ((rc = check_device())) return rc;
+  void *sp = nullptr;
+  if ((rc = scratch_ptr(&sp))) return rc;
+  rc = final_head_impl(dims, layout, video, audio, x, out_video, out_audio, reinterpret_cast<float *>(sp), &total,
+                       (hipStream_t)stream);
+  if (rc) return rc;
+  return final_head_launch(dims, layout, video, audio, x, out_video, out_audio, reinterpret_cast<float *>(sp),
                            (hipStream_t)stream);
 }
 

@@ -221,6 +221,20 @@ H3DIT_API int h3dit_final_head(const h3dit_dims *dims, const h3dit_layout *layou
                                const h3dit_head_part *audio, const uint16_t *x, uint16_t *out_video,
                                uint16_t *out_audio, void *workspace, size_t *workspace_bytes, void *stream);
 
+/* h3dit_final_head without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the row
+ * statistics go to a static device array of 512 KiB that the library holds on each device it
+ * runs on until the process ends, so each part may have at most 65536 rows (n_video and
+ * n_audio); larger parts return H3DIT_EWORKSPACE before any launch.  The caller still passes
+ * x and the outputs.  Nothing in the array needs clearing (every row's statistics are written
+ * before they are read).  All calls on one device share the array: calls that overlap on one
+ * device (on different streams, or from different host threads without ordering) race and
+ * must not be made.  Other arguments, results and errors as h3dit_final_head; the output is
+ * byte-identical to it. */
+H3DIT_API int h3dit_final_head_noalloc(const h3dit_dims *dims, const h3dit_layout *layout,
+                                       const h3dit_head_part *video, const h3dit_head_part *audio, const uint16_t *x,
+                                       uint16_t *out_video, uint16_t *out_audio, void *stream);
+
 /* Denoising schedule ([DD] "速度/质量预设矩阵": denoising steps, whole-denoiser velocity reuse,
  * active blocks and core-residual reuse, with reuse and core reuse mutually exclusive;
  * [DD] "Token 缩减": the bypass comes back before block 40 in the first ten noise evaluations
