@@ -92,12 +92,34 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// int8 code of v with scale s (s > 0): round-half-even(v / s), clamped to +-127
-__device__ __forceinline__ int8_t q8_code(float v, float s) {
-  if (s == 0.0f) return 0;
-  float c = rintf(v / s);
-  c = fminf(fmaxf(c, -127.0f), 127.0f);
-  return (int8_t)(int)c;
+// int8 codes of 8 values of one span with scale s: round-half-even(v / s) of the correctly
+// rounded quotient, clamped to +-127, 0 when s == 0; packed little-endian into two words.
+// inv = 1/s (correctly rounded, once per span).  The quotient is first approximated by
+// t = v * inv: with |v / s| <= 127 (s is the span's absmax / 127), t and the correctly rounded
+// v / s differ by at most |v/s| (2^-23 + 2^-24) < 2.3e-5, so they round to the same integer
+// unless a half-integer lies within that distance of t.  Values within 4e-5 of a half-integer
+// (and non-finite t) take the true division, for the whole wave at once (a uniform branch
+// taken for a few percent of the 8-value chunks), so the codes are those of rintf(v / s).
+__device__ __forceinline__ uint2 q8_pack8(const float *v, float s, float inv) {
+  if (s == 0.0f) return make_uint2(0u, 0u);   // the span is all zeros
+  float c[8];
+  bool exact = false;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const float t = v[e] * inv;
+    c[e] = rintf(t);
+    exact |= !(fabsf(t) < 128.0f) || fabsf(fabsf(t - c[e]) - 0.5f) <= 4e-5f;
+  }
+  if (__any(exact)) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) c[e] = rintf(v[e] / s);
+  }
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)(int)fminf(fmaxf(c[e], -127.0f), 127.0f) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)(int)fminf(fmaxf(c[4 + e], -127.0f), 127.0f) << (8 * e);
+  return make_uint2(lo, hi);
 }
 
 }  // namespace h3

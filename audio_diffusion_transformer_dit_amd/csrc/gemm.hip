@@ -29,6 +29,9 @@
 namespace h3 {
 
 constexpr int GKB = 128;        // bytes of K per slice and row
+// s_waitcnt immediate that waits for lgkmcnt == 0 only (gfx9 encoding: vmcnt bits 3:0 and 15:14
+// at their maximum, expcnt bits 6:4 at 7, lgkmcnt bits 11:8 at 0)
+constexpr int kLgkmZero = 0xC07F;
 
 struct GemmP {
   const uint8_t *a;
@@ -316,6 +319,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
     for (int li = 0; li < NL; li++) load_one(stage_reg[1], kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1, li);
     __syncthreads();
     read_step(smem + (kt0 & 1) * C::STAGE, 0, fa[0], fb[0]);
+    // No LDS or scalar-memory operation is left pending where the loop is entered or repeated
+    // (the step-0 fragments of the next slice are read a whole K step earlier), which lets the
+    // wait-count insertion see that the first MFMAs of an iteration need no wait, instead of
+    // waiting for every LDS read issued so far at the loop header.
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);
     auto iter1 = [&](int kt, const u32x4 *cur, u32x4 *nxt, auto steady) {
       constexpr bool STEADY = decltype(steady)::value;
       const bool more = STEADY || kt + 1 < kt1;
@@ -356,6 +364,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
             }
           }
       }
+      __builtin_amdgcn_s_waitcnt(kLgkmZero);   // the next slice's step-0 reads, issued 16 MFMAs ago
     };
     using Steady = std::integral_constant<bool, true>;
     using Tail = std::integral_constant<bool, false>;

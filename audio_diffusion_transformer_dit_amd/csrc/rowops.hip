@@ -27,16 +27,6 @@ __device__ __forceinline__ float block_max(float v, float *red) {
   return t;
 }
 
-// int8 codes of 8 values with scale sa, packed little-endian into two words
-__device__ __forceinline__ uint2 q8_pack8(const float *v, float sa) {
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q8_code(v[e], sa) << (8 * e);
-#pragma unroll
-  for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q8_code(v[4 + e], sa) << (8 * e);
-  return make_uint2(lo, hi);
-}
-
 // Gated residual and/or AdaLN, one token row per wave (four rows per workgroup): lane l holds
 // the 16-byte chunks l, l + 64, ... of its row in registers (MAXJ of them), so the row is read
 // once and every reduction is a wave reduction (no LDS, no barrier).  GATE: x_out = bf16(x +
@@ -157,7 +147,7 @@ __global__ __launch_bounds__(64 * RW_WAVES) void k_row(int64_t n, int d, float e
       }
     }
     if (q) {
-      const float sa = wave_max(amax) / 127.0f;
+      const float sa = wave_max(amax) / 127.0f, inv = 1.0f / sa;
       if (lane == 0) s[row] = sa;
 #pragma unroll
       for (int j = 0; j < MAXJ; j++) {
@@ -165,7 +155,7 @@ __global__ __launch_bounds__(64 * RW_WAVES) void k_row(int64_t n, int d, float e
         if (c < nch) {
           float r[8];
           unpack8(xv[j], r);
-          reinterpret_cast<uint2 *>(q + row * d)[c] = q8_pack8(r, sa);
+          reinterpret_cast<uint2 *>(q + row * d)[c] = q8_pack8(r, sa, inv);
         }
       }
     }
@@ -259,13 +249,13 @@ __global__ __launch_bounds__(64 * RW_WAVES) void k_quant_span(int64_t rows, int6
 #pragma unroll
         for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(val[j][e]));
       }
-    const float sa = wave_max(amax) / 127.0f;
+    const float sa = wave_max(amax) / 127.0f, inv = 1.0f / sa;
     if (lane == 0) s[r * ng + g0 + k] = sa;
     uint2 *dst = reinterpret_cast<uint2 *>(q + r * cols + (g0 + k) * group);
 #pragma unroll
     for (int j = 0; j < CPL; j++) {
       const int c = lane + 64 * j;
-      if (c < nch) dst[c] = q8_pack8(val[j], sa);
+      if (c < nch) dst[c] = q8_pack8(val[j], sa, inv);
     }
   }
 }
@@ -294,13 +284,13 @@ __global__ __launch_bounds__(QWIDE_THREADS) void k_quant_wide(int64_t cols, int 
       for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(val[j][e]));
     }
   }
-  const float sa = block_max<QWIDE_THREADS / 64>(amax, red) / 127.0f;
+  const float sa = block_max<QWIDE_THREADS / 64>(amax, red) / 127.0f, inv = 1.0f / sa;
   if (tid == 0) s[r * (cols / group) + g] = sa;
   uint2 *dst = reinterpret_cast<uint2 *>(q + r * cols + g * group);
 #pragma unroll
   for (int j = 0; j < QWIDE_MAXJ; j++) {
     const int c = tid + j * QWIDE_THREADS;
-    if (c < nch) dst[c] = q8_pack8(val[j], sa);
+    if (c < nch) dst[c] = q8_pack8(val[j], sa, inv);
   }
 }
 
@@ -320,13 +310,13 @@ __global__ __launch_bounds__(ROW_THREADS) void k_quant_long(int64_t cols, int64_
 #pragma unroll
     for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(f[e]));
   }
-  const float sa = block_max<ROW_THREADS / 64>(amax, red) / 127.0f;
+  const float sa = block_max<ROW_THREADS / 64>(amax, red) / 127.0f, inv = 1.0f / sa;
   if (threadIdx.x == 0) s[r * (cols / group) + g] = sa;
   uint2 *dst = reinterpret_cast<uint2 *>(q + r * cols + g * group);
   for (int64_t c = threadIdx.x; c < nch; c += ROW_THREADS) {
     float f[8];
     unpack8(src[c], f);
-    dst[c] = q8_pack8(f, sa);
+    dst[c] = q8_pack8(f, sa, inv);
   }
 }
 

@@ -130,6 +130,47 @@ def test_quantize_rows(rows, cols, group, hm):
     assert_bitexact(cpu(s), s_ref)
 
 
+def near_tie_rows(rows, cols, seed):
+    """bf16 rows whose values sit on and next to the half-integer points of their own code
+    scale: each row draws an absmax, and its values are bf16 roundings of (k + 1/2) * s nudged
+    by -3..3 bf16 steps (k random), where a quotient approximated through 1/s and the correctly
+    rounded quotient could round to different integers."""
+    g = torch.Generator().manual_seed(seed)
+    amax = torch.exp(torch.empty(rows, 1).uniform_(-6.0, 6.0, generator=g)).to(torch.bfloat16).to(torch.float64)
+    # every fourth row: absmax 127 * 2^j, a scale of exactly 2^j, so (k + 1/2) * s is an exact tie
+    amax[::4] = 127.0 * torch.exp2(torch.randint(-4, 5, (len(amax[::4]), 1), generator=g).to(torch.float64))
+    s = (amax.to(torch.float32) / 127.0).to(torch.float64)
+    k = torch.randint(-127, 127, (rows, cols), generator=g).to(torch.float64)
+    v = ((k + 0.5) * s).to(torch.bfloat16)
+    nudge = torch.randint(-3, 4, (rows, cols), generator=g, dtype=torch.int16)
+    v = (v.view(torch.int16) + nudge).view(torch.bfloat16)
+    v = torch.where(v.to(torch.float64).abs() > amax, amax.to(torch.bfloat16).expand(rows, cols), v)
+    v[:, 0] = amax[:, 0].to(torch.bfloat16)                 # the absmax itself: code 127
+    return v.contiguous()
+
+
+@pytest.mark.parametrize("rows,cols,group", [(512, 1024, 1024), (64, 20480, 1024), (96, 5120, 5120), (8, 20480, 20480)])
+def test_quantize_rows_near_ties_bitexact(rows, cols, group):
+    """Codes of values on and next to half-integer quotients (ties go to even) equal the oracle's
+    rintf(v / s) bit for bit, in every code kernel (1024 groups, whole 5120 and 20480 rows)."""
+    v = near_tie_rows(rows, cols, rows + cols)
+    q, s = h3.quantize_rows(to_dev(v), rows, cols, group)
+    q_ref, s_ref = oracle.q8_rows(v, group)
+    assert_bitexact(cpu(s), s_ref)
+    assert_bitexact(cpu(q), q_ref)
+    # and through the row kernel's fused codes (AdaLN with shift = value, scale = -1: h == shift)
+    if cols == 5120:
+        for r in range(0, rows, 32):
+            zero = torch.zeros(cols, dtype=torch.bfloat16)
+            minus = torch.full((cols,), -1.0, dtype=torch.bfloat16)
+            x = bf_randn((1, cols), r + 1)
+            qg = torch.empty((1, cols), dtype=torch.int8, device="cuda")
+            sg = torch.empty(1, dtype=torch.float32, device="cuda")
+            h3.row_gate_adaln(to_dev(x), shift=to_dev(v[r].contiguous()), scale=to_dev(minus), q=qg, s=sg)
+            qr, sr = oracle.q8_rows(v[r:r + 1].contiguous())
+            assert_bitexact(cpu(qg), qr, "row kernel codes")
+
+
 def test_quantize_weights():
     w = bf_randn((384, 1024), 11, 0.02)
     q, s = h3.quantize_weights(to_dev(w))
