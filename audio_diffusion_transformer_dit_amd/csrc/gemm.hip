@@ -29,6 +29,10 @@
 namespace h3 {
 
 constexpr int GKB = 128;        // bytes of K per slice and row
+// Tile of the grouped int8 FC2 (two accumulator sets per lane: int32 within a group, fp32
+// across groups): G_BM x G_BN, a G_WGM x G_WGN grid of waves of 64 x 64, two workgroups per
+// CU.  (256 x 128 tiles of eight such waves, one workgroup per CU, measured the same.)
+constexpr int G_BM = 128, G_BN = 128, G_WGM = G_BM / 64, G_WGN = 2;
 // s_waitcnt immediate that waits for lgkmcnt == 0 only (gfx9 encoding: vmcnt bits 3:0 and 15:14
 // at their maximum, expcnt bits 6:4 at 7, lgkmcnt bits 11:8 at 0)
 constexpr int kLgkmZero = 0xC07F;
@@ -817,7 +821,7 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
   pl.part_bytes = 0;
   pl.bn = 128;
   pl.n_dp = (int)(tm * (a.N / 128));
-  if (grouped) pl.n_dp = (int)((a.M + 127) / 128 * (a.N / 128));   // 128 x 128 tiles
+  if (grouped) pl.n_dp = (int)((a.M + G_BM - 1) / G_BM * (a.N / G_BN));
   if (!wide) return pl;
   const int64_t tiles = tm * (a.N / 256), full = tiles / kCUs, rem = tiles % kCUs;
   const double t_tile_us = (double)KT * 128 * 0.0277 / 2;   // one 256 x 256 tile over the whole K
@@ -853,7 +857,7 @@ static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st)
   if constexpr (GROUPED) {
     // two accumulator sets (int32 per group, fp32 across groups) per lane: 128 x 128 tiles of
     // 4 waves of 64 x 64, two workgroups per CU (1280 tiles at 4096 x 5120: whole rounds)
-    return run_gemm<128, 128, 2, 2, INT8, OUT, GROUPED, false>(p, pl, st);
+    return run_gemm<G_BM, G_BN, G_WGM, G_WGN, INT8, OUT, GROUPED, false>(p, pl, st);
   } else {
     // bf16: four waves of 128 x 128; int8: eight waves of 128 x 64 (measured faster for int8)
     if (pl.bn == 256) {
@@ -877,7 +881,7 @@ void linear_a_extent(const h3dit_linear_args &a, uint64_t *max_end, uint64_t *ba
   const int esz = i8 ? 1 : 2;
   int BM, NW;
   if (grouped) {
-    BM = 128; NW = 4;
+    BM = G_BM; NW = G_WGM * G_WGN;
   } else if (pl.bn == 256) {
     BM = 256; NW = i8 ? 8 : 4;
   } else {
@@ -907,11 +911,11 @@ void linear_a_extent(const h3dit_linear_args &a, uint64_t *max_end, uint64_t *ba
             }
           }
   if (grouped) {
-    // the group scales [M][K / a_group] fp32 of the grouped FC2 (4 waves of 64 x 64, 2 x 2)
+    // the group scales [M][K / a_group] fp32 of the grouped FC2 (waves of 64 x 64, G_WGM rows of them)
     const int ng = (int)(a.K / a.a_group);
     uint64_t stop = 0;
     for (int64_t tm = 0; tm < tiles_m; tm++)
-      for (int wm = 0; wm < 2; wm++)
+      for (int wm = 0; wm < G_WGM; wm++)
         for (int hsel = 0; hsel < 2; hsel++)
           for (int i = 0; i < 2; i++)
             for (int q4 = 0; q4 < 4; q4++)

@@ -51,6 +51,11 @@ def parse():
                     help="also time 20-step denoising runs (h3dit_denoise_fwd) at the pages' slow, default and "
                          "token-reduction presets (kept out of the default run: its reduced-sequence launches share "
                          "kernel names with the full-size ones and would mix into the profiled per-kernel averages)")
+    ap.add_argument("--precision", choices=["bf16", "int8", "int8_mlp", "int8_attn"], default=None,
+                    help="precision of the main leg (default: the workload's)")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="time the main stack leg only (no per-kernel loops, no other legs, no CPU leg): a "
+                         "profiled run of it traces the kernels as they run inside the stack")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only-kernels: also run one plain device copy of this many bytes, the reference "
                          "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -368,7 +373,12 @@ def main():
     if args.fc2_group:
         w = w.replace(fc2_group=args.fc2_group)
     seed = synth.seed_for(args.workload)
-    int8_main = w.precision == "int8"
+    main_prec = args.precision or w.precision
+    int8_main = main_prec != "bf16"
+    if main_prec in ("int8_mlp", "int8_attn") and not args.stack_only:
+        print("--precision int8_mlp / int8_attn time the stack only: add --stack-only (the default run times "
+              "those paths as extra legs)", file=sys.stderr)
+        sys.exit(2)
     red = (w.reduce_after, w.restore_before) if w.reduce_after >= 0 else None
     N, d, f = w.n_tokens, w.hidden, w.mlp
     print(f"[bench] workload {w.name}: {w.blocks} blocks, N={N}, d={d}, f={f}, {w.precision}", file=sys.stderr,
@@ -392,11 +402,16 @@ def main():
         print(json.dumps(out))
         return
 
-    blocks = make_blocks(w, w.blocks, seed, dev, int8_main)
+    blocks = make_blocks(w, w.blocks, seed, dev, int8_main, mlp_only=main_prec == "int8_mlp",
+                         attn_only=main_prec == "int8_attn")
     torch.cuda.synchronize()
     print("[bench] weights resident; timing the stack", file=sys.stderr, flush=True)
     step_stats = {}
     ms, wall, ws_bytes = time_stack(w, blocks, x, args.steps, args.warmup, red, step_stats)
+    if args.stack_only:
+        print(json.dumps({"workload": w.name, "precision": main_prec, "ms_per_step": round(ms, 3), **step_stats}),
+              flush=True)
+        return
     if red:
         nr = w.video_t * w.video_h * (w.video_w // 2 + w.video_w % 2) + w.n_text + w.n_audio
         full = red[0] + 1 + max(0, w.blocks - red[1])
@@ -409,7 +424,7 @@ def main():
     kern = kernel_breakdown(w, blocks[0], x, args.kernel_iters, int8_main)
     mm = {k: v for k, v in kern.items() if "flop" in v}
     dom = max(mm, key=lambda k: mm[k]["ms"])
-    prec = "int8" if int8_main else "bf16"
+    prec = main_prec
     # attention multiplies bf16 on both paths; the int8 path's projections use the int8 peak
     kprec = "int8" if (int8_main and dom != "attention") else "bf16"
     roof = {"bound": "mfma", "kernel": dom, "achieved": mm[dom]["tflops"], "peak": PEAK[kprec],

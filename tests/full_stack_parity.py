@@ -12,11 +12,17 @@ two phases because the oracle needs about half an hour of 16 CPU cores for 146 T
 
 Both phases draw the same seeded inputs and weights (synth is bit-exact across devices).  The
 oracle runs the blocks one at a time, which equals its fused stack bit for bit (pinned in
-test_oracle_pins.py), printing progress after each block.  The comparison is the one the
-stack tests use (the residual in the max norm, the stack's total update on average), with the
-bar raised, where it is larger, to 1.5x the divergence that a one-step change of a single input
-element causes on the GPU over the same blocks: GPU and oracle add in different orders, and
-after tens of blocks such rounding-sized differences have grown as far as that change does."""
+test_oracle_pins.py), printing progress after each block.  The comparison: the residual in the
+max norm and the stack's total update on average, against the single-stage bars (2e-2, 5%)
+raised, where it is larger, to 1.5x the divergence that a one-step change of a single input
+element causes over the same blocks.  This is the chain argument of the collected six-block
+production-width test (test_gpu_fullsize.test_stack_production_width_matches_oracle): GPU and
+oracle add in different orders, every stage differs by rounding-sized amounts, and down a chain
+such differences grow as the chain amplifies a rounding-sized change of its input.  That test
+measures the amplification with the oracle itself; at 50 blocks a second oracle chain would
+take another half hour, so this script measures it on the GPU (the GPU and the oracle compute
+the same chain, so their amplification of a one-step input change is the same to within its
+own rounding noise)."""
 import os
 import sys
 import time
