@@ -14,6 +14,10 @@
 // K and V^T tiles go global -> LDS with buffer_load ... lds, double-buffered; the 16-byte
 // chunks of a row are XOR-swizzled so that the 16 lanes of an LDS read phase (16 rows, one
 // chunk) cover all 64 banks: c ^ (r & 15) for 256-byte rows, c ^ ((r >> 1) & 7) for 128.
+// The key blocks are software-pipelined: the score MFMAs of block j+1 are interleaved with the
+// exponentials of block j, and block j's O^T MFMAs with its row sums and block j+1's max, so
+// that the matrix pipe and the VALU work on different blocks.  Values past the last key are
+// cleared in the V^T fragments of the last block (the rows' padding may hold anything).
 #include "common.hpp"
 
 namespace h3 {
@@ -32,58 +36,78 @@ struct AttCfg {
   static constexpr int STAGE = KBYTES + VBYTES;
 };
 
+// v_max3_f32 without the NaN canonicalisation of the inputs that fmaxf brings (scores are
+// finite or -inf)
+__device__ __forceinline__ float att_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_VALU = 0x2, SG_MFMA = 0x8, SG_DS_READ = 0x100;
+
 // LDS slot of 16-byte chunk c in row r of a tile whose rows are `chunks` chunks long
 __device__ __forceinline__ int att_slot(int c, int r, int chunks) {
   return chunks >= 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
+// Global -> LDS copies of one key block, 16 bytes per lane and instruction.  The buffer
+// resource starts at the block (its range ends with the tensor, so rows past the end read as
+// 0); the lane's offset inside the block is the same for every instruction of a wave up to a
+// uniform stride, since the swizzle depends only on row bits that the stride leaves alone.
+//
+// K: AKV rows of HD*2 bytes (HD/8 chunks), 1024/KROW rows per instruction.  Lane offset
+// of the wave's first row (wid) and of its own chunk:
 template <int HD>
-__device__ __forceinline__ void att_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint8_t *st,
-                                         int64_t kbase_row, int64_t vbase_row, int ldv, int kb) {
+__device__ __forceinline__ uint32_t att_lane_k(int wid, int lane) {
   using C = AttCfg<HD>;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  // K: rows of HD*2 bytes = HD/8 chunks; one instruction fills 1 KiB = 1024/KROW rows
-  constexpr int KCH = HD / 8;
+  constexpr int KCH = HD / 8, KRPI = 1024 / C::KROW;
+  const int row = wid * KRPI + lane / KCH;
+  return (uint32_t)(row * C::KROW + (att_slot(lane % KCH, row, KCH) << 4));
+}
+template <int HD>
+__device__ __forceinline__ void att_load_k(const uint16_t *k, uint32_t k_bytes, uint8_t *dst, int64_t first_row,
+                                           int wid, uint32_t lane_off) {
+  using C = AttCfg<HD>;
   constexpr int KRPI = 1024 / C::KROW;
-  {
-    const int rl = lane / KCH, slot = lane % KCH;
+  const int64_t at = first_row * C::KROW;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(k + first_row * HD, k_bytes - (uint32_t)at);
 #pragma unroll
-    for (int i = 0; i < AKV / (KRPI * ANW); i++) {
-      const int rb = i * ANW + wid;
-      const int row = rb * KRPI + rl;
-      const int chunk = att_slot(slot, row, KCH);
-      const uint32_t off = (uint32_t)(((kbase_row + (int64_t)kb * AKV + row) * HD + chunk * 8) * 2);
-      buffer_load_lds16(rk, (lds_void *)(st + rb * 1024), off);
-    }
-  }
-  // V^T: HD rows of 128 bytes (8 chunks), 8 rows per instruction
-  {
-    const int rl = lane >> 3, slot = lane & 7;
+  for (int i = 0; i < AKV / (KRPI * ANW); i++)
+    buffer_load_lds16(rs, (lds_void *)(dst + (i * ANW + wid) * 1024), lane_off + (uint32_t)(i * ANW * 1024));
+}
+// V^T: HD rows of AKV keys = 128 bytes (8 chunks), 8 rows per instruction; rows are ldv
+// elements apart
+__device__ __forceinline__ uint32_t att_lane_v(int wid, int lane, int ldv) {
+  const int row = wid * 8 + (lane >> 3);
+  return (uint32_t)row * (uint32_t)ldv * 2u + (uint32_t)(att_slot(lane & 7, row, 8) << 4);
+}
+template <int HD>
+__device__ __forceinline__ void att_load_v(const uint16_t *vt, uint32_t v_bytes, uint8_t *dst, int64_t first_elem,
+                                           int ldv, int wid, uint32_t lane_off) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(vt + first_elem, v_bytes - (uint32_t)(first_elem * 2));
 #pragma unroll
-    for (int i = 0; i < HD / (8 * ANW); i++) {
-      const int rb = i * ANW + wid;
-      const int row = rb * 8 + rl;
-      const int chunk = att_slot(slot, row, 8);
-      const uint32_t off = (uint32_t)((((vbase_row + row) * (int64_t)ldv) + (int64_t)kb * AKV + chunk * 8) * 2);
-      buffer_load_lds16(rv, (lds_void *)(st + C::KBYTES + rb * 1024), off);
-    }
-  }
+  for (int i = 0; i < HD / (8 * ANW); i++)
+    buffer_load_lds16(rs, (lds_void *)(dst + (i * ANW + wid) * 1024), lane_off + (uint32_t)(i * ANW * 8 * ldv * 2));
 }
 
-template <int HD>
 // q and o may be the same buffer (the output written over the queries): neither is marked
 // __restrict__.  Every Q load of a wave precedes its first O store, and waves read and write
 // only their own query rows.
+template <int HD>
 __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, const uint16_t *__restrict__ k,
                                                            const uint16_t *__restrict__ vt, uint16_t *o, int64_t N,
                                                            int ldv, int heads, float *row_max, float *row_sum) {
   using C = AttCfg<HD>;
   constexpr int KS = HD / 16;   // 16-dim steps of the score product
   constexpr int DT = HD / 32;   // 32-dim output tiles
-  // two LDS stages as separate objects, so that the compiler sees that the prefetch of one
-  // never aliases the reads of the other (and does not wait for the prefetch before them)
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[C::STAGE];
+  // two K and two V^T buffers as separate objects, so that the compiler sees that a prefetch
+  // into one never aliases the reads of another
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf0[C::KBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf1[C::KBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf0[C::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf1[C::VBYTES];
 
   // Workgroups are dealt round-robin to the 8 XCDs in launch order.  When the head count
   // allows, all query tiles of one head go to the same XCD, so that its K and V^T are fetched
@@ -96,17 +120,24 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
     h = (b & 7) + 8 * (j / QT);
     qt = j % QT;
   }
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform in the wave
   const int hsel = lane >> 5, l32 = lane & 31;
   const int64_t q0 = (int64_t)qt * AQ + wid * 32;
   const int64_t qrow = q0 + l32;
   const int64_t head_rows = (int64_t)h * N;
+  const int64_t vfirst = (int64_t)h * HD * ldv;   // first element of the head's V^T rows
 
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k, (uint32_t)((int64_t)heads * N * HD * 2));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt, (uint32_t)((int64_t)heads * HD * ldv * 2));
+  const uint32_t k_bytes = (uint32_t)((int64_t)heads * N * HD * 2);
+  const uint32_t v_bytes = (uint32_t)((int64_t)heads * HD * ldv * 2);
+  const uint32_t lane_k = att_lane_k<HD>(wid, lane), lane_v = att_lane_v(wid, lane, ldv);
+  auto load_k = [&](uint8_t *dst, int kb) { att_load_k<HD>(k, k_bytes, dst, head_rows + (int64_t)kb * AKV, wid, lane_k); };
+  auto load_v = [&](uint8_t *dst, int kb) { att_load_v<HD>(vt, v_bytes, dst, vfirst + (int64_t)kb * AKV, ldv, wid, lane_v); };
 
   const int nkb = (int)((N + AKV - 1) / AKV);
-  att_load<HD>(rk, rv, stage0, head_rows, (int64_t)h * HD, ldv, 0);
+  const int last_valid = (int)(N - (int64_t)(nkb - 1) * AKV);   // keys in the last block, 1..AKV
+  load_k(kbuf0, 0);
+  load_v(vbuf0, 0);
 
   // Q fragments (B operand: column = query, 8 dims per lane and step), kept in registers
   u32x4 qf[KS];
@@ -127,49 +158,34 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
   // for the row statistics; l_run sums 2^((s - m_ref) c2).
   float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
 
-  wait_vmem();
-  __syncthreads();
-
-  // one key block: multiply out of `cur`, prefetch the next block into `nxt`
-  auto block = [&](int kb, uint8_t *cur, uint8_t *nxt) {
-    if (kb + 1 < nkb) att_load<HD>(rk, rv, nxt, head_rows, (int64_t)h * HD, ldv, kb + 1);
-    const int valid = (int)min((int64_t)AKV, N - (int64_t)kb * AKV);
-    if (valid < AKV) {
-      // keys past the end: zero their values so that 0-weight * garbage stays 0
-      for (int idx = threadIdx.x; idx < HD * AKV; idx += ATHREADS) {
-        const int row = idx / AKV, key = idx % AKV;
-        if (key >= valid) {
-          const int ps = (int)vt_pos(key);   // physical position of the key in the row
-          *reinterpret_cast<uint16_t *>(cur + C::KBYTES + row * C::VROW + (att_slot(ps >> 3, row, 8) << 4) + (ps & 7) * 2) = 0;
-        }
-      }
-      __syncthreads();
-    }
-    // S^T for 64 keys x 32 queries: two 32-key tiles
-    f32x16 s[2];
+  // S^T = K Q^T for the 64 keys of one block: two 32-key tiles (lane = one query; register r
+  // of tile t holds key 32t + 8(r/4) + 4 hsel + r%4)
+  auto scores = [&](const uint8_t *kb_, f32x16 (&s)[2]) {
+    s[0] = f32x16{0};
+    s[1] = f32x16{0};
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-      s[t] = f32x16{0};
-      const int krow = t * 32 + l32;
+    for (int st = 0; st < KS; st++)
 #pragma unroll
-      for (int st = 0; st < KS; st++) {
-        const u32x4 kf = *reinterpret_cast<const u32x4 *>(cur + krow * C::KROW + (att_slot(2 * st + hsel, krow, HD / 8) << 4));
+      for (int t = 0; t < 2; t++) {
+        const int krow = t * 32 + l32;
+        const u32x4 kf = *reinterpret_cast<const u32x4 *>(kb_ + krow * C::KROW + (att_slot(2 * st + hsel, krow, HD / 8) << 4));
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[st]),
                                                        s[t], 0, 0, 0);
       }
-    }
-    // online softmax over this block (lane = one query; rows r are keys).  The max is taken
-    // on raw scores (the scale c2 > 0 keeps the order); p = 2^(s*c2 - m*c2) with one fma.
-    // Keys past the end exist only in the last block.
-    if (valid < AKV) {
+  };
+  // keys past the end (the last block only) get score -inf
+  // (the lane's keys are 4 hsel + c for constants c: one comparison with lim per key)
+  auto mask = [&](f32x16 (&s)[2]) {
+    const int lim = last_valid - 4 * hsel;
 #pragma unroll
-      for (int t = 0; t < 2; t++)
+    for (int t = 0; t < 2; t++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int key = t * 32 + 8 * (r / 4) + 4 * hsel + (r % 4);
-          if (key >= valid) s[t][r] = -INFINITY;
-        }
-    }
+      for (int r = 0; r < 16; r++)
+        if (t * 32 + 8 * (r / 4) + (r % 4) >= lim) s[t][r] = -INFINITY;
+  };
+  // block max on raw scores (the scale c2 > 0 keeps the order), over the lane's 32 keys and
+  // the other half-wave's
+  auto block_max = [&](const f32x16 (&s)[2]) {
     float mq[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) mq[u] = fmaxf(s[u >> 1][(u & 1) * 8], s[u >> 1][(u & 1) * 8 + 1]);
@@ -179,10 +195,12 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
       for (int r = 0; r < 16; r++)
         if ((r & 7) > 1) mq[t * 2 + (r >> 3)] = fmaxf(mq[t * 2 + (r >> 3)], s[t][r]);
     float mb = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    return fmaxf(mb, __shfl_xor(mb, 32, 64));
+  };
+  // raise the reference (and rescale what was summed against the old one) only when a lane's
+  // scores would exceed it by more than 2^8; the first block always does
+  auto rebase = [&](float mb) {
     m_true = fmaxf(m_true, mb);
-    // raise the reference (and rescale what was summed against the old one) only when a
-    // lane's scores would exceed it by more than 2^8; the first block always does
     if (__any((mb - m_ref) * c2 > 8.0f)) {
       const float m_new = fmaxf(m_ref, mb);
       const float corr = __builtin_amdgcn_exp2f((m_ref - m_new) * c2);   // 0 on the first block
@@ -193,40 +211,197 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
         for (int r = 0; r < 16; r++) acc[t][r] *= corr;
       m_ref = m_new;
     }
+  };
+  // p = 2^(s c2 - m_ref c2), one fma and one exp2 per score, in place
+  auto probs = [&](f32x16 (&s)[2]) {
     const float mc = m_ref * c2;
-    float lq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c2, -mc));
-        s[t][r] = p;
-        lq[t * 2 + (r >> 3)] += p;
-      }
-    float ls = (lq[0] + lq[1]) + (lq[2] + lq[3]);
-    ls += __shfl_xor(ls, 32, 64);
-    l_run += ls;
-    // O^T += V^T P^T over four 16-key steps
+      for (int r = 0; r < 16; r++) s[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c2, -mc));
+  };
+  // O^T += V^T P^T over four 16-key steps, and the row sum of P.  The key order inside a step is
+  // the score layout's: keys 16ps+4h..+3 and 16ps+8+4h..+3 sit at positions 16ps+8h..+7 of the
+  // V^T row, chunk 2ps+h.  In the last block, values of keys past the end (the row's padding,
+  // which may hold anything, NaN included) are cleared in the fragment, so that their zero
+  // weights give zero.
+  auto pv = [&](const uint8_t *vb_, const f32x16 (&s)[2], bool tail) {
+    float lq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ps = 0; ps < 4; ps++) {
       const int t = ps >> 1, rb = 8 * (ps & 1);
       bf16x8 pf;
 #pragma unroll
       for (int j = 0; j < 8; j++) pf[j] = (__bf16)s[t][rb + j];
-      // keys 16ps+4h..+3 and 16ps+8+4h..+3 sit at positions 16ps+8h..+7: chunk 2ps+h of the row
+      uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
+      if (tail) {
+        const int lim = last_valid - 4 * hsel;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          const int c = 16 * ps + 8 * (w >> 1) + 2 * (w & 1);   // keys 4 hsel + c, + 1 of the word's halves
+          keep[w] = (c < lim ? 0xFFFFu : 0u) | (c + 1 < lim ? 0xFFFF0000u : 0u);
+        }
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; dt++) {
         const int row = dt * 32 + l32;
-        const u32x4 vf = *reinterpret_cast<const u32x4 *>(cur + C::KBYTES + row * C::VROW + (att_slot(2 * ps + hsel, row, 8) << 4));
+        u32x4 vf = *reinterpret_cast<const u32x4 *>(vb_ + row * C::VROW + (att_slot(2 * ps + hsel, row, 8) << 4));
+        if (tail) {
+#pragma unroll
+          for (int w = 0; w < 4; w++) vf[w] &= keep[w];
+        }
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf), pf, acc[dt], 0, 0, 0);
       }
+#pragma unroll
+      for (int j = 0; j < 8; j++) lq[ps] += s[t][rb + j];
     }
+    float ls = (lq[0] + lq[1]) + (lq[2] + lq[3]);
+    l_run += ls + __shfl_xor(ls, 32, 64);
+  };
+
+  // The steady-state phases below are written in the order the instructions should issue:
+  // each MFMA is followed by its share of the VALU work of the other block, and each LDS
+  // fragment is read one MFMA pair ahead of its use.
+  auto kfrag = [&](const uint8_t *kb_, int st, int t) {
+    const int krow = t * 32 + l32;
+    return *reinterpret_cast<const u32x4 *>(kb_ + krow * C::KROW + (att_slot(2 * st + hsel, krow, HD / 8) << 4));
+  };
+  auto vfrag = [&](const uint8_t *vb_, int ps, int dt) {
+    const int row = dt * 32 + l32;
+    return *reinterpret_cast<const u32x4 *>(vb_ + row * C::VROW + (att_slot(2 * ps + hsel, row, 8) << 4));
+  };
+  // scores of the next block (sn) on MFMA, probabilities of the current one (sc) on VALU
+  auto scores_probs = [&](const uint8_t *kb_, f32x16 (&sn)[2], f32x16 (&sc)[2]) {
+    constexpr int PER = 32 / KS;   // probabilities per score step
+    const float mc = m_ref * c2;
+    sn[0] = f32x16{0};
+    sn[1] = f32x16{0};
+    u32x4 k0 = kfrag(kb_, 0, 0), k1 = kfrag(kb_, 0, 1);
+#pragma unroll
+    for (int st = 0; st < KS; st++) {
+      u32x4 n0 = k0, n1 = k1;
+      if (st + 1 < KS) {
+        n0 = kfrag(kb_, st + 1, 0);
+        n1 = kfrag(kb_, st + 1, 1);
+      }
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0), __builtin_bit_cast(bf16x8, qf[st]),
+                                                      sn[0], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < PER / 2; e++) {
+        const int i = st * PER + e;
+        sc[i >> 4][i & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i >> 4][i & 15], c2, -mc));
+      }
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1), __builtin_bit_cast(bf16x8, qf[st]),
+                                                      sn[1], 0, 0, 0);
+#pragma unroll
+      for (int e = PER / 2; e < PER; e++) {
+        const int i = st * PER + e;
+        sc[i >> 4][i & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i >> 4][i & 15], c2, -mc));
+      }
+      k0 = n0;
+      k1 = n1;
+    }
+  };
+  // O^T update with the current block's probabilities on MFMA; their row sum and the next
+  // block's max on VALU.  Returns the next block's max (both half-waves).
+  auto pv_max = [&](const uint8_t *vb_, const f32x16 (&sc)[2], const f32x16 (&sn)[2]) {
+    float lq[4], mq[4];
+    u32x4 v = vfrag(vb_, 0, 0);
+#pragma unroll
+    for (int ps = 0; ps < 4; ps++) {
+      const int t = ps >> 1, rb = 8 * (ps & 1);
+      bf16x8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; j++) pf[j] = (__bf16)sc[t][rb + j];
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) {
+        u32x4 nv = v;
+        if (dt + 1 < DT)
+          nv = vfrag(vb_, ps, dt + 1);
+        else if (ps + 1 < 4)
+          nv = vfrag(vb_, ps + 1, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf, acc[dt], 0, 0, 0);
+        if (dt == 0) {
+          lq[ps] = sc[t][rb];
+#pragma unroll
+          for (int j = 1; j < 8; j++) lq[ps] += sc[t][rb + j];
+        }
+        if (dt == 1) {
+          mq[ps] = att_max3(sn[t][rb], sn[t][rb + 1], sn[t][rb + 2]);
+          mq[ps] = att_max3(mq[ps], sn[t][rb + 3], sn[t][rb + 4]);
+          mq[ps] = att_max3(mq[ps], sn[t][rb + 5], sn[t][rb + 6]);
+          mq[ps] = fmaxf(mq[ps], sn[t][rb + 7]);
+        }
+        v = nv;
+      }
+    }
+    float ls = (lq[0] + lq[1]) + (lq[2] + lq[3]);
+    l_run += ls + __shfl_xor(ls, 32, 64);
+    const float mb = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+    return fmaxf(mb, __shfl_xor(mb, 32, 64));
+  };
+
+  // Software pipeline over the key blocks: while the MFMAs of block j+1's scores run, the VALU
+  // turns block j's scores into probabilities; while the MFMAs of block j's O^T update run, it
+  // sums block j's probabilities and takes block j+1's max.  K runs one block ahead of V^T:
+  // during step j, K(j+2) is fetched into the buffer K(j) used and V^T(j+1) into the one of
+  // V^T(j-1); the barrier at the start of each step orders both after the last reads of what
+  // they overwrite.
+  f32x16 sa[2], sb[2];
+  if (nkb > 1) load_k(kbuf1, 1);
+  wait_vmem();
+  __syncthreads();
+  scores(kbuf0, sa);
+  if (nkb == 1 && last_valid < AKV) mask(sa);
+  rebase(block_max(sa));
+
+  // step j: K(j+1) sits in kn, V^T(j) in vc; kc (K(j)'s buffer) receives K(j+2), vn V^T(j+1)
+  // (interior: j + 3 < nkb is known, so that neither test below branches)
+  auto step = [&](bool interior, int j, uint8_t *kc, const uint8_t *kn, uint8_t *vc, uint8_t *vn, f32x16 (&sc)[2],
+                  f32x16 (&sn)[2]) {
     wait_vmem();
     __syncthreads();
+    if (interior || j + 2 < nkb) load_k(kc, j + 2);
+    load_v(vn, j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    scores_probs(kn, sn, sc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!interior && j + 2 == nkb && last_valid < AKV) mask(sn);
+    __builtin_amdgcn_sched_barrier(0);
+    const float mb = pv_max(vc, sc, sn);
+#pragma unroll
+    for (int i = 0; i < 4 * DT; i++) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 16 / DT, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    rebase(mb);
   };
-  for (int kb = 0; kb < nkb; kb += 2) {
-    block(kb, stage0, stage1);
-    if (kb + 1 < nkb) block(kb + 1, stage1, stage0);
+  // last step: V^T(nkb-1) in vc, its probabilities from sc
+  auto last = [&](const uint8_t *vc, f32x16 (&sc)[2]) {
+    wait_vmem();
+    __syncthreads();
+    probs(sc);
+    pv(vc, sc, true);
+  };
+  // Steps run in pairs so that every buffer is named statically; the pairs whose steps are all
+  // interior loop, the last one or two steps and the last block follow.
+  int j = 0;
+  for (; j + 3 < nkb; j += 2) {
+    step(true, j, kbuf0, kbuf1, vbuf0, vbuf1, sa, sb);
+    step(true, j + 1, kbuf1, kbuf0, vbuf1, vbuf0, sb, sa);
+  }
+  if (j + 1 < nkb) {
+    step(false, j, kbuf0, kbuf1, vbuf0, vbuf1, sa, sb);
+    if (j + 2 < nkb) {
+      step(false, j + 1, kbuf1, kbuf0, vbuf1, vbuf0, sb, sa);
+      last(vbuf0, sa);
+    } else {
+      last(vbuf1, sb);
+    }
+  } else {
+    last(vbuf0, sa);
   }
 
   // O[h][q][dim] = O^T / l; lane holds dims dt*32 + 8(r/4) + 4 hsel + r%4 of query qrow
