@@ -15,7 +15,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libh3dit.so")
+# H3DIT_LIB names another build of the same sources (the host-sanitizer build of the host tests)
+LIB_PATH = os.environ.get("H3DIT_LIB") or os.path.join(HERE, "libh3dit.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "

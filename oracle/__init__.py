@@ -12,7 +12,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# H3DIT_ORACLE_LIB names another build of the same source (the sanitizer build of the tests)
+_LIB_PATH = os.environ.get("H3DIT_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 _lib = None
 
 
