@@ -554,56 +554,91 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
       const int d = p.heads * p.hd;
       const int part = (int)(n0 / d);
       if (part < 2) {
+        // A thread takes one 8-element chunk ci of a head row and does it for every head of the
+        // tile (the heads of one token share its rotary table entries), rows tid / cph, +
+        // NT / cph, ... (head rows of at least 8 chunks: hd >= 64)
+        const int cph = p.hd / 8;              // chunks per head row
+        const int hpt = BN / p.hd;             // heads per tile
+        const int ci = tid % cph, i0 = ci * 8;
+        const int h0 = (int)(n0 % d) / p.hd;   // first head of the tile
+        uint16_t *dst0 = (part == 0 ? p.oq : p.ok) + (int64_t)h0 * p.M * p.hd + i0;
         const int half = p.hd / 2;
-        const int col = (int)(n0 % d) + c * 8;
-        const int h = col / p.hd, i0 = col % p.hd;
-        uint16_t *dst = (part == 0 ? p.oq : p.ok) + (int64_t)h * p.M * p.hd + i0;
         const float *cos_c = p.cos_t + i0 / 2, *sin_c = p.sin_t + i0 / 2;
-        for (int r = tid / CH; r < BM; r += NT / CH) {
-          const int64_t row = m0 + r;
-          if (row >= p.M) break;   // later rows are past the end too
-          float f[8], o[8];
-          unpack8(*reinterpret_cast<const u32x4 *>(smem + r * C::CPITCH + c * 16), f);
-          const float4 cs = *reinterpret_cast<const float4 *>(cos_c + row * half);
-          const float4 sn = *reinterpret_cast<const float4 *>(sin_c + row * half);
-          const float cc[4] = {cs.x, cs.y, cs.z, cs.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+        // the table entries of all the thread's rows (BM * cph / NT of them; cph <= 16) are
+        // loaded first, so that their latencies overlap
+        constexpr int MAXR = BM * 16 / NT;
+        const int r0 = tid / cph, rstep = NT / cph;
+        float4 tcos[MAXR], tsin[MAXR];
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            o[2 * e] = f[2 * e] * cc[e] - f[2 * e + 1] * ss[e];
-            o[2 * e + 1] = f[2 * e] * ss[e] + f[2 * e + 1] * cc[e];
+        for (int k = 0; k < MAXR; k++) {
+          const int r = r0 + k * rstep;
+          if (r < BM && m0 + r < p.M) {
+            tcos[k] = *reinterpret_cast<const float4 *>(cos_c + (m0 + r) * half);
+            tsin[k] = *reinterpret_cast<const float4 *>(sin_c + (m0 + r) * half);
           }
-          *reinterpret_cast<u32x4 *>(dst + row * p.hd) = pack8(o);
         }
-      } else {
-        // V^T[h][i][vt_pos(m)]: one lane per (feature column, group of 16 tokens); inside a
-        // group, tokens 0-3 | 8-11 | 4-7 | 12-15 land at slots 0-15 (two 16-byte stores)
-        // (a thread keeps one feature column: NT is a multiple of BN)
-        static_assert(NT % BN == 0, "whole feature columns per pass");
-        const int cv = tid % BN;
-        const int col = (int)(n0 % d) + cv;
-        const int h = col / p.hd, i = col % p.hd;
-        uint16_t *dst_c = p.ov + ((int64_t)h * p.hd + i) * p.ldv;
-        for (int rb = tid / BN; rb < BM / 16; rb += NT / BN) {
-          const int64_t row = m0 + rb * 16;
-          if (row >= p.M) break;   // later groups are past the end too
-          uint16_t v16[16];
 #pragma unroll
-          for (int e = 0; e < 16; e++)
-            v16[vt_pos(e)] = *reinterpret_cast<const uint16_t *>(smem + (rb * 16 + e) * C::CPITCH + cv * 2);
-          uint16_t *dst = dst_c + row;
-          if (row + 16 <= p.M) {
-            u32x4 v0, v1;
+        for (int k = 0; k < MAXR; k++) {
+          const int r = r0 + k * rstep;
+          const int64_t row = m0 + r;
+          if (r >= BM || row >= p.M) break;   // later rows are past the tile or the end too
+          const float cc[4] = {tcos[k].x, tcos[k].y, tcos[k].z, tcos[k].w};
+          const float ss[4] = {tsin[k].x, tsin[k].y, tsin[k].z, tsin[k].w};
+          for (int hh = 0; hh < hpt; hh++) {
+            float f[8], o[8];
+            unpack8(*reinterpret_cast<const u32x4 *>(smem + r * C::CPITCH + (hh * cph + ci) * 16), f);
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-              v0[e] = (uint32_t)v16[2 * e] | ((uint32_t)v16[2 * e + 1] << 16);
-              v1[e] = (uint32_t)v16[8 + 2 * e] | ((uint32_t)v16[8 + 2 * e + 1] << 16);
+              o[2 * e] = f[2 * e] * cc[e] - f[2 * e + 1] * ss[e];
+              o[2 * e + 1] = f[2 * e] * ss[e] + f[2 * e + 1] * cc[e];
             }
-            reinterpret_cast<u32x4 *>(dst)[0] = v0;
-            reinterpret_cast<u32x4 *>(dst)[1] = v1;
+            *reinterpret_cast<u32x4 *>(dst0 + (int64_t)hh * p.M * p.hd + row * p.hd) = pack8(o);
+          }
+        }
+      } else {
+        // V^T[h][i][vt_pos(m)].  Inside a 16-token group, positions 0-7 hold tokens 0-3 and
+        // 8-11, positions 8-15 tokens 4-7 and 12-15.  A unit is (group rb, half hh, 8-feature
+        // chunk fc): the half's 8 tokens are read as 16-byte rows of the staged tile (the
+        // chunk's 8 features each), transposed in registers and stored as one 16-byte piece
+        // of each of the chunk's 8 V^T rows.
+        constexpr int FCH = BN / 8;                   // feature chunks per tile
+        constexpr int UNITS = (BM / 16) * 2 * FCH;
+        static_assert(UNITS % NT == 0, "whole passes");
+        const int fc = tid % FCH;
+        const int col = (int)(n0 % d) + fc * 8;       // first feature of the chunk
+        const int h = col / p.hd, i = col % p.hd;     // the chunk's 8 features share the head
+        uint16_t *dst_c = p.ov + ((int64_t)h * p.hd + i) * p.ldv;
+        for (int gh = tid / FCH; gh < (BM / 16) * 2; gh += NT / FCH) {
+          const int rb = gh >> 1, hh = gh & 1;
+          const int64_t row0 = m0 + rb * 16;
+          if (row0 >= p.M) break;   // later groups are past the end too
+          u32x4 x[8];
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const int tok = (j & 3) + 4 * hh + 8 * (j >> 2);
+            x[j] = *reinterpret_cast<const u32x4 *>(smem + (rb * 16 + tok) * C::CPITCH + fc * 16);
+          }
+          // word w of feature e's piece: tokens 2w (low half) and 2w + 1 (high half)
+          u32x4 y[8];
+#pragma unroll
+          for (int e = 0; e < 8; e++)
+#pragma unroll
+            for (int w = 0; w < 4; w++)
+              y[e][w] = __builtin_amdgcn_perm(x[2 * w + 1][e >> 1], x[2 * w][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+          uint16_t *dst = dst_c + row0 + 8 * hh;
+          if (row0 + 16 <= p.M) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) *reinterpret_cast<u32x4 *>(dst + (int64_t)e * p.ldv) = y[e];
           } else {
 #pragma unroll
-            for (int e = 0; e < 16; e++)
-              if (row + e < p.M) dst[vt_pos(e)] = v16[vt_pos(e)];
+            for (int j = 0; j < 8; j++) {
+              const int tok = (j & 3) + 4 * hh + 8 * (j >> 2);
+              if (row0 + tok < p.M) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                  dst[(int64_t)e * p.ldv + j] = (uint16_t)(y[e][j >> 1] >> (16 * (j & 1)));
+              }
+            }
           }
         }
       }
