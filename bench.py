@@ -158,11 +158,10 @@ def time_streamed(w, blocks, x, steps, warmup, reduction=None):
 
 
 def kernel_breakdown(w, p, x, iters, int8):
-    """Times each kernel of one block on its own (HIP events on the current stream): each kernel
-    runs `iters` times back to back on the same buffers, so its operands stay in the 256 MB
-    last-level cache between launches.  These are isolated-loop figures; the same kernels'
-    times inside the stack (where each reads what the previous kernel just wrote) come from the
-    committed rocprofv3 traces."""
+    """Times each kernel of one block where it runs in the block: `iters` passes over the
+    block's launches in order, every launch bracketed by HIP events on the current stream (the
+    stream the library launches on), so each kernel reads what the kernel before it just wrote,
+    as in the stack; a stage's time is the mean of its launches' event intervals."""
     import torch
     import audio_diffusion_transformer_dit_amd as h3
     dev = x.device
@@ -248,16 +247,18 @@ def kernel_breakdown(w, p, x, iters, int8):
     for fn, _, _ in ops.values():
         fn()
     torch.cuda.synchronize()
+    evs = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+           for name in ops}
+    for it in range(iters):
+        for name, (fn, _, _) in ops.items():
+            s, e = evs[name][it]
+            s.record()
+            fn()
+            e.record()
+    torch.cuda.synchronize()
     res = {}
     for name, (fn, flop, nbytes) in ops.items():
-        fn()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(iters):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / iters
+        ms = sum(s.elapsed_time(e) for s, e in evs[name]) / iters
         r = {"ms": round(ms, 4)}
         if flop:
             r["tflops"] = round(flop / ms / 1e9, 1)
@@ -432,7 +433,7 @@ def main():
             "traffic": traffic_for(dom)}
     extra = {"ms_per_block": round(ms / w.blocks, 3), **step_stats, "tflop_per_step": round(step_flop / 1e12, 2),
              "workspace_bytes": ws_bytes, "kernels": kern,
-             "kernels_note": "isolated loops: each kernel launched back to back on one block's buffers",
+             "kernels_note": "per-launch HIP event intervals over repeated passes of one block's launch sequence",
              "wall_s_timed": round(wall, 3)}
     if args.streamed:
         print("[bench] timing the stack with weights streamed from host memory", file=sys.stderr, flush=True)
