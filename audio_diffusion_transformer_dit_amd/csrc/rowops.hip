@@ -212,16 +212,21 @@ hipError_t launch_row_stats(int64_t n, int d, float eps, const uint16_t *x, floa
 // Spans of up to 8192 columns (the per-token codes of a d-wide row, the 1024-channel groups of
 // the FC2 input): one wave per GPW consecutive spans of one row, lane l holding chunks l, l + 64,
 // ... of each span (CPL per span), so that a lane has several 16-byte loads in flight and every
-// absmax is a wave reduction.  Head-major input (hm_hd > 0): element (r, c) of the token-major
-// view sits at ((c / hd) * rows + r) * hd + c % hd; a chunk of 8 never crosses a head.
+// absmax is a wave reduction.  Waves are numbered across rows (wave w: row w / upr, spans from
+// (w % upr) * GPW, upr = ceil(spans per row / GPW)), so that every wave of a workgroup has work
+// even where a row has fewer units than a workgroup has waves.  Head-major input (hm_hd > 0):
+// element (r, c) of the token-major view sits at ((c / hd) * rows + r) * hd + c % hd; a chunk of
+// 8 never crosses a head.
 template <int CPL, int GPW>
 __global__ __launch_bounds__(64 * RW_WAVES) void k_quant_span(int64_t rows, int64_t cols, int group,
                                                               const uint16_t *__restrict__ v, int hm_hd,
                                                               int8_t *__restrict__ q, float *__restrict__ s) {
   const int64_t ng = cols / group;
-  const int64_t r = blockIdx.x;
-  const int64_t g0 = ((int64_t)blockIdx.y * RW_WAVES + (threadIdx.x >> 6)) * GPW;
-  if (g0 >= ng) return;   // whole waves
+  const int64_t upr = (ng + GPW - 1) / GPW;   // wave units per row
+  const int64_t w = (int64_t)blockIdx.x * RW_WAVES + (threadIdx.x >> 6);
+  if (w >= rows * upr) return;   // whole waves
+  const int64_t r = w / upr;
+  const int64_t g0 = (w % upr) * GPW;
   const int lane = threadIdx.x & 63;
   const int nch = group >> 3;
   u32x4 raw[GPW][CPL];
@@ -333,9 +338,11 @@ hipError_t launch_quant_rows(int64_t rows, int64_t cols, int64_t group, const ui
       k_quant_long<<<grid, ROW_THREADS, 0, st>>>(cols, group, v, q, s);
     return hipGetLastError();
   }
-  // chunks per lane and span, and spans per wave (at least about eight 16-byte loads per lane)
+  // chunks per lane and span, and spans per wave (at least about eight 16-byte loads per lane);
+  // one wave per unit of GPW spans, numbered across rows (grid of at most 2^30 workgroups)
+  if (rows * ng > ((int64_t)1 << 32)) return hipErrorInvalidValue;
   const int need = (int)((group / 8 + 63) / 64);
-#define H3_QS(CPL, GPW)                                                                                           k_quant_span<CPL, GPW><<<dim3((unsigned)rows, (unsigned)((ng + RW_WAVES * GPW - 1) / (RW_WAVES * GPW))),                                64 * RW_WAVES, 0, st>>>(rows, cols, (int)group, v, hm_hd, q, s)
+#define H3_QS(CPL, GPW)                                                                                           k_quant_span<CPL, GPW><<<(unsigned)((rows * ((ng + GPW - 1) / GPW) + RW_WAVES - 1) / RW_WAVES),                  64 * RW_WAVES, 0, st>>>(rows, cols, (int)group, v, hm_hd, q, s)
   if (need <= 1) H3_QS(1, 8);
   else if (need <= 2) H3_QS(2, 4);
   else if (need <= 4) H3_QS(4, 2);
