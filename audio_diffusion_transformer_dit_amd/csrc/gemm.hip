@@ -513,21 +513,40 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
         }
     return;
   } else {
-    // registers -> bf16 tile in LDS
+    // registers -> bf16 tile in LDS.  int8: every row and column scale the lane needs is
+    // loaded before any is used (one round trip): rows m0 + rbase + 32 i + 8 q .. + 3 as one
+    // 16-byte load through a resource that ends with the scale array (rows >= M read 0)
+    float4 sa4[INT8 && !GROUPED ? FM : 1][4];
+    float swj[INT8 ? FN : 1];
+    if constexpr (INT8 && !GROUPED) {
+      const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.a_scale, (uint32_t)(p.M * 4));
+#pragma unroll
+      for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++)
+          sa4[i][q4] = __builtin_bit_cast(
+              float4, __builtin_amdgcn_raw_buffer_load_b128(rsa, (uint32_t)((m0 + rbase + 32 * i + 8 * q4) * 4), 0, 0));
+    }
+    if constexpr (INT8) {
+#pragma unroll
+      for (int j = 0; j < FN; j++) swj[j] = p.w_scale[n0 + cbase + 32 * j];
+    }
 #pragma unroll
     for (int i = 0; i < FM; i++) {
       float sa_r[16];
       if constexpr (INT8 && !GROUPED) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int64_t row = m0 + rbase + 32 * i + 8 * (r / 4) + (r % 4);
-          sa_r[r] = row < p.M ? p.a_scale[row] : 0.0f;
+        for (int q4 = 0; q4 < 4; q4++) {
+          sa_r[4 * q4] = sa4[i][q4].x;
+          sa_r[4 * q4 + 1] = sa4[i][q4].y;
+          sa_r[4 * q4 + 2] = sa4[i][q4].z;
+          sa_r[4 * q4 + 3] = sa4[i][q4].w;
         }
       }
 #pragma unroll
       for (int j = 0; j < FN; j++) {
         float sw = 0.0f;
-        if constexpr (INT8) sw = p.w_scale[n0 + cbase + 32 * j];
+        if constexpr (INT8) sw = swj[j];
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           float v;
