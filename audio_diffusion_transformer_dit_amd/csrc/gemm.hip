@@ -515,7 +515,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
   } else {
     // registers -> bf16 tile in LDS.  int8: every row and column scale the lane needs is
     // loaded before any is used (one round trip): rows m0 + rbase + 32 i + 8 q .. + 3 as one
-    // 16-byte load through a resource that ends with the scale array (rows >= M read 0)
+    // 16-byte load through a resource that ends with the scale array; the range check is per
+    // dword, so rows >= M read 0 while the rows before them in the same load read their scales
+    // (the ragged int8 QKV case M = 130 checks it bit for bit)
     float4 sa4[INT8 && !GROUPED ? FM : 1][4];
     float swj[INT8 ? FN : 1];
     if constexpr (INT8 && !GROUPED) {
