@@ -392,17 +392,20 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
     step(true, j, kbuf0, kbuf1, vbuf0, vbuf1, sa, sb);
     step(true, j + 1, kbuf1, kbuf0, vbuf1, vbuf0, sb, sa);
   }
+  // (one or two steps left, or none; the last block's probabilities are brought into sa so
+  // that one copy of the last step serves every count)
+  const uint8_t *vlast = vbuf0;
   if (j + 1 < nkb) {
     step(false, j, kbuf0, kbuf1, vbuf0, vbuf1, sa, sb);
     if (j + 2 < nkb) {
       step(false, j + 1, kbuf1, kbuf0, vbuf1, vbuf0, sb, sa);
-      last(vbuf0, sa);
     } else {
-      last(vbuf1, sb);
+      sa[0] = sb[0];
+      sa[1] = sb[1];
+      vlast = vbuf1;
     }
-  } else {
-    last(vbuf0, sa);
   }
+  last(vlast, sa);
 
   // O[h][q][dim] = O^T / l; lane holds dims dt*32 + 8(r/4) + 4 hsel + r%4 of query qrow
   if (qrow < N) {
