@@ -36,13 +36,8 @@ struct AttCfg {
   static constexpr int STAGE = KBYTES + VBYTES;
 };
 
-// v_max3_f32 without the NaN canonicalisation of the inputs that fmaxf brings (scores are
-// finite or -inf)
-__device__ __forceinline__ float att_max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// three-input max (the compiler forms v_max3_f32)
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int SG_VALU = 0x2, SG_MFMA = 0x8, SG_DS_READ = 0x100;
@@ -194,7 +189,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
 #pragma unroll
       for (int r = 0; r < 16; r++)
         if ((r & 7) > 1) mq[t * 2 + (r >> 3)] = fmaxf(mq[t * 2 + (r >> 3)], s[t][r]);
-    float mb = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+    const float mb = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     return fmaxf(mb, __shfl_xor(mb, 32, 64));
   };
   // raise the reference (and rescale what was summed against the old one) only when a lane's
@@ -327,9 +322,9 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
           for (int j = 1; j < 8; j++) lq[ps] += sc[t][rb + j];
         }
         if (dt == 1) {
-          mq[ps] = att_max3(sn[t][rb], sn[t][rb + 1], sn[t][rb + 2]);
-          mq[ps] = att_max3(mq[ps], sn[t][rb + 3], sn[t][rb + 4]);
-          mq[ps] = att_max3(mq[ps], sn[t][rb + 5], sn[t][rb + 6]);
+          mq[ps] = max3f(sn[t][rb], sn[t][rb + 1], sn[t][rb + 2]);
+          mq[ps] = max3f(mq[ps], sn[t][rb + 3], sn[t][rb + 4]);
+          mq[ps] = max3f(mq[ps], sn[t][rb + 5], sn[t][rb + 6]);
           mq[ps] = fmaxf(mq[ps], sn[t][rb + 7]);
         }
         v = nv;
@@ -337,7 +332,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
     }
     float ls = (lq[0] + lq[1]) + (lq[2] + lq[3]);
     l_run += ls + __shfl_xor(ls, 32, 64);
-    const float mb = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+    const float mb = max3f(mq[0], mq[1], fmaxf(mq[2], mq[3]));
     return fmaxf(mb, __shfl_xor(mb, 32, 64));
   };
 
