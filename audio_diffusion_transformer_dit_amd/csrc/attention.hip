@@ -16,7 +16,10 @@
 // chunk) cover all 64 banks: c ^ (r & 15) for 256-byte rows, c ^ ((r >> 1) & 7) for 128.
 // The key blocks are software-pipelined: the score MFMAs of block j+1 are interleaved with the
 // exponentials of block j, and block j's O^T MFMAs with its row sums and block j+1's max, so
-// that the matrix pipe and the VALU work on different blocks.  Values past the last key are
+// that the matrix pipe and the VALU work on different blocks.  Each MFMA of the pipelined
+// steps sits in a scheduling region of its own with the LDS fragment of the MFMA two places
+// later read before it: left to itself, the scheduler read each V^T fragment just before its
+// MFMA and waited for it there.  Values past the last key are
 // cleared in the V^T fragments of the last block (the rows' padding may hold anything).
 #include "common.hpp"
 
@@ -38,9 +41,6 @@ struct AttCfg {
 
 // three-input max (the compiler forms v_max3_f32)
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-
-// instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int SG_VALU = 0x2, SG_MFMA = 0x8, SG_DS_READ = 0x100;
 
 // LDS slot of 16-byte chunk c in row r of a tile whose rows are `chunks` chunks long
 __device__ __forceinline__ int att_slot(int c, int r, int chunks) {
@@ -97,6 +97,9 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
   using C = AttCfg<HD>;
   constexpr int KS = HD / 16;   // 16-dim steps of the score product
   constexpr int DT = HD / 32;   // 32-dim output tiles
+  // LDS fragments are read two MFMAs ahead of their use in both products (deeper lookahead
+  // measured no faster)
+  constexpr int KD = 2, VD = 2;
   // two K and two V^T buffers as separate objects, so that the compiler sees that a prefetch
   // into one never aliases the reads of another
   __shared__ __attribute__((aligned(16))) uint8_t kbuf0[C::KBYTES];
@@ -265,70 +268,76 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
     const int row = dt * 32 + l32;
     return *reinterpret_cast<const u32x4 *>(vb_ + row * C::VROW + (att_slot(2 * ps + hsel, row, 8) << 4));
   };
-  // scores of the next block (sn) on MFMA, probabilities of the current one (sc) on VALU
-  auto scores_probs = [&](const uint8_t *kb_, f32x16 (&sn)[2], f32x16 (&sc)[2]) {
+  // scores of the next block (sn) on MFMA, probabilities of the current one (sc) on VALU; each
+  // MFMA in a scheduling region of its own with the K fragment KD MFMAs later read before it.
+  // The first VD V^T fragments of the O^T update (vb_) are read during the last score MFMAs.
+  constexpr int NK = 2 * KS, NV = 4 * DT;
+  auto scores_probs = [&](const uint8_t *kb_, const uint8_t *vb_, f32x16 (&sn)[2], f32x16 (&sc)[2],
+                          u32x4 (&fv)[VD]) {
     constexpr int PER = 32 / KS;   // probabilities per score step
     const float mc = m_ref * c2;
     sn[0] = f32x16{0};
     sn[1] = f32x16{0};
-    u32x4 k0 = kfrag(kb_, 0, 0), k1 = kfrag(kb_, 0, 1);
+    u32x4 fk[KD];
 #pragma unroll
-    for (int st = 0; st < KS; st++) {
-      u32x4 n0 = k0, n1 = k1;
-      if (st + 1 < KS) {
-        n0 = kfrag(kb_, st + 1, 0);
-        n1 = kfrag(kb_, st + 1, 1);
-      }
-      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0), __builtin_bit_cast(bf16x8, qf[st]),
-                                                      sn[0], 0, 0, 0);
+    for (int i = 0; i < KD; i++) fk[i] = kfrag(kb_, i >> 1, i & 1);
+#pragma unroll
+    for (int i = 0; i < NK; i++) {
+      const int st = i >> 1, t = i & 1;
+      u32x4 nk = fk[0];
+      if (i + KD < NK) nk = kfrag(kb_, (i + KD) >> 1, (i + KD) & 1);
+      if (i + VD >= NK) fv[i + VD - NK] = vfrag(vb_, (i + VD - NK) / DT, (i + VD - NK) % DT);
+      sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fk[0]), __builtin_bit_cast(bf16x8, qf[st]),
+                                                      sn[t], 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < PER / 2; e++) {
-        const int i = st * PER + e;
-        sc[i >> 4][i & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i >> 4][i & 15], c2, -mc));
+        const int k = st * PER + t * (PER / 2) + e;
+        sc[k >> 4][k & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[k >> 4][k & 15], c2, -mc));
       }
-      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1), __builtin_bit_cast(bf16x8, qf[st]),
-                                                      sn[1], 0, 0, 0);
 #pragma unroll
-      for (int e = PER / 2; e < PER; e++) {
-        const int i = st * PER + e;
-        sc[i >> 4][i & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i >> 4][i & 15], c2, -mc));
-      }
-      k0 = n0;
-      k1 = n1;
+      for (int r = 0; r + 1 < KD; r++) fk[r] = fk[r + 1];
+      fk[KD - 1] = nk;
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // O^T update with the current block's probabilities on MFMA; their row sum and the next
-  // block's max on VALU.  Returns the next block's max (both half-waves).
-  auto pv_max = [&](const uint8_t *vb_, const f32x16 (&sc)[2], const f32x16 (&sn)[2]) {
+  // block's max on VALU.  Returns the next block's max (both half-waves).  The MFMAs go in
+  // (ps, dt) order, each in a scheduling region of its own, with the V^T fragment of the MFMA
+  // VD places later read before it (fv: the first VD, read by the caller), and the
+  // probabilities of step ps+1 converted during step ps.
+  auto pv_max = [&](const uint8_t *vb_, u32x4 (&fv)[VD], const f32x16 (&sc)[2], const f32x16 (&sn)[2]) {
     float lq[4], mq[4];
-    u32x4 v = vfrag(vb_, 0, 0);
+    bf16x8 pf, pn;
 #pragma unroll
-    for (int ps = 0; ps < 4; ps++) {
+    for (int j = 0; j < 8; j++) pf[j] = (__bf16)sc[0][j];
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int ps = i / DT, dt = i % DT;
       const int t = ps >> 1, rb = 8 * (ps & 1);
-      bf16x8 pf;
+      u32x4 nv = fv[0];
+      if (i + VD < NV) nv = vfrag(vb_, (i + VD) / DT, (i + VD) % DT);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fv[0]), pf, acc[dt], 0, 0, 0);
+      if (dt == 0) {
+        lq[ps] = sc[t][rb];
 #pragma unroll
-      for (int j = 0; j < 8; j++) pf[j] = (__bf16)sc[t][rb + j];
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++) {
-        u32x4 nv = v;
-        if (dt + 1 < DT)
-          nv = vfrag(vb_, ps, dt + 1);
-        else if (ps + 1 < 4)
-          nv = vfrag(vb_, ps + 1, 0);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf, acc[dt], 0, 0, 0);
-        if (dt == 0) {
-          lq[ps] = sc[t][rb];
-#pragma unroll
-          for (int j = 1; j < 8; j++) lq[ps] += sc[t][rb + j];
-        }
-        if (dt == 1) {
-          mq[ps] = max3f(sn[t][rb], sn[t][rb + 1], sn[t][rb + 2]);
-          mq[ps] = max3f(mq[ps], sn[t][rb + 3], sn[t][rb + 4]);
-          mq[ps] = max3f(mq[ps], sn[t][rb + 5], sn[t][rb + 6]);
-          mq[ps] = fmaxf(mq[ps], sn[t][rb + 7]);
-        }
-        v = nv;
+        for (int j = 1; j < 8; j++) lq[ps] += sc[t][rb + j];
       }
+      if (dt == 1) {
+        mq[ps] = max3f(sn[t][rb], sn[t][rb + 1], sn[t][rb + 2]);
+        mq[ps] = max3f(mq[ps], sn[t][rb + 3], sn[t][rb + 4]);
+        mq[ps] = max3f(mq[ps], sn[t][rb + 5], sn[t][rb + 6]);
+        mq[ps] = fmaxf(mq[ps], sn[t][rb + 7]);
+      }
+      if (dt == DT / 2 && ps + 1 < 4) {
+        const int t1 = (ps + 1) >> 1, rb1 = 8 * ((ps + 1) & 1);
+#pragma unroll
+        for (int j = 0; j < 8; j++) pn[j] = (__bf16)sc[t1][rb1 + j];
+      }
+      if (dt == DT - 1) pf = pn;
+#pragma unroll
+      for (int r = 0; r + 1 < VD; r++) fv[r] = fv[r + 1];
+      fv[VD - 1] = nv;
+      __builtin_amdgcn_sched_barrier(0);
     }
     float ls = (lq[0] + lq[1]) + (lq[2] + lq[3]);
     l_run += ls + __shfl_xor(ls, 32, 64);
@@ -359,18 +368,12 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
     if (interior || j + 2 < nkb) load_k(kc, j + 2);
     load_v(vn, j + 1);
     __builtin_amdgcn_sched_barrier(0);
-    scores_probs(kn, sn, sc);
+    u32x4 fv[VD];
+    scores_probs(kn, vc, sn, sc, fv);
     __builtin_amdgcn_sched_barrier(0);
     if (!interior && j + 2 == nkb && last_valid < AKV) mask(sn);
     __builtin_amdgcn_sched_barrier(0);
-    const float mb = pv_max(vc, sc, sn);
-#pragma unroll
-    for (int i = 0; i < 4 * DT; i++) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_VALU, 16 / DT, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    const float mb = pv_max(vc, fv, sc, sn);
     rebase(mb);
   };
   // last step: V^T(nkb-1) in vc, its probabilities from sc
