@@ -42,6 +42,18 @@ struct AttCfg {
 // three-input max (the compiler forms v_max3_f32)
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// max and sum of v over lanes l and l ^ 32 (the two half-waves), in every lane: one
+// v_permlane32_swap, no LDS round trip.  The swap leaves lanes 0..31 of v in both halves of
+// the first result and lanes 32..63 in both halves of the second.
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // LDS slot of 16-byte chunk c in row r of a tile whose rows are `chunks` chunks long
 __device__ __forceinline__ int att_slot(int c, int r, int chunks) {
   return chunks >= 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
@@ -153,7 +165,8 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
   // Lazy rescaling: probabilities are taken relative to a reference m_ref (raw score units)
   // that is raised only when some lane's block max exceeds it by more than 2^8 in the exp2
   // domain, so p <= 256 and most blocks skip the output rescale.  m_true tracks the true max
-  // for the row statistics; l_run sums 2^((s - m_ref) c2).
+  // for the row statistics; l_run sums 2^((s - m_ref) c2) over the lane's own keys (the two
+  // half-waves' sums are added at the end).
   float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
 
   // S^T = K Q^T for the 64 keys of one block: two 32-key tiles (lane = one query; register r
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
       for (int r = 0; r < 16; r++)
         if ((r & 7) > 1) mq[t * 2 + (r >> 3)] = fmaxf(mq[t * 2 + (r >> 3)], s[t][r]);
     const float mb = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    return fmaxf(mb, __shfl_xor(mb, 32, 64));
+    return halves_max(mb);
   };
   // raise the reference (and rescale what was summed against the old one) only when a lane's
   // scores would exceed it by more than 2^8; the first block always does
@@ -254,7 +267,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
       for (int j = 0; j < 8; j++) lq[ps] += s[t][rb + j];
     }
     float ls = (lq[0] + lq[1]) + (lq[2] + lq[3]);
-    l_run += ls + __shfl_xor(ls, 32, 64);
+    l_run += ls;
   };
 
   // The steady-state phases below are written in the order the instructions should issue:
@@ -340,9 +353,9 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
       __builtin_amdgcn_sched_barrier(0);
     }
     float ls = (lq[0] + lq[1]) + (lq[2] + lq[3]);
-    l_run += ls + __shfl_xor(ls, 32, 64);
+    l_run += ls;
     const float mb = max3f(mq[0], mq[1], fmaxf(mq[2], mq[3]));
-    return fmaxf(mb, __shfl_xor(mb, 32, 64));
+    return halves_max(mb);
   };
 
   // Software pipeline over the key blocks: while the MFMAs of block j+1's scores run, the VALU
@@ -406,6 +419,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
   last(vlast, sa);
 
   // O[h][q][dim] = O^T / l; lane holds dims dt*32 + 8(r/4) + 4 hsel + r%4 of query qrow
+  l_run = halves_sum(l_run);
   if (qrow < N) {
     const float inv = 1.0f / l_run;
     uint16_t *dst = o + (head_rows + qrow) * HD;
