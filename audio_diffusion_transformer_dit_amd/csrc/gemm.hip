@@ -15,11 +15,8 @@
 //    stalls the schedule is explicit: slice k+1's LDS stores and slice k+2's loads are spread
 //    between the MFMAs of slice k, and the per-slice barrier sits before the last K step so
 //    that the next slice's first fragments are read under that step's MFMAs.
-//  * int8 (and the 256 x 128 shape): 8 waves (two per SIMD) of 128 x 64 (the grouped int8
-//    FC2: 4-wave 128 x 128 tiles of 64 x 64, two workgroups per CU); while slice k is
-//    multiplied, slice k+1 is stored to the other LDS stage at the top of the iteration and
-//    the loads of slice k+3 are spread between the MFMAs, so each load has more than a whole
-//    iteration to arrive.
+//  * int8 (and the 256 x 128 shape): 8 waves (two per SIMD) of 128 x 64 (256 x 128: 64 x 64,
+//    also the grouped int8 FC2), in the same loop.
 // Rows past M read as zeros (buffer range check, see a_load).  The epilogue stages the bf16 tile in LDS
 // and writes 16-byte row chunks (or, for V, 16-byte token chunks of V^T).  Workgroups are
 // dealt round-robin to the 8 XCDs; the tile order is remapped so that each XCD sweeps a
@@ -30,9 +27,9 @@ namespace h3 {
 
 constexpr int GKB = 128;        // bytes of K per slice and row
 // Tile of the grouped int8 FC2 (two accumulator sets per lane: int32 within a group, fp32
-// across groups): G_BM x G_BN, a G_WGM x G_WGN grid of waves of 64 x 64, two workgroups per
-// CU.  (256 x 128 tiles of eight such waves, one workgroup per CU, measured the same.)
-constexpr int G_BM = 128, G_BN = 128, G_WGM = G_BM / 64, G_WGN = 2;
+// across groups): G_BM x G_BN, a G_WGM x G_WGN grid of waves of 64 x 64, one workgroup per CU.
+// (128 x 128 tiles of four such waves, two workgroups per CU, ran 3% slower in this loop.)
+constexpr int G_BM = 256, G_BN = 128, G_WGM = G_BM / 64, G_WGN = 2;
 // s_waitcnt immediate that waits for lgkmcnt == 0 only (gfx9 encoding: vmcnt bits 3:0 and 15:14
 // at their maximum, expcnt bits 6:4 at 7, lgkmcnt bits 11:8 at 0)
 constexpr int kLgkmZero = 0xC07F;
@@ -157,7 +154,7 @@ __device__ __forceinline__ u32x4 lds_frag(const uint8_t *base, int row, int chun
 // HM: A is the head-major attention output [K/hd][M][hd] (bf16 only).  FIX: the split-K fixup
 // launch (sums partial tiles and runs the epilogue; its own kernel so that profiles separate it).
 template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM, bool FIX>
-__global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1) void k_gemm(GemmP p) {
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   using C = GemmCfg<BM, BN, WGM, WGN>;
   constexpr int FM = C::FM, FN = C::FN, NW = C::NW, NT = C::NT, LA = C::LA, LW = C::LW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -279,6 +276,35 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
     const int64_t slot = (int64_t)(tile - p.n_dp) * p.split + sg;
     return reinterpret_cast<i32x4 *>(p.part + slot * (BM * BN * 4) + ((wid * FM + i) * FN + j) * 4096 + lane * 64);
   };
+  // close group g: sum += (float)acc * row scale, acc = 0; one 32-row block at a time, so that
+  // only 16 row scales are live; accumulator r of block i sits at row
+  // (m0 + 32 i + 8 (r / 4)) + sc_v + r % 4 (sc_load)
+  auto fold = [&](int g) {
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int i = 0; i < FM; i++) {
+        float sc[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+          const int64_t u = m0 + 32 * i + 8 * q4;
+          const ScLoad L0 = sc_load(p.M, n_groups, u, sc_v, 0, g);
+          const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.a_scale + L0.base, (uint32_t)L0.nrec);
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            sc[4 * q4 + e] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rsc, sc_load(p.M, n_groups, u, sc_v, e, g).voff, 0, 0));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+#pragma unroll
+          for (int j = 0; j < FN; j++) {
+            sum[i][j][r] = sum[i][j][r] + (float)acc[i][j][r] * sc[r];
+            acc[i][j][r] = 0;
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
   if constexpr (!GROUPED && FIX) {
     // sum of the segments' partial tiles, in segment order.  (Vectors are reinterpreted
     // whole: clang's __builtin_bit_cast of a single ext_vector element reads element 0.)
@@ -299,10 +325,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
           acc[i][j] = sg == 0 ? val : acc[i][j] + val;
         }
   } else {
-  if constexpr (!GROUPED) {
     // bf16 256 x 256: one wave per SIMD, 128 x 128 each (accumulators in AGPRs), a third fewer
-    // LDS bytes per MFMA than 8 waves of 128 x 64.  int8 and the 256 x 128 tiles: 8 waves, two
-    // per SIMD, of the same workgroup.  Iteration kt: MFMA steps 0..3 of slice kt from stage
+    // LDS bytes per MFMA than 8 waves of 128 x 64.  int8, the grouped int8 FC2 and the 256 x 128
+    // tiles: 8 waves, two per SIMD, of the same workgroup.  Iteration kt: MFMA steps 0..3 of slice kt from stage
     // kt&1 with fragments read one step ahead; the register set holding slice kt+1 goes to
     // stage (kt+1)&1 during steps 0 to 2, and the loads of slice kt+2 into the other set are
     // spread over the iteration.
@@ -311,11 +336,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
     // and the barrier at the top of the iteration instead, the two waves of a SIMD reach the
     // slice boundary together and both wait for the first fragments: int8 QKV and FC1 ran
     // 6-7% slower, the int8 out-projection 4%).
-    // LDS store li follows MFMA 2 li of the iteration, global load li follows MFMA LSTEP li + 1
-    // (4 li + 1 where that fits: spread over all four steps)
+    // LDS store li follows MFMA SSTEP li of the iteration (2 li where that fits), global load li
+    // follows MFMA LSTEP li + 1 (4 li + 1 where that fits: spread over all four steps).  The
+    // grouped FC2 closes a group at the end of the iteration that finishes it.
     constexpr int NSTEP = FM * FN;
     constexpr int LSTEP = (4 * NSTEP - 2) / (NL - 1) < 4 ? (4 * NSTEP - 2) / (NL - 1) : 4;
-    static_assert(2 * (NL - 1) < 3 * NSTEP && LSTEP * (NL - 1) + 1 < 4 * NSTEP && LSTEP >= 1, "store / load placement");
+    constexpr int SSTEP = (3 * NSTEP - 1) / (NL - 1) < 2 ? (3 * NSTEP - 1) / (NL - 1) : 2;
+    static_assert(SSTEP * (NL - 1) < 3 * NSTEP && LSTEP * (NL - 1) + 1 < 4 * NSTEP && LSTEP >= 1 && SSTEP >= 1,
+                  "store / load placement");
     u32x4 fa[2][FM], fb[2][FN];
     auto store_one = [&](const u32x4 *src, int kt, int li) {
       uint8_t *st = smem + (kt & 1) * C::STAGE + lds0;
@@ -360,7 +388,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
                                                                   __builtin_bit_cast(bf16x8, fb[ks & 1][j]), acc[i][j], 0, 0, 0);
 #pragma unroll
             for (int li = 0; li < NL; li++) {
-              if (g == 2 * li && more) {
+              if (g == SSTEP * li && more) {
                 __builtin_amdgcn_sched_barrier(0);
                 store_one(cur, kt + 1, li);
                 __builtin_amdgcn_sched_barrier(0);
@@ -374,6 +402,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
           }
       }
       __builtin_amdgcn_s_waitcnt(kLgkmZero);   // the next slice's step-0 reads, issued 16 MFMAs ago
+      if constexpr (GROUPED) {
+        if ((kt + 1) % kt_per_group == 0) fold(kt / kt_per_group);
+      }
     };
     using Steady = std::integral_constant<bool, true>;
     using Tail = std::integral_constant<bool, false>;
@@ -384,117 +415,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, (GROUPED && WGM * WGN == 4) ? 2 : 1
     }
     if (kt < kt1) iter1(kt, stage_reg[1], stage_reg[0], Tail{});
     if (kt + 1 < kt1) iter1(kt + 1, stage_reg[0], stage_reg[1], Tail{});
-  } else {
-  // prologue: slice kt0 into its LDS stage, slices kt0+1 and kt0+2 in the two register sets
-#pragma unroll
-  for (int li = 0; li < NL; li++) load_one(stage_reg[0], kt0, li);
-  store_slice(stage_reg[0], kt0);
-#pragma unroll
-  for (int li = 0; li < NL; li++) load_one(stage_reg[1], kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1, li);
-#pragma unroll
-  for (int li = 0; li < NL; li++) load_one(stage_reg[0], kt0 + 2 < kt1 ? kt0 + 2 : kt1 - 1, li);
-  __syncthreads();
-
-  // The grouped int8 FC2 (128 x 128 tiles, 4 waves, two workgroups per CU; the group sums
-  // close at the end of an iteration).
-  // Iteration kt: the register set holding slice kt+1 -> LDS stage (kt+1)&1 (last read in
-  // iteration kt-1), then the same set receives slice kt+3, its loads spread between the MFMAs
-  // of slice kt; the other set (slice kt+2) stays in flight for the whole iteration; barrier.
-  // Past the end the loads repeat the last slice (in range, never stored).  sched_barrier
-  // fixes the issue order.
-  constexpr int NMMA = 4 * FM * FN;                 // MFMAs per slice; load li follows MFMA li*NMMA/NL
-  auto iteration = [&](int kt, const u32x4 *cur, u32x4 *nxt, auto steady) {
-    constexpr bool STEADY = decltype(steady)::value;
-    if (STEADY || kt + 1 < kt1) store_slice(cur, kt + 1);
-    const int ktl = kt + 3 < kt1 ? kt + 3 : kt1 - 1;
-    const uint8_t *sa = smem + (kt & 1) * C::STAGE;
-    u32x4 fa[2][FM], fb[2][FN];
-    read_step(sa, 0, fa[0], fb[0]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      if (ks < 3) read_step(sa, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+    wait_vmem();   // the register loads past the end
+    if (!GROUPED && seg >= 0) {
+      // one K segment of a split tile: store the raw partial, the fixup launch finishes it
 #pragma unroll
       for (int i = 0; i < FM; i++)
 #pragma unroll
         for (int j = 0; j < FN; j++) {
-          const int m = (ks * FM + i) * FN + j;
-          if constexpr (INT8)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa[ks & 1][i]),
-                                                              __builtin_bit_cast(i32x4, fb[ks & 1][j]), acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[ks & 1][i]),
-                                                                __builtin_bit_cast(bf16x8, fb[ks & 1][j]), acc[i][j], 0, 0, 0);
+          i32x4 *dst = part_ptr(seg, i, j);
+          const i32x16 bits = __builtin_bit_cast(i32x16, acc[i][j]);
 #pragma unroll
-          for (int li = 0; li < NL; li++)
-            if (STEADY && li * NMMA / NL == m) {
-              __builtin_amdgcn_sched_barrier(0);
-              load_one(nxt, ktl, li);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    }
-    if constexpr (GROUPED) {
-      if ((kt + 1) % kt_per_group == 0) {
-        const int g = kt / kt_per_group;
-        // one 32-row block at a time, so that only 16 row scales are live; accumulator r of
-        // block i sits at row (m0 + 32 i + 8 (r / 4)) + sc_v + r % 4 (sc_load)
+          for (int q = 0; q < 4; q++) {
+            i32x4 v;
 #pragma unroll
-        for (int i = 0; i < FM; i++) {
-          float sc[16];
-#pragma unroll
-          for (int q4 = 0; q4 < 4; q4++) {
-            const int64_t u = m0 + 32 * i + 8 * q4;
-            const ScLoad L0 = sc_load(p.M, n_groups, u, sc_v, 0, g);
-            const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.a_scale + L0.base, (uint32_t)L0.nrec);
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              sc[4 * q4 + e] = __builtin_bit_cast(
-                  float, __builtin_amdgcn_raw_buffer_load_b32(rsc, sc_load(p.M, n_groups, u, sc_v, e, g).voff, 0, 0));
+            for (int e = 0; e < 4; e++) v[e] = bits[4 * q + e];
+            dst[q] = v;
           }
-#pragma unroll
-          for (int r = 0; r < 16; r++)
-#pragma unroll
-            for (int j = 0; j < FN; j++) {
-              sum[i][j][r] = sum[i][j][r] + (float)acc[i][j][r] * sc[r];
-              acc[i][j][r] = 0;
-            }
-          __builtin_amdgcn_sched_barrier(0);
         }
-      }
+      return;
     }
-    __syncthreads();
-  };
-  // two iterations per trip so that each register set is addressed statically
-  using Steady = std::integral_constant<bool, true>;
-  using Tail = std::integral_constant<bool, false>;
-  int kt = kt0;
-  for (; kt + 2 < kt1; kt += 2) {
-    iteration(kt, stage_reg[1], stage_reg[1], Steady{});
-    iteration(kt + 1, stage_reg[0], stage_reg[0], Steady{});
-  }
-  if (kt < kt1) iteration(kt, stage_reg[1], stage_reg[1], Tail{});
-  if (kt + 1 < kt1) iteration(kt + 1, stage_reg[0], stage_reg[0], Tail{});
-  }
-  wait_vmem();   // the register loads past the end
-  if (!GROUPED && seg >= 0) {
-    // one K segment of a split tile: store the raw partial, the fixup launch finishes it
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-      for (int j = 0; j < FN; j++) {
-        i32x4 *dst = part_ptr(seg, i, j);
-        const i32x16 bits = __builtin_bit_cast(i32x16, acc[i][j]);
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          i32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; e++) v[e] = bits[4 * q + e];
-          dst[q] = v;
-        }
-      }
-    return;
-  }
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -866,7 +805,7 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
 //     accumulate K in the same segments.  Where the per-tile fixup runs instead (fp32, GELU
 //     and rotary outputs) this under-costs it; at the block's shapes (2048-8192 tokens) it
 //     selects the same plans as costing that fixup would.
-// The grouped int8 FC2 uses 128 x 128 tiles (its second accumulator set does not fit 256 wide).
+// The grouped int8 FC2 uses 256 x 128 tiles (its second accumulator set does not fit 256 wide).
 constexpr int kCUs = 256;
 
 LinearPlan plan_linear(const h3dit_linear_args &a) {
@@ -918,8 +857,8 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
 template <bool INT8, int OUT, bool GROUPED, bool HM = false>
 static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st) {
   if constexpr (GROUPED) {
-    // two accumulator sets (int32 per group, fp32 across groups) per lane: 128 x 128 tiles of
-    // 4 waves of 64 x 64, two workgroups per CU (1280 tiles at 4096 x 5120: whole rounds)
+    // two accumulator sets (int32 per group, fp32 across groups) per lane: 256 x 128 tiles of
+    // 8 waves of 64 x 64
     return run_gemm<G_BM, G_BN, G_WGM, G_WGN, INT8, OUT, GROUPED, false>(p, pl, st);
   } else {
     // bf16: four waves of 128 x 128; int8: eight waves of 128 x 64 (measured faster for int8)
