@@ -100,26 +100,32 @@ __device__ __forceinline__ float gelu_tanh(float u) {
 // unless a half-integer lies within that distance of t.  Values within 4e-5 of a half-integer
 // (and non-finite t) take the true division, for the whole wave at once (a uniform branch
 // taken for a few percent of the 8-value chunks), so the codes are those of rintf(v / s).
+// Rounding: y = t + 1.5 * 2^23 is rintf(t) + 1.5 * 2^23 exactly for |t| < 2^22 (the sum has an
+// ulp of 1 and rounds to nearest even), so the low byte of y's bits is the two's complement
+// code, and y - 1.5 * 2^23 is rintf(t).  |t - rintf(t)| <= 1/2, so the tie test is one
+// comparison.  |t| <= 127 (1 + 2^-22) needs no clamp; the true-division path clamps.
 __device__ __forceinline__ uint2 q8_pack8(const float *v, float s, float inv) {
   if (s == 0.0f) return make_uint2(0u, 0u);   // the span is all zeros
-  float c[8];
+  constexpr float MAGIC = 12582912.0f;         // 1.5 * 2^23
+  float y[8];
   bool exact = false;
 #pragma unroll
   for (int e = 0; e < 8; e++) {
     const float t = v[e] * inv;
-    c[e] = rintf(t);
-    exact |= !(fabsf(t) < 128.0f) || fabsf(fabsf(t - c[e]) - 0.5f) <= 4e-5f;
+    y[e] = t + MAGIC;
+    const float d = t - (y[e] - MAGIC);
+    exact |= !(fabsf(t) < 128.0f) || fabsf(d) >= 0.5f - 4e-5f;
   }
   if (__any(exact)) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) c[e] = rintf(v[e] / s);
+    for (int e = 0; e < 8; e++) y[e] = fminf(fmaxf(rintf(v[e] / s), -127.0f), 127.0f) + MAGIC;
   }
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)(int)fminf(fmaxf(c[e], -127.0f), 127.0f) << (8 * e);
-#pragma unroll
-  for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)(int)fminf(fmaxf(c[4 + e], -127.0f), 127.0f) << (8 * e);
-  return make_uint2(lo, hi);
+  // low bytes of y[0..3] and y[4..7]: two byte pairs per v_perm, then the pairs into a word
+  const uint32_t p01 = __builtin_amdgcn_perm(__float_as_uint(y[1]), __float_as_uint(y[0]), 0x0c0c0400u);
+  const uint32_t p23 = __builtin_amdgcn_perm(__float_as_uint(y[3]), __float_as_uint(y[2]), 0x0c0c0400u);
+  const uint32_t p45 = __builtin_amdgcn_perm(__float_as_uint(y[5]), __float_as_uint(y[4]), 0x0c0c0400u);
+  const uint32_t p67 = __builtin_amdgcn_perm(__float_as_uint(y[7]), __float_as_uint(y[6]), 0x0c0c0400u);
+  return make_uint2(__builtin_amdgcn_perm(p23, p01, 0x05040100u), __builtin_amdgcn_perm(p67, p45, 0x05040100u));
 }
 
 }  // namespace h3
