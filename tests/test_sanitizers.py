@@ -74,8 +74,20 @@ def test_oracle_pins_under_sanitizers():
     assert "AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr
 
 
+def hip_file_flags():
+    """Per-source flags of the library build (loaded from build.py's file, so that the package,
+    which maps the library on import, is not imported here)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "h3dit_build", os.path.join(ROOT, "audio_diffusion_transformer_dit_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.FILE_FLAGS
+
+
 def build_host_sanitized(out_dir):
     """The HIP library with host code under ASan + UBSan (device code as usual)."""
+    file_flags = hip_file_flags()
     san = []
     for flag in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
                  "-fno-omit-frame-pointer"):
@@ -88,7 +100,8 @@ def build_host_sanitized(out_dir):
         procs.append(subprocess.Popen(
             [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-ffp-contract=off",
              "-fvisibility=hidden", "-fno-gpu-rdc", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-I", os.path.join(ROOT, "include"), *san, "-c", s, "-o", obj],
+             "-I", os.path.join(ROOT, "include"), *file_flags.get(os.path.basename(s), []), *san, "-c", s,
+             "-o", obj],
             stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
     for p in procs:
         _, err = p.communicate()
