@@ -446,7 +446,15 @@ def linear(M, N, K, a, w, out_kind=OUT_BF16, out=None, precision=BF16, a_headmaj
            w_scale=None, cos=None, sin=None, heads=0, head_dim=0, out_q=None, out_k=None, out_v=None, stream=None,
            workspace=None):
     """out = a w^T through h3dit_linear.  The split-K workspace the call needs (if any) is taken
-    from `workspace` (a uint8 device tensor) when it is large enough, else allocated."""
+    from `workspace` (a uint8 device tensor) when it is large enough, else allocated.  The C ABI
+    sees pointers only; where `out` is a tensor its size is checked against the output kind
+    here (M x N elements of 4 bytes for fp32 / int32 accumulators, 2 bytes otherwise)."""
+    if out is not None and not isinstance(out, int) and out_kind != OUT_QKV:
+        need_out = M * N * (4 if out_kind in (OUT_F32, OUT_I32) else 2)
+        have = out.numel() * out.element_size()
+        if have < need_out or not out.is_contiguous():
+            raise ValueError(f"linear: output tensor holds {have} bytes (contiguous: {out.is_contiguous()}), "
+                             f"the {M} x {N} output of kind {out_kind} needs {need_out}")
     args = LinearArgs(M, N, K, precision, _ptr(a), a_headmajor_hd, _ptr(a_scale), a_group, _ptr(w), _ptr(w_scale),
                       out_kind, _ptr(out), _ptr(cos), _ptr(sin), heads, head_dim, _ptr(out_q), _ptr(out_k),
                       _ptr(out_v))

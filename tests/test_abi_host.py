@@ -212,6 +212,20 @@ def test_linear_workspace_plan():
     assert h3.lib().h3dit_linear(C.byref(args), None) == h3.EINVAL       # misaligned
 
 
+def test_linear_binding_checks_the_output_tensor():
+    """The C ABI takes an output pointer only; the binding checks a tensor's bytes against the
+    output kind before the call (fp32 / int32 accumulators need 4 bytes per element)."""
+    import torch
+    M, N, K = 4, 256, 128
+    a = torch.zeros(M, K, dtype=torch.bfloat16)
+    w = torch.zeros(N, K, dtype=torch.bfloat16)
+    for kind, out in ((h3.OUT_F32, torch.zeros(M, N, dtype=torch.bfloat16)),
+                      (h3.OUT_BF16, torch.zeros(M, N - 1, dtype=torch.bfloat16)),
+                      (h3.OUT_BF16, torch.zeros(M, 2 * N, dtype=torch.bfloat16)[:, :N])):
+        with pytest.raises(ValueError):
+            h3.linear(M, N, K, a, w, kind, out)
+
+
 @pytest.mark.parametrize("M", [1, 7, 64, 129, 255, 256, 257, 300, 513, 2048, 4097, 4480])
 def test_linear_a_loads_stay_inside_a(M):
     """Walks every A-operand load (and, for the grouped FC2, every group-scale load) of the
