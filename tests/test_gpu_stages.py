@@ -206,14 +206,14 @@ def test_linear_bf16(M, N, K):
     assert_close_bf16(glc, ref, "GELU epilogue")
 
 
-@pytest.mark.parametrize("M,K,int8", [(4096, 128, False), (4000, 256, False), (4096, 384, False),
-                                      (4096, 384, True), (3900, 640, True)])
-def test_linear_full_round_short_k(M, K, int8):
+@pytest.mark.parametrize("M,K,int8,N", [(4096, 128, False, 4096), (4000, 256, False, 4096), (4096, 384, False, 4096),
+                                        (4096, 384, True, 4096), (3900, 640, True, 4096), (4096, 640, False, 20480)])
+def test_linear_full_round_short_k(M, K, int8, N):
     # 16 x 16 tiles of 256 x 256 fill one round of the chip, so the plan takes whole 256 x 256
-    # tiles (bf16: the 4-wave loop; int8: the 8-wave loop) with only a few K slices: the paths
-    # where the steady loop runs zero or few times and the peeled tail does the work (int8 with
-    # 3 and 5 slices: odd counts); M = 4000 / 3900 leaves a ragged last tile row
-    N = 4096
+    # tiles (bf16: 4 waves of 128 x 128; int8: 8 waves of 128 x 64) with only a few K slices: the
+    # paths where the steady loop runs zero or few times and the peeled tail does the work (int8
+    # with 3 and 5 slices: odd counts); M = 4000 / 3900 leaves a ragged last tile row; N = 20480
+    # gives five whole rounds of 10-slice tiles
     assert h3.linear_workspace(M, N, K, precision=h3.INT8 if int8 else h3.BF16) == 0
     a = bf_randn((M, K), 40 + K)
     wt = bf_randn((N, K), 41 + K, 0.02)
