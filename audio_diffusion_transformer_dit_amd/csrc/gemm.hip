@@ -544,22 +544,48 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
             tsin[k] = *reinterpret_cast<const float4 *>(sin_c + (m0 + r) * half);
           }
         }
-#pragma unroll
-        for (int k = 0; k < MAXR; k++) {
-          const int r = r0 + k * rstep;
-          const int64_t row = m0 + r;
-          if (r >= BM || row >= p.M) break;   // later rows are past the tile or the end too
+        auto rope = [&](u32x4 v, int k) {
           const float cc[4] = {tcos[k].x, tcos[k].y, tcos[k].z, tcos[k].w};
           const float ss[4] = {tsin[k].x, tsin[k].y, tsin[k].z, tsin[k].w};
-          for (int hh = 0; hh < hpt; hh++) {
-            float f[8], o[8];
-            unpack8(*reinterpret_cast<const u32x4 *>(smem + r * C::CPITCH + (hh * cph + ci) * 16), f);
+          float f[8], o[8];
+          unpack8(v, f);
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-              o[2 * e] = f[2 * e] * cc[e] - f[2 * e + 1] * ss[e];
-              o[2 * e + 1] = f[2 * e] * ss[e] + f[2 * e + 1] * cc[e];
-            }
-            *reinterpret_cast<u32x4 *>(dst0 + (int64_t)hh * p.M * p.hd + row * p.hd) = pack8(o);
+          for (int e = 0; e < 4; e++) {
+            o[2 * e] = f[2 * e] * cc[e] - f[2 * e + 1] * ss[e];
+            o[2 * e + 1] = f[2 * e] * ss[e] + f[2 * e + 1] * cc[e];
+          }
+          return pack8(o);
+        };
+        if (hpt == 2 && m0 + BM <= p.M && MAXR * rstep == BM) {
+          // whole tile, two heads per tile: every row of the thread is in the tile and inside M,
+          // and the LDS reads of a batch of rows (both heads) go out together
+          constexpr int RB = 4;
+          static_assert(MAXR % RB == 0, "whole batches");
+#pragma unroll
+          for (int k0 = 0; k0 < MAXR; k0 += RB) {
+            u32x4 x[RB][2];
+#pragma unroll
+            for (int u = 0; u < RB; u++)
+#pragma unroll
+              for (int hh = 0; hh < 2; hh++)
+                x[u][hh] = *reinterpret_cast<const u32x4 *>(smem + (r0 + (k0 + u) * rstep) * C::CPITCH +
+                                                            (hh * cph + ci) * 16);
+#pragma unroll
+            for (int u = 0; u < RB; u++)
+#pragma unroll
+              for (int hh = 0; hh < 2; hh++)
+                *reinterpret_cast<u32x4 *>(dst0 + (int64_t)hh * p.M * p.hd + (m0 + r0 + (k0 + u) * rstep) * p.hd) =
+                    rope(x[u][hh], k0 + u);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < MAXR; k++) {
+            const int r = r0 + k * rstep;
+            const int64_t row = m0 + r;
+            if (r >= BM || row >= p.M) break;   // later rows are past the tile or the end too
+            for (int hh = 0; hh < hpt; hh++)
+              *reinterpret_cast<u32x4 *>(dst0 + (int64_t)hh * p.M * p.hd + row * p.hd) =
+                  rope(*reinterpret_cast<const u32x4 *>(smem + r * C::CPITCH + (hh * cph + ci) * 16), k);
           }
         }
       } else {
@@ -611,10 +637,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
       }
     } else {
       uint16_t *out = reinterpret_cast<uint16_t *>(p.out) + n0 + c * 8;
-      for (int r = tid / CH; r < BM; r += NT / CH) {
-        const int64_t row = m0 + r;
-        if (row >= p.M) break;   // later rows are past the end too
-        u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * C::CPITCH + c * 16);
+      auto finish = [&](u32x4 v) {
         if constexpr (OUT == H3DIT_OUT_GELU) {
           float f[8];
           unpack8(v, f);
@@ -622,7 +645,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
           for (int e = 0; e < 8; e++) f[e] = gelu_tanh(f[e]);
           v = pack8(f);
         }
-        *reinterpret_cast<u32x4 *>(out + row * p.N) = v;
+        return v;
+      };
+      constexpr int RSTEP = NT / CH, RPT = BM / RSTEP, UB = RPT < 8 ? RPT : 8;   // rows per pass / thread / batch
+      static_assert(RPT % UB == 0, "whole batches");
+      if (m0 + BM <= p.M) {
+        // whole tile: the LDS reads of a batch of rows go out together, so that their latency
+        // is paid once per batch and not once per row
+        for (int k0 = 0; k0 < RPT; k0 += UB) {
+          u32x4 v[UB];
+#pragma unroll
+          for (int u = 0; u < UB; u++)
+            v[u] = *reinterpret_cast<const u32x4 *>(smem + (tid / CH + (k0 + u) * RSTEP) * C::CPITCH + c * 16);
+#pragma unroll
+          for (int u = 0; u < UB; u++)
+            *reinterpret_cast<u32x4 *>(out + (m0 + tid / CH + (k0 + u) * RSTEP) * p.N) = finish(v[u]);
+        }
+      } else {
+        for (int r = tid / CH; r < BM; r += RSTEP) {
+          const int64_t row = m0 + r;
+          if (row >= p.M) break;   // later rows are past the end too
+          *reinterpret_cast<u32x4 *>(out + row * p.N) =
+              finish(*reinterpret_cast<const u32x4 *>(smem + r * C::CPITCH + c * 16));
+        }
       }
     }
   }
