@@ -8,15 +8,15 @@
 // (full cache lines per row) that travel global -> VGPR -> LDS.  Chunk c of row r sits at LDS
 // slot c ^ ((r >> 1) & 7): the 16 lanes of one LDS read phase (16 rows, one chunk) cover all
 // 64 banks.  Fragment reads of the next 16-byte K step overlap the MFMAs of the current one.
-// The main shape is 256 x 256, in one of two forms:
+// The main shape is 256 x 256, in one of two wave layouts:
 //  * bf16: 4 waves (one per SIMD) of 128 x 128, accumulators in AGPRs.  Measured on gfx950 the
 //    fragment reads out of LDS are what holds the matrix pipe back, and a 128 x 128 wave tile
-//    reads a third fewer LDS bytes per MFMA than 128 x 64.  With no second wave to cover
-//    stalls the schedule is explicit: slice k+1's LDS stores and slice k+2's loads are spread
-//    between the MFMAs of slice k, and the per-slice barrier sits before the last K step so
-//    that the next slice's first fragments are read under that step's MFMAs.
+//    reads a third fewer LDS bytes per MFMA than 128 x 64.
 //  * int8 (and the 256 x 128 shape): 8 waves (two per SIMD) of 128 x 64 (256 x 128: 64 x 64,
-//    also the grouped int8 FC2), in the same loop.
+//    also the grouped int8 FC2).
+// One loop serves both, its schedule explicit: slice k+1's LDS stores and slice k+2's loads
+// are spread between the MFMAs of slice k, and the per-slice barrier sits before the last K
+// step so that the next slice's first fragments are read under that step's MFMAs.
 // Rows past M read as zeros (buffer range check, see a_load).  The epilogue stages the bf16 tile in LDS
 // and writes 16-byte row chunks (or, for V, 16-byte token chunks of V^T).  Workgroups are
 // dealt round-robin to the 8 XCDs; the tile order is remapped so that each XCD sweeps a
@@ -214,8 +214,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
 #pragma unroll
   for (int li = 0; li < LA; li++) ra[li] = a_rsrc(li, 0);
 
-  // Slices travel global -> registers -> LDS through two register sets (the loop forms below
-  // say which slices they hold when).
+  // Slices travel global -> registers -> LDS through two register sets (the loop below says
+  // which slices they hold when).
   constexpr int NL = LA + LW;                       // 16-byte loads per lane per slice
   u32x4 stage_reg[2][NL];
   auto load_one = [&](u32x4 *dst, int kt, int li) {
@@ -327,10 +327,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   } else {
     // bf16 256 x 256: one wave per SIMD, 128 x 128 each (accumulators in AGPRs), a third fewer
     // LDS bytes per MFMA than 8 waves of 128 x 64.  int8, the grouped int8 FC2 and the 256 x 128
-    // tiles: 8 waves, two per SIMD, of the same workgroup.  Iteration kt: MFMA steps 0..3 of slice kt from stage
-    // kt&1 with fragments read one step ahead; the register set holding slice kt+1 goes to
-    // stage (kt+1)&1 during steps 0 to 2, and the loads of slice kt+2 into the other set are
-    // spread over the iteration.
+    // tiles: 8 waves, two per SIMD, of the same workgroup.
+    // Iteration kt: MFMA steps 0..3 of slice kt from stage kt&1 with fragments read one step
+    // ahead; the register set holding slice kt+1 goes to stage (kt+1)&1 during steps 0 to 2,
+    // and the loads of slice kt+2 into the other set are spread over the iteration.
     // The barrier sits before step 3, whose fragments are already in registers; the step-0
     // fragments of slice kt+1 are read right after it, under step 3's MFMAs (with the stores
     // and the barrier at the top of the iteration instead, the two waves of a SIMD reach the
