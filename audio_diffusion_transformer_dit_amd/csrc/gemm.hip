@@ -26,10 +26,13 @@
 namespace h3 {
 
 constexpr int GKB = 128;        // bytes of K per slice and row
-// Tile of the grouped int8 FC2 (two accumulator sets per lane: int32 within a group, fp32
-// across groups): G_BM x G_BN, a G_WGM x G_WGN grid of waves of 64 x 64, one workgroup per CU.
-// (128 x 128 tiles of four such waves, two workgroups per CU, ran 3% slower in this loop.)
+// Tiles of the grouped int8 FC2 (two accumulator sets per lane: int32 within a group, fp32
+// across groups), waves of 64 x 64: G_BM x G_BN, a G_WGM x G_WGN grid of them, one workgroup
+// per CU; and the half-size GS_BM x GS_BN tile of four such waves, which covers the last
+// columns where whole rounds of the large tile would leave the chip partly idle.  (Used for
+// the whole output, the small tile ran 3% slower than the large one, two workgroups per CU.)
 constexpr int G_BM = 256, G_BN = 128, G_WGM = G_BM / 64, G_WGN = 2;
+constexpr int GS_BM = 128, GS_BN = 128, GS_WGM = GS_BM / 64, GS_WGN = 4;
 // s_waitcnt immediate that waits for lgkmcnt == 0 only (gfx9 encoding: vmcnt bits 3:0 and 15:14
 // at their maximum, expcnt bits 6:4 at 7, lgkmcnt bits 11:8 at 0)
 constexpr int kLgkmZero = 0xC07F;
@@ -54,6 +57,7 @@ struct GemmP {
   // and runs the epilogue
   int n_dp, split, kt_seg;
   uint8_t *part;
+  int64_t n_lo;   // first output column of this launch (its tiles cover columns n_lo ..)
 };
 
 template <int BM, int BN, int WGM, int WGN>
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm(GemmP p) {
   }
   int tm, tn;
   tile_coords(tile, tm, tn, p.tiles_m, p.tiles_n);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t m0 = (int64_t)tm * BM, n0 = p.n_lo + (int64_t)tn * BN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
   constexpr int esz = INT8 ? 1 : 2;
@@ -700,7 +704,7 @@ __global__ __launch_bounds__(SK_THREADS) void k_splitk_bf16(GemmP p, int n_split
   int tm, tn;
   tile_coords(p.n_dp + ti, tm, tn, p.tiles_m, p.tiles_n);
   const int wm = wid / 2, wn = wid % 2, hsel = lane >> 5;
-  const int64_t col = (int64_t)tn * 256 + wn * 128 + 32 * j + (lane & 31);
+  const int64_t col = p.n_lo + (int64_t)tn * 256 + wn * 128 + 32 * j + (lane & 31);
   uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
 #pragma unroll
   for (int r = 0; r < 16; r++) {
@@ -811,10 +815,13 @@ hipError_t launch_head_gemm(int64_t n, int c, int d, const uint16_t *x, const fl
   return hipGetLastError();
 }
 
+// One launch over the output columns [n_lo, n_hi): pl.n_dp whole tiles, then pl.n_split
+// tiles in pl.split K segments.
 template <int BM, int BN, int WGM, int WGN, bool INT8, int OUT, bool GROUPED, bool HM>
-static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
+static hipError_t run_gemm(GemmP p, const LinearPlan &pl, int64_t n_lo, int64_t n_hi, hipStream_t st) {
   p.tiles_m = (int)((p.M + BM - 1) / BM);
-  p.tiles_n = (int)(p.N / BN);
+  p.tiles_n = (int)((n_hi - n_lo) / BN);
+  p.n_lo = n_lo;
   p.n_dp = pl.n_dp;
   p.split = pl.split;
   p.kt_seg = pl.kt_seg;
@@ -850,7 +857,12 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, hipStream_t st) {
 //     accumulate K in the same segments.  Where the per-tile fixup runs instead (fp32, GELU
 //     and rotary outputs) this under-costs it; at the block's shapes (2048-8192 tokens) it
 //     selects the same plans as costing that fixup would.
-// The grouped int8 FC2 uses 256 x 128 tiles (its second accumulator set does not fit 256 wide).
+// The grouped int8 FC2 uses 256 x 128 tiles (its second accumulator set does not fit 256 wide)
+// over its first n_big columns and 128 x 128 tiles over the rest, n_big chosen to fill whole
+// rounds: a round of large tiles costs 1, a round of small tiles ~0.62 (one per CU, as its
+// registers allow: four waves, one per SIMD, each with a large tile's per-wave work and its
+// SIMD to itself).  No K is split: every element sums its groups in ascending order within
+// one workgroup, whichever tile holds it.
 constexpr int kCUs = 256;
 
 LinearPlan plan_linear(const h3dit_linear_args &a) {
@@ -868,7 +880,25 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
   pl.part_bytes = 0;
   pl.bn = 128;
   pl.n_dp = (int)(tm * (a.N / 128));
-  if (grouped) pl.n_dp = (int)((a.M + G_BM - 1) / G_BM * (a.N / G_BN));
+  pl.n_big = a.N;
+  pl.n_small = 0;
+  if (grouped) {
+    const int64_t tmb = (a.M + G_BM - 1) / G_BM, tms = (a.M + GS_BM - 1) / GS_BM, nc = a.N / G_BN;
+    int64_t best_c = nc;
+    double best = (double)((tmb * nc + kCUs - 1) / kCUs);
+    for (int64_t c = nc - 1; c >= 0; c--) {
+      const int64_t nb = tmb * c, ns = tms * (nc - c) * (G_BN / GS_BN);
+      const double cost = (double)((nb + kCUs - 1) / kCUs) + 0.62 * (double)((ns + kCUs - 1) / kCUs);
+      if (cost < best - 0.01) {
+        best = cost;
+        best_c = c;
+      }
+    }
+    pl.n_big = best_c * G_BN;
+    pl.n_dp = (int)(tmb * best_c);
+    pl.n_small = (int)(tms * (nc - best_c) * (G_BN / GS_BN));
+    return pl;
+  }
   if (!wide) return pl;
   const int64_t tiles = tm * (a.N / 256), full = tiles / kCUs, rem = tiles % kCUs;
   const double t_tile_us = (double)KT * 128 * 0.0277 / 2;   // one 256 x 256 tile over the whole K
@@ -903,15 +933,22 @@ template <bool INT8, int OUT, bool GROUPED, bool HM = false>
 static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st) {
   if constexpr (GROUPED) {
     // two accumulator sets (int32 per group, fp32 across groups) per lane: 256 x 128 tiles of
-    // 8 waves of 64 x 64
-    return run_gemm<G_BM, G_BN, G_WGM, G_WGN, INT8, OUT, GROUPED, false>(p, pl, st);
+    // 8 waves of 64 x 64 over columns [0, n_big), 128 x 128 tiles of 4 such waves after them
+    hipError_t e = hipSuccess;
+    if (pl.n_big > 0) e = run_gemm<G_BM, G_BN, G_WGM, G_WGN, INT8, OUT, GROUPED, false>(p, pl, 0, pl.n_big, st);
+    if (e == hipSuccess && pl.n_small > 0) {
+      LinearPlan sp = pl;
+      sp.n_dp = pl.n_small;
+      e = run_gemm<GS_BM, GS_BN, GS_WGM, GS_WGN, INT8, OUT, GROUPED, false>(p, sp, pl.n_big, p.N, st);
+    }
+    return e;
   } else {
     // bf16: four waves of 128 x 128; int8: eight waves of 128 x 64 (measured faster for int8)
     if (pl.bn == 256) {
-      if constexpr (INT8) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, pl, st);
-      else return run_gemm<256, 256, 2, 2, INT8, OUT, GROUPED, HM>(p, pl, st);
+      if constexpr (INT8) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, pl, 0, p.N, st);
+      else return run_gemm<256, 256, 2, 2, INT8, OUT, GROUPED, HM>(p, pl, 0, p.N, st);
     }
-    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, HM>(p, pl, st);
+    return run_gemm<256, 128, 4, 2, INT8, OUT, GROUPED, HM>(p, pl, 0, p.N, st);
   }
 }
 
@@ -926,60 +963,64 @@ void linear_a_extent(const h3dit_linear_args &a, uint64_t *max_end, uint64_t *ba
   const bool i8 = a.precision == H3DIT_INT8;
   const bool grouped = i8 && a.a_group > 0;
   const int esz = i8 ? 1 : 2;
-  int BM, NW;
-  if (grouped) {
-    BM = G_BM; NW = G_WGM * G_WGN;
-  } else if (pl.bn == 256) {
-    BM = 256; NW = i8 ? 8 : 4;
-  } else {
-    BM = 256; NW = 8;
-  }
-  const int LA = BM / (8 * NW);
   const int KT = (int)(a.K * esz / GKB);
   const int hm_hd = i8 ? 0 : a.a_headmajor_hd;
-  const int64_t tiles_m = (a.M + BM - 1) / BM;
   uint64_t top = 0, nbad = 0;
-  for (int64_t tm = 0; tm < tiles_m; tm++)
-    for (int r0 = 0; r0 < NW * 8; r0++)
-      for (int cl = 0; cl < 8; cl++)
-        for (int li = 0; li < LA; li++)
-          for (int kt = 0; kt < KT; kt++) {
-            const int64_t m0 = tm * BM;
-            const ALoad L = a_load(a.M, a.K, esz, hm_hd, NW, m0, r0, cl, li, kt);
-            const int64_t row = m0 + r0 + (int64_t)NW * 8 * li;
-            const bool masked = (int64_t)L.voff >= L.nrec;
-            // a row < M is always read; a row >= M reads zeros (token-major A) or, head-major,
-            // a row of the next head inside A, masked only past the last head
-            if ((row < a.M && masked) || (!hm_hd && row >= a.M && !masked)) nbad++;
-            if (!masked) {
-              if ((int64_t)L.voff + L.soff + 16 > L.nrec) nbad++;
-              const uint64_t end = (uint64_t)(L.base + L.voff + L.soff + 16);
-              if (end > top) top = end;
-            }
-          }
-  if (grouped) {
-    // the group scales [M][K / a_group] fp32 of the grouped FC2 (waves of 64 x 64, G_WGM rows of them)
-    const int ng = (int)(a.K / a.a_group);
-    uint64_t stop = 0;
+  // one tile form: BM rows, NW waves in a WGM-row grid
+  auto walk = [&](int BM, int NW, int WGM) {
+    const int LA = BM / (8 * NW);
+    const int64_t tiles_m = (a.M + BM - 1) / BM;
     for (int64_t tm = 0; tm < tiles_m; tm++)
-      for (int wm = 0; wm < G_WGM; wm++)
-        for (int hsel = 0; hsel < 2; hsel++)
-          for (int i = 0; i < 2; i++)
-            for (int q4 = 0; q4 < 4; q4++)
-              for (int e = 0; e < 4; e++)
-                for (int g = 0; g < ng; g++) {
-                  const int64_t u = tm * BM + 32 * i + 8 * q4;
-                  const int v = wm * 64 + 4 * hsel;
-                  const ScLoad L = sc_load(a.M, ng, u, v, e, g);
-                  const bool masked = (int64_t)L.voff >= L.nrec;
-                  if (masked != (u + v + e >= a.M)) nbad++;
-                  if (!masked) {
-                    if ((int64_t)L.voff + 4 > L.nrec) nbad++;
-                    const uint64_t end = (uint64_t)(L.base * 4 + L.voff + 4);
-                    if (end > stop) stop = end;
+      for (int r0 = 0; r0 < NW * 8; r0++)
+        for (int cl = 0; cl < 8; cl++)
+          for (int li = 0; li < LA; li++)
+            for (int kt = 0; kt < KT; kt++) {
+              const int64_t m0 = tm * BM;
+              const ALoad L = a_load(a.M, a.K, esz, hm_hd, NW, m0, r0, cl, li, kt);
+              const int64_t row = m0 + r0 + (int64_t)NW * 8 * li;
+              const bool masked = (int64_t)L.voff >= L.nrec;
+              // a row < M is always read; a row >= M reads zeros (token-major A) or, head-major,
+              // a row of the next head inside A, masked only past the last head
+              if ((row < a.M && masked) || (!hm_hd && row >= a.M && !masked)) nbad++;
+              if (!masked) {
+                if ((int64_t)L.voff + L.soff + 16 > L.nrec) nbad++;
+                const uint64_t end = (uint64_t)(L.base + L.voff + L.soff + 16);
+                if (end > top) top = end;
+              }
+            }
+    if (grouped) {
+      // the group scales [M][K / a_group] fp32 of the grouped FC2 (waves of 64 x 64, WGM rows
+      // of them, two 32-row blocks each)
+      const int ng = (int)(a.K / a.a_group);
+      uint64_t stop = 0;
+      for (int64_t tm = 0; tm < tiles_m; tm++)
+        for (int wm = 0; wm < WGM; wm++)
+          for (int hsel = 0; hsel < 2; hsel++)
+            for (int i = 0; i < 2; i++)
+              for (int q4 = 0; q4 < 4; q4++)
+                for (int e = 0; e < 4; e++)
+                  for (int g = 0; g < ng; g++) {
+                    const int64_t u = tm * BM + 32 * i + 8 * q4;
+                    const int v = wm * 64 + 4 * hsel;
+                    const ScLoad L = sc_load(a.M, ng, u, v, e, g);
+                    const bool masked = (int64_t)L.voff >= L.nrec;
+                    if (masked != (u + v + e >= a.M)) nbad++;
+                    if (!masked) {
+                      if ((int64_t)L.voff + 4 > L.nrec) nbad++;
+                      const uint64_t end = (uint64_t)(L.base * 4 + L.voff + 4);
+                      if (end > stop) stop = end;
+                    }
                   }
-                }
-    if (stop > (uint64_t)a.M * ng * 4) nbad++;
+      if (stop > (uint64_t)a.M * ng * 4) nbad++;
+    }
+  };
+  if (grouped) {
+    if (pl.n_dp > 0) walk(G_BM, G_WGM * G_WGN, G_WGM);
+    if (pl.n_small > 0) walk(GS_BM, GS_WGM * GS_WGN, GS_WGM);
+  } else if (pl.bn == 256) {
+    walk(256, i8 ? 8 : 4, 2);
+  } else {
+    walk(256, 8, 4);
   }
   *max_end = top;
   *bad = nbad;

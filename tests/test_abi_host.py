@@ -238,6 +238,7 @@ def test_linear_a_loads_stay_inside_a(M):
                                   (5120, 5120, h3.BF16, 0, 128),      # head-major attention output
                                   (768, 256, h3.BF16, 0, 64),         # head-major, head_dim 64
                                   (1024, 4096, h3.INT8, 1024, 0),     # grouped FC2 (128 x 128)
+                                  (5120, 2048, h3.INT8, 512, 0),      # grouped, 256 x 128 and 128 x 128 tiles
                                   (256, 8192, h3.INT8, 128, 0)):      # grouped, many groups
         end, bad = h3.linear_a_extent(M, N, K, prec, group, a_headmajor_hd=hm)
         esz = 1 if prec == h3.INT8 else 2

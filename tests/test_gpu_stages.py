@@ -301,7 +301,11 @@ def test_linear_int8_splitk_sampled_rows():
 
 
 @pytest.mark.parametrize("M,N,K,G", [(300, 256, 2048, 1024), (129, 512, 1024, 1024), (64, 256, 3072, 1024),
-                                     (200, 256, 1024, 256)])
+                                     (200, 256, 1024, 256),
+                                     # 280 large tiles would take two rounds: 252 large tiles plus a
+                                     # second launch of 128 x 128 tiles over the last 512 columns,
+                                     # ragged in both
+                                     (1700, 5120, 2048, 512)])
 def test_fc2_grouped_int8(M, N, K, G):
     gl = bf_randn((M, K), 18)
     wt = bf_randn((N, K), 19, 0.02)
