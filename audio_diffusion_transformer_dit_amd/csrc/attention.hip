@@ -288,6 +288,10 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
   auto scores_probs = [&](const uint8_t *kb_, const uint8_t *vb_, f32x16 (&sn)[2], f32x16 (&sc)[2],
                           u32x4 (&fv)[VD]) {
     constexpr int PER = 32 / KS;   // probabilities per score step
+    // The score phase (each MFMA followed by two exponentials of the other block) runs at
+    // raised wave priority: on a SIMD shared with a wave in its O^T phase its instructions
+    // issue first and the other wave's fill in (about 1% faster on one box)
+    __builtin_amdgcn_s_setprio(1);
     const float mc = m_ref * c2;
     sn[0] = f32x16{0};
     sn[1] = f32x16{0};
@@ -312,6 +316,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void k_attention(const uint16_t *q, co
       fk[KD - 1] = nk;
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // O^T update with the current block's probabilities on MFMA; their row sum and the next
   // block's max on VALU.  Returns the next block's max (both half-waves).  The MFMAs go in

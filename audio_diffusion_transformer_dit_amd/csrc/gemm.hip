@@ -27,10 +27,10 @@ namespace h3 {
 
 constexpr int GKB = 128;        // bytes of K per slice and row
 // Tiles of the grouped int8 FC2 (two accumulator sets per lane: int32 within a group, fp32
-// across groups), waves of 64 x 64: G_BM x G_BN, a G_WGM x G_WGN grid of them, one workgroup
-// per CU; and the half-size GS_BM x GS_BN tile of four such waves, which covers the last
-// columns where whole rounds of the large tile would leave the chip partly idle.  (Used for
-// the whole output, the small tile ran 3% slower than the large one, two workgroups per CU.)
+// across groups): G_BM x G_BN, a G_WGM x G_WGN grid of waves of 64 x 64, one workgroup
+// per CU; and the half-size GS_BM x GS_BN tile of eight waves of 64 x 32, which covers the
+// last columns where whole rounds of the large tile would leave the chip partly idle.  (Four
+// waves of 64 x 64 on that tile, one per SIMD, took as long as a large tile.)
 constexpr int G_BM = 256, G_BN = 128, G_WGM = G_BM / 64, G_WGN = 2;
 constexpr int GS_BM = 128, GS_BN = 128, GS_WGM = GS_BM / 64, GS_WGN = 4;
 // s_waitcnt immediate that waits for lgkmcnt == 0 only (gfx9 encoding: vmcnt bits 3:0 and 15:14
@@ -859,10 +859,10 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, int64_t n_lo, int64_t 
 //     selects the same plans as costing that fixup would.
 // The grouped int8 FC2 uses 256 x 128 tiles (its second accumulator set does not fit 256 wide)
 // over its first n_big columns and 128 x 128 tiles over the rest, n_big chosen to fill whole
-// rounds: a round of large tiles costs 1, a round of small tiles ~0.62 (one per CU, as its
-// registers allow: four waves, one per SIMD, each with a large tile's per-wave work and its
-// SIMD to itself).  No K is split: every element sums its groups in ascending order within
-// one workgroup, whichever tile holds it.
+// rounds: a round of large tiles costs 1, a round of 256 small tiles 0.86 (measured at 4096
+// tokens: eight waves of 64 x 32, two per SIMD, half a large tile's MFMAs but three quarters
+// of its LDS fragment reads).  No K is split: every element sums its groups in ascending
+// order within one workgroup, whichever tile holds it.
 constexpr int kCUs = 256;
 
 LinearPlan plan_linear(const h3dit_linear_args &a) {
@@ -888,7 +888,7 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
     double best = (double)((tmb * nc + kCUs - 1) / kCUs);
     for (int64_t c = nc - 1; c >= 0; c--) {
       const int64_t nb = tmb * c, ns = tms * (nc - c) * (G_BN / GS_BN);
-      const double cost = (double)((nb + kCUs - 1) / kCUs) + 0.62 * (double)((ns + kCUs - 1) / kCUs);
+      const double cost = (double)((nb + kCUs - 1) / kCUs) + 0.86 * (double)((ns + kCUs - 1) / kCUs);
       if (cost < best - 0.01) {
         best = cost;
         best_c = c;
@@ -933,7 +933,7 @@ template <bool INT8, int OUT, bool GROUPED, bool HM = false>
 static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st) {
   if constexpr (GROUPED) {
     // two accumulator sets (int32 per group, fp32 across groups) per lane: 256 x 128 tiles of
-    // 8 waves of 64 x 64 over columns [0, n_big), 128 x 128 tiles of 4 such waves after them
+    // 8 waves of 64 x 64 over columns [0, n_big), 128 x 128 tiles of 8 waves of 64 x 32 after them
     hipError_t e = hipSuccess;
     if (pl.n_big > 0) e = run_gemm<G_BM, G_BN, G_WGM, G_WGN, INT8, OUT, GROUPED, false>(p, pl, 0, pl.n_big, st);
     if (e == hipSuccess && pl.n_small > 0) {
@@ -989,7 +989,7 @@ void linear_a_extent(const h3dit_linear_args &a, uint64_t *max_end, uint64_t *ba
               }
             }
     if (grouped) {
-      // the group scales [M][K / a_group] fp32 of the grouped FC2 (waves of 64 x 64, WGM rows
+      // the group scales [M][K / a_group] fp32 of the grouped FC2 (waves 64 rows high, WGM rows
       // of them, two 32-row blocks each)
       const int ng = (int)(a.K / a.a_group);
       uint64_t stop = 0;
