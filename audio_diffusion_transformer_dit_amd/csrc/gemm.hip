@@ -857,6 +857,12 @@ static hipError_t run_gemm(GemmP p, const LinearPlan &pl, int64_t n_lo, int64_t 
 //     accumulate K in the same segments.  Where the per-tile fixup runs instead (fp32, GELU
 //     and rotary outputs) this under-costs it; at the block's shapes (2048-8192 tokens) it
 //     selects the same plans as costing that fixup would.
+//   int8 (not the QKV epilogue, whose V^T pass is laid out for the wider tiles): 256 x 256
+//     tiles over the first columns and a second launch
+//     of 128 x 128 tiles (eight waves of 64 x 32) over the rest, a round of those ~0.43 of a
+//     round of whole tiles (measured at 4096 x 5120 x 5120: one round of each, 118-121 us,
+//     against 131-132 us for 2.5 rounds of 256 x 128 tiles).  int8 sums are exact, so the
+//     output does not depend on the plan.
 // The grouped int8 FC2 uses 256 x 128 tiles (its second accumulator set does not fit 256 wide)
 // over its first n_big columns and 128 x 128 tiles over the rest, n_big chosen to fill whole
 // rounds: a round of large tiles costs 1, a round of 256 small tiles 0.86 (measured at 4096
@@ -917,6 +923,28 @@ LinearPlan plan_linear(const h3dit_linear_args &a) {
       best_s = sp;
     }
   }
+  // int8 (exact whatever the plan): whole 256 x 256 tiles over the first c * 256 columns,
+  // 128 x 128 tiles over the rest
+  int64_t mix_c = -1;
+  if (i8 && a.out_kind != H3DIT_OUT_QKV) {
+    const int64_t tms = (a.M + 127) / 128, nc = a.N / 256;
+    for (int64_t c = nc - 1; c >= 1; c--) {
+      const int64_t nb = tm * c, ns = tms * (a.N - 256 * c) / 128;
+      const double cost = (double)((nb + kCUs - 1) / kCUs) + 0.43 * (double)((ns + kCUs - 1) / kCUs);
+      if (cost < best - 1e-9 && cost < c128 - 1e-9) {
+        best = cost;
+        best_s = 1;
+        mix_c = c;
+      }
+    }
+  }
+  if (mix_c > 0) {
+    pl.bn = 256;
+    pl.n_dp = (int)(tm * mix_c);
+    pl.n_big = mix_c * 256;
+    pl.n_small = (int)((a.M + 127) / 128 * (a.N - 256 * mix_c) / 128);
+    return pl;
+  }
   if (c128 < best - 1e-9) return pl;
   pl.bn = 256;
   pl.n_dp = (int)tiles;
@@ -945,6 +973,15 @@ static hipError_t dispatch(const GemmP &p, const LinearPlan &pl, hipStream_t st)
   } else {
     // bf16: four waves of 128 x 128; int8: eight waves of 128 x 64 (measured faster for int8)
     if (pl.bn == 256) {
+      if constexpr (INT8 && OUT != H3DIT_OUT_QKV) {
+        if (pl.n_small > 0) {
+          hipError_t e = run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, pl, 0, pl.n_big, st);
+          LinearPlan sp = pl;
+          sp.n_dp = pl.n_small;
+          if (e == hipSuccess) e = run_gemm<GS_BM, GS_BN, GS_WGM, GS_WGN, INT8, OUT, GROUPED, HM>(p, sp, pl.n_big, p.N, st);
+          return e;
+        }
+      }
       if constexpr (INT8) return run_gemm<256, 256, 2, 4, INT8, OUT, GROUPED, HM>(p, pl, 0, p.N, st);
       else return run_gemm<256, 256, 2, 2, INT8, OUT, GROUPED, HM>(p, pl, 0, p.N, st);
     }
@@ -1019,6 +1056,7 @@ void linear_a_extent(const h3dit_linear_args &a, uint64_t *max_end, uint64_t *ba
     if (pl.n_small > 0) walk(GS_BM, GS_WGM * GS_WGN, GS_WGM);
   } else if (pl.bn == 256) {
     walk(256, i8 ? 8 : 4, 2);
+    if (pl.n_small > 0) walk(GS_BM, GS_WGM * GS_WGN, GS_WGM);
   } else {
     walk(256, 8, 4);
   }

@@ -72,7 +72,8 @@ H3DIT_API int h3dit_quantize_rows(int64_t rows, int64_t cols, int64_t group, con
  *                   pairwise by cos/sin (fp32 [M][head_dim/2]) and rounded once, written
  *                   head-major to out_q, out_k; v written as V^T to out_v.
  * M >= 1; N % 128 == 0; K % 128 == 0 (int8: K % 128 == 0 and K % a_group == 0).
- * Work plan: when the output tiles do not fill whole rounds of the chip, the tiles of the last
+ * Work plan: when the output tiles do not fill whole rounds of the chip, the last columns may
+ * be computed in smaller tiles by a second launch (int8 path), or the tiles of the last
  * round are computed as K segments whose fp32 (int32 on the int8 path) partial tiles go to
  * `workspace` (device, 256-byte aligned, workspace_bytes long) and are summed in segment
  * order by a second launch.  h3dit_linear_workspace gives the bytes a call needs (0 when it

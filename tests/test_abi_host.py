@@ -235,6 +235,7 @@ def test_linear_a_loads_stay_inside_a(M):
     for N, K, prec, group, hm in ((256, 256, h3.BF16, 0, 0),          # small: 256 x 128 tiles
                                   (5120, 5120, h3.BF16, 0, 0),        # 256 x 256 bf16, split-K tail
                                   (15360, 5120, h3.INT8, 0, 0),       # 256 x 256 int8 (8 waves)
+                                  (5120, 5120, h3.INT8, 0, 0),        # int8: 256 x 256 and 128 x 128 tiles
                                   (5120, 5120, h3.BF16, 0, 128),      # head-major attention output
                                   (768, 256, h3.BF16, 0, 64),         # head-major, head_dim 64
                                   (1024, 4096, h3.INT8, 1024, 0),     # grouped FC2 (128 x 128)

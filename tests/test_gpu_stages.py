@@ -278,6 +278,30 @@ def test_linear_int8(M, N, K):
     assert relerr(cpu(gl), oracle.gelu_rows(deq)) <= BF16_TOL
 
 
+@pytest.mark.parametrize("M", [4096, 4000])
+def test_linear_int8_column_split_sampled_rows(M):
+    """M x 5120 x 5120 on the int8 path (the out-projection's shape): 256 x 256 tiles over
+    columns 0-4095 and a second launch of 128 x 128 tiles over 4096-5119 (one round each instead
+    of 2.5 rounds of 256 x 128 tiles); M = 4000 leaves both launches a ragged last tile row.
+    Accumulators and dequantised output exact on sampled rows across both column ranges."""
+    N = K = 5120
+    assert h3.linear_workspace(M, N, K, h3.INT8) == 0
+    qa = torch.randint(-127, 128, (M, K), dtype=torch.int8, generator=torch.Generator().manual_seed(15))
+    qw = torch.randint(-127, 128, (N, K), dtype=torch.int8, generator=torch.Generator().manual_seed(16))
+    sa = torch.rand(M, generator=torch.Generator().manual_seed(17)) * 0.01 + 1e-3
+    sw = torch.rand(N, generator=torch.Generator().manual_seed(18)) * 0.01 + 1e-3
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    h3.linear(M, N, K, to_dev(qa), to_dev(qw), h3.OUT_I32, acc, precision=h3.INT8, a_scale=to_dev(sa),
+              w_scale=to_dev(sw))
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    h3.linear(M, N, K, to_dev(qa), to_dev(qw), h3.OUT_BF16, out, precision=h3.INT8, a_scale=to_dev(sa),
+              w_scale=to_dev(sw))
+    rows = torch.tensor([0, 1, 127, 128, 255, 1029, 2048, 3071, 3333, 3840, 3967, M - 2, M - 1])
+    ref = oracle.gemm_i32(qa[rows].contiguous(), qw)
+    assert_bitexact(cpu(acc)[rows], ref, "int32 accumulators, both column ranges")
+    assert_bitexact(cpu(out)[rows], oracle.dequant_bf16(ref, sa[rows].contiguous(), sw), "dequantised output")
+
+
 def test_linear_int8_splitk_sampled_rows():
     """4096 x 5120 x 20480 on the int8 path without groups: 64 of the 320 tiles are summed from
     4 K segments of int32 partials, which must give the exact accumulators."""
