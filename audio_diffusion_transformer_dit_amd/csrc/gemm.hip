@@ -14,6 +14,8 @@
 //    reads a third fewer LDS bytes per MFMA than 128 x 64.
 //  * int8 (and the 256 x 128 shape): 8 waves (two per SIMD) of 128 x 64 (256 x 128: 64 x 64,
 //    also the grouped int8 FC2).
+// Where whole rounds of those tiles would leave the chip partly idle, the int8 projections can
+// hand their last columns to a second launch of 128 x 128 tiles (8 waves of 64 x 32).
 // One loop serves both, its schedule explicit: slice k+1's LDS stores and slice k+2's loads
 // are spread between the MFMAs of slice k, and the per-slice barrier sits before the last K
 // step so that the next slice's first fragments are read under that step's MFMAs.
@@ -28,9 +30,10 @@ namespace h3 {
 constexpr int GKB = 128;        // bytes of K per slice and row
 // Tiles of the grouped int8 FC2 (two accumulator sets per lane: int32 within a group, fp32
 // across groups): G_BM x G_BN, a G_WGM x G_WGN grid of waves of 64 x 64, one workgroup
-// per CU; and the half-size GS_BM x GS_BN tile of eight waves of 64 x 32, which covers the
-// last columns where whole rounds of the large tile would leave the chip partly idle.  (Four
-// waves of 64 x 64 on that tile, one per SIMD, took as long as a large tile.)
+// per CU; and the small GS_BM x GS_BN tile of eight waves of 64 x 32, which covers the last
+// columns where whole rounds of the large tile would leave the chip partly idle (also for the
+// ungrouped int8 projections after 256 x 256 tiles).  (Four waves of 64 x 64 on that tile, one
+// per SIMD, took as long as a large tile.)
 constexpr int G_BM = 256, G_BN = 128, G_WGM = G_BM / 64, G_WGN = 2;
 constexpr int GS_BM = 128, GS_BN = 128, GS_WGM = GS_BM / 64, GS_WGN = 4;
 // s_waitcnt immediate that waits for lgkmcnt == 0 only (gfx9 encoding: vmcnt bits 3:0 and 15:14
