@@ -278,13 +278,13 @@ def test_linear_int8(M, N, K):
     assert relerr(cpu(gl), oracle.gelu_rows(deq)) <= BF16_TOL
 
 
-@pytest.mark.parametrize("M", [4096, 4000])
-def test_linear_int8_column_split_sampled_rows(M):
-    """M x 5120 x 5120 on the int8 path (the out-projection's shape): 256 x 256 tiles over
-    columns 0-4095 and a second launch of 128 x 128 tiles over 4096-5119 (one round each instead
-    of 2.5 rounds of 256 x 128 tiles); M = 4000 leaves both launches a ragged last tile row.
-    Accumulators and dequantised output exact on sampled rows across both column ranges."""
-    N = K = 5120
+@pytest.mark.parametrize("M,N,K", [(4096, 5120, 5120), (4000, 5120, 5120), (3500, 5120, 1024)])
+def test_linear_int8_column_split_sampled_rows(M, N, K):
+    """The int8 path's column split: at the out-projection's shape (M x 5120 x 5120) 256 x 256
+    tiles over columns 0-4095 and a second launch of 128 x 128 tiles over 4096-5119 (one round
+    each instead of 2.5 rounds of 256 x 128 tiles); M = 4000 leaves both launches a ragged last
+    tile row; 3500 x 5120 x 1024 splits at column 4608.  Accumulators and dequantised output
+    exact, GELU output at the bf16 bar, on sampled rows across both column ranges."""
     assert h3.linear_workspace(M, N, K, h3.INT8) == 0
     qa = torch.randint(-127, 128, (M, K), dtype=torch.int8, generator=torch.Generator().manual_seed(15))
     qw = torch.randint(-127, 128, (N, K), dtype=torch.int8, generator=torch.Generator().manual_seed(16))
@@ -296,10 +296,15 @@ def test_linear_int8_column_split_sampled_rows(M):
     out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     h3.linear(M, N, K, to_dev(qa), to_dev(qw), h3.OUT_BF16, out, precision=h3.INT8, a_scale=to_dev(sa),
               w_scale=to_dev(sw))
-    rows = torch.tensor([0, 1, 127, 128, 255, 1029, 2048, 3071, 3333, 3840, 3967, M - 2, M - 1])
+    rows = torch.tensor([0, 1, 127, 128, 255, 1029, 2048, 3071, 3333, 3456, M - 2, M - 1])
     ref = oracle.gemm_i32(qa[rows].contiguous(), qw)
     assert_bitexact(cpu(acc)[rows], ref, "int32 accumulators, both column ranges")
-    assert_bitexact(cpu(out)[rows], oracle.dequant_bf16(ref, sa[rows].contiguous(), sw), "dequantised output")
+    deq = oracle.dequant_bf16(ref, sa[rows].contiguous(), sw)
+    assert_bitexact(cpu(out)[rows], deq, "dequantised output")
+    gl = torch.empty_like(out)
+    h3.linear(M, N, K, to_dev(qa), to_dev(qw), h3.OUT_GELU, gl, precision=h3.INT8, a_scale=to_dev(sa),
+              w_scale=to_dev(sw))
+    assert relerr(cpu(gl)[rows], oracle.gelu_rows(deq)) <= BF16_TOL
 
 
 def test_linear_int8_splitk_sampled_rows():
