@@ -169,7 +169,7 @@ struct LinearPlan {
   int kt_seg;       // 128-byte K slices per segment
   int n_split;      // split tiles
   size_t part_bytes;  // workspace for their partial tiles
-  int64_t n_big;    // grouped int8 FC2: columns [0, n_big) in 256 x 128 tiles (n_dp of them),
+  int64_t n_big;    // int8 column split: columns [0, n_big) in the wide tiles (n_dp of them),
   int n_small;      // the rest in n_small 128 x 128 tiles (a second launch); otherwise N and 0
 };
 LinearPlan plan_linear(const h3dit_linear_args &a);
