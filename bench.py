@@ -157,7 +157,7 @@ def time_streamed(w, blocks, x, steps, warmup, reduction=None):
             "workspace_bytes": stack.workspace_bytes}
 
 
-def kernel_breakdown(w, p, x, iters, int8):
+def kernel_breakdown(w, p, x, iters, int8, progress=False):
     """Times each kernel of one block where it runs in the block: `iters` passes over the
     block's launches in order, every launch bracketed by HIP events on the current stream (the
     stream the library launches on), so each kernel reads what the kernel before it just wrote,
@@ -247,6 +247,8 @@ def kernel_breakdown(w, p, x, iters, int8):
     for fn, _, _ in ops.values():
         fn()
     torch.cuda.synchronize()
+    if progress:
+        print(f"[bench] {'int8' if int8 else 'bf16'} block launches: first pass done", file=sys.stderr, flush=True)
     evs = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
            for name in ops}
     for it in range(iters):
@@ -255,6 +257,9 @@ def kernel_breakdown(w, p, x, iters, int8):
             s.record()
             fn()
             e.record()
+        if progress:   # profiled runs: the profiler serialises the launches, so this tracks the GPU
+            print(f"[bench] {'int8' if int8 else 'bf16'} block launches: pass {it + 1}/{iters} issued", file=sys.stderr,
+                  flush=True)
     torch.cuda.synchronize()
     res = {}
     for name, (fn, flop, nbytes) in ops.items():
@@ -386,13 +391,17 @@ def main():
           flush=True)
 
     x = synth.make_x(w, seed, dev)
+    torch.cuda.synchronize()
+    print("[bench] input residual ready", file=sys.stderr, flush=True)
     out = {}
     if args.only_kernels:
         p = make_blocks(w, 1, seed, dev, int8_main)[0]
-        out["kernels"] = kernel_breakdown(w, p, x, args.kernel_iters, int8_main)
+        torch.cuda.synchronize()
+        print("[bench] block weights ready", file=sys.stderr, flush=True)
+        out["kernels"] = kernel_breakdown(w, p, x, args.kernel_iters, int8_main, progress=True)
         if not int8_main and not args.no_int8:
             import audio_diffusion_transformer_dit_amd as h3
-            out["kernels_int8"] = kernel_breakdown(w, h3.quantize_block(p), x, args.kernel_iters, True)
+            out["kernels_int8"] = kernel_breakdown(w, h3.quantize_block(p), x, args.kernel_iters, True, progress=True)
         if args.copy_bytes:
             src = torch.ones(args.copy_bytes // 2, dtype=torch.bfloat16, device=dev)
             dst = torch.empty_like(src)
